@@ -1,0 +1,35 @@
+"""Plain CPU oracle for paged KV-cache decode attention (test infrastructure).
+
+This package is test infrastructure. Only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import or call it; the product
+path (``paged_kv_cache_154_amd``) never does, and the two share no code.
+
+Everything here is written from the four web pages on PagedAttention that the
+package documentation names, in float64 for attention (exact conversion from
+fp32/fp16/bf16 storage) and as bit copies for the cache operations.
+
+Pins (checked by ``tests/test_oracle_*.py`` without a GPU):
+  * ``decode``: contiguous scaled-dot-product attention from torch in float64
+    on an independently gathered K/V, seq_len = 1 returns the V row, q = 0
+    returns the mean of V, a dominant key selects its V row, GQA equals MHA
+    with each KV head repeated, invariance under physical-block permutation
+    and under re-packing at another block size, NaN in unused slots ignored.
+  * ``reshape_and_cache``: the slot worked out from the block table of the
+    three-level mapping example (PagedAttention principle, tbr8.org, §2.1)
+    and the slot rule of the block engine (LLM inference engine internals,
+    §2.3); every other byte unchanged.
+  * ``copy_blocks``: destination equals the pre-call source, all else
+    unchanged, and decode after a copy-on-write remap equals decode before.
+  * closed forms: the printed KV-size, block-size and pool-sizing numbers.
+No function here is "parity unpinned".
+"""
+
+from .paged_attention import (  # noqa: F401
+    blocks_needed,
+    block_bytes,
+    copy_blocks,
+    decode,
+    decode_one,
+    kv_cache_bytes,
+    reshape_and_cache,
+)
