@@ -1,0 +1,185 @@
+/*
+ * pagedkv.h - C ABI of the paged KV-cache decode library for AMD CDNA4
+ * (MI355X, gfx950).
+ *
+ * The problem, as the PagedAttention pages state it: the K and V of every
+ * cached token live in fixed-size physical blocks of a shared pool; a
+ * sequence reaches its tokens through a block table that maps its logical
+ * block i to a physical block ("PagedAttention principle", tbr8.org,
+ * sections 2.1-2.2; "LLM inference engine internals", sections 2.2-2.4).
+ *
+ * Conventions for every entry point:
+ *   - Every pointer is a DEVICE pointer (memory of the current HIP device),
+ *     dense and row-major; no strides. The caller allocates and owns all of
+ *     it, including the split-K workspace. The library allocates nothing and
+ *     keeps no state between calls; calls are reentrant.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and the call
+ *     returns without waiting for it.
+ *   - Return value: PKV_OK (0) or a negative pkv_status. Arguments are
+ *     checked on the host before anything is launched; a call that fails the
+ *     check launches nothing. PKV_ERR_HIP reports a launch failure
+ *     (hipGetLastError after the launch). No C++ exception crosses the ABI.
+ *   - Contents of device buffers (block ids, slots, lengths) are the
+ *     caller's contract and are not checked in the fast path, but the kernels
+ *     never read or write outside the buffers the shape arguments describe:
+ *     an out-of-range block id, slot or length is skipped or clamped, and
+ *     then the result for that sequence or token is unspecified.
+ *     pagedkv_check_decode_inputs() reports such entries.
+ *   - dtype codes: PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 (IEEE binary32,
+ *     binary16, bfloat16).
+ */
+#ifndef PAGEDKV_H_
+#define PAGEDKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef PAGEDKV_STREAM_T_DEFINED
+#define PAGEDKV_STREAM_T_DEFINED
+/* Same type as HIP's hipStream_t (an opaque handle). */
+typedef struct ihipStream_t* hipStream_t;
+#endif
+
+enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 };
+
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,        /* a required pointer is NULL */
+  PKV_ERR_SHAPE = -2,       /* inconsistent or negative sizes */
+  PKV_ERR_UNSUPPORTED = -3, /* valid but not built: dtype, head_dim, block_size, group size */
+  PKV_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
+  PKV_ERR_HIP = -5          /* the HIP runtime reported an error at launch */
+};
+
+/*
+ * paged_attn_decode - one decode step of attention for a batch of sequences,
+ * each with one query token, over K/V held in a paged block pool.
+ *
+ * For sequence s, query head h, with G = num_heads / num_kv_heads and KV head
+ * j = h / G (consecutive query heads share a KV head), L = seq_lens[s]:
+ *   k_t = key_cache[block_table[s][t / block_size], t % block_size, j, :]
+ *   v_t = value_cache[same]                                   (t = 0 .. L-1)
+ *   out[s, h, :] = sum_t softmax_t(scale * q . k_t) * v_t
+ * The gather through the block table, the stop at seq_len and the score scale
+ * follow the paged-attention listing of "PagedAttention principle" section
+ * 2.2 and the two-level addressing of "LLM inference engine internals"
+ * section 2.4; the softmax runs over all L positions of one (sequence, head).
+ * L counts every cached token the query attends to, the new token included
+ * (write it with reshape_and_cache first). L = 0 gives a zero row. Slots at
+ * positions >= L are never read into the arithmetic (they may hold NaN).
+ * Accumulation is in fp32.
+ *
+ *   out          [num_seqs, num_heads, head_dim], dtype out_dtype
+ *   query        [num_seqs, num_heads, head_dim], dtype kv_dtype
+ *   key_cache,
+ *   value_cache  [num_blocks, block_size, num_kv_heads, head_dim], kv_dtype
+ *   block_table  int32 [num_seqs, max_blocks_per_seq]; entries of logical
+ *                blocks 0 .. ceil(L/block_size)-1 must be in [0, num_blocks)
+ *   seq_lens     int32 [num_seqs], each in [0, max_seq_len]
+ *   max_seq_len  host-side upper bound of seq_lens; sizes the launch without
+ *                a device->host copy; must be <= max_blocks_per_seq*block_size
+ *   scale        score scale (the pages use 1/sqrt(head_dim))
+ *   kv_dtype     PKV_F32, PKV_F16 or PKV_BF16
+ *   out_dtype    kv_dtype or PKV_F32 (narrowing rounds to nearest even)
+ *   partition_size  0: the library chooses; otherwise the number of tokens
+ *                of one sequence partition (a multiple of 16 and of
+ *                block_size, at most 16384 tokens when it does not split the
+ *                longest sequence). Sequences longer than one partition are
+ *                split; each partition's (max, sum, weighted V) is written to
+ *                the workspace and a second kernel merges them.
+ *   workspace    device scratch of at least paged_attn_workspace_size(...)
+ *                bytes for the same arguments (may be NULL when that is 0);
+ *                its contents need no initialisation and are garbage after.
+ * Supported: head_dim 64 or 128; block_size 8, 16 or 32; 1 <= G <= 16.
+ */
+int paged_attn_decode(void* out, const void* query, const void* key_cache,
+                      const void* value_cache, const int32_t* block_table,
+                      const int32_t* seq_lens, int num_seqs, int num_heads,
+                      int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, int max_blocks_per_seq, int max_seq_len,
+                      float scale, int kv_dtype, int out_dtype,
+                      int partition_size, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_attn_partition_tokens - the partition length paged_attn_decode uses
+ * for these arguments (resolving partition_size = 0), or a negative
+ * pkv_status for invalid arguments. A value >= max_seq_len means no split.
+ */
+int paged_attn_partition_tokens(int num_seqs, int num_kv_heads, int block_size,
+                                int max_seq_len, int partition_size);
+
+/*
+ * paged_attn_workspace_size - bytes of split-K workspace paged_attn_decode
+ * needs for these arguments: fp32 (max, sum) pairs and head_dim weighted-V
+ * partial sums per (sequence, head, partition); 0 when no sequence is split
+ * or the arguments are invalid.
+ */
+size_t paged_attn_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
+                                 int head_dim, int block_size, int max_seq_len,
+                                 int partition_size);
+
+/*
+ * reshape_and_cache - write the K and V of each new token into its slot of
+ * the pools. slot_mapping[i] = physical_block * block_size + offset, the slot
+ * the block engine hands out for the token ("LLM inference engine
+ * internals" section 2.3, append_slot; growth as in "vLLM core concepts"
+ * section 4.2.2). key_cache[slot / block_size, slot % block_size] = key[i],
+ * and the same for value, as bit copies. slot < 0 means "no slot": the token
+ * is skipped. Slots must be distinct (else which write lands is
+ * unspecified); slots >= num_blocks*block_size are skipped.
+ *
+ *   key, value        [num_tokens, num_kv_heads, head_dim], dtype
+ *   key_cache, value_cache  [num_blocks, block_size, num_kv_heads, head_dim]
+ *   slot_mapping      int64 [num_tokens]
+ */
+int reshape_and_cache(const void* key, const void* value, void* key_cache,
+                      void* value_cache, const int64_t* slot_mapping,
+                      int num_tokens, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, int dtype,
+                      hipStream_t stream);
+
+/*
+ * copy_blocks - copy-on-write block copies: for each pair (src, dst) of
+ * block_mapping, the whole physical block src of both pools (every slot, every
+ * KV head) is copied to block dst. A block shared by several sequences is
+ * copied before one of them modifies it ("vLLM core concepts" section 4.2.2;
+ * "LLM inference engine internals" sections 3.1 (blocks_to_copy) and 3.3;
+ * "PagedAttention principle" section 5). The destinations must be distinct
+ * and disjoint from every source (then the result equals reading every
+ * source before writing any destination). Pairs with an id outside
+ * [0, num_blocks) are skipped.
+ *
+ *   block_mapping  int64 [num_pairs, 2], row = (src, dst)
+ */
+int copy_blocks(void* key_cache, void* value_cache,
+                const int64_t* block_mapping, int num_pairs, int num_blocks,
+                int block_size, int num_kv_heads, int head_dim, int dtype,
+                hipStream_t stream);
+
+/*
+ * pagedkv_check_decode_inputs - the contract check that the fast path does
+ * not make. Counts, on the device, the block-table entries of used logical
+ * blocks outside [0, num_blocks) and the seq_lens outside [0, max_seq_len];
+ * writes the two counts to counts[0] and counts[1] (device int32[2], cleared
+ * by the call). Asynchronous like the others; read counts after the stream
+ * has finished.
+ */
+int pagedkv_check_decode_inputs(const int32_t* block_table,
+                                const int32_t* seq_lens, int num_seqs,
+                                int block_size, int num_blocks,
+                                int max_blocks_per_seq, int max_seq_len,
+                                int32_t* counts, hipStream_t stream);
+
+/* pagedkv_status_string - a static, NUL-terminated name for a status code. */
+const char* pagedkv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H_ */

@@ -1,0 +1,158 @@
+"""Paged KV-cache decode attention for AMD MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``include/pagedkv.h``: it only turns
+torch tensors (device memory) and the current HIP stream into the pointers
+and sizes the library takes. Every step of the computation runs in the HIP
+kernels of ``libpagedkv.so``; there is no Python or CPU fallback.
+
+    paged_attn_decode(out, query, key_cache, value_cache, block_table,
+                      seq_lens, scale, max_seq_len, partition_size=0,
+                      workspace=None)
+    reshape_and_cache(key, value, key_cache, value_cache, slot_mapping)
+    copy_blocks(key_cache, value_cache, block_mapping)
+
+Shapes (all dense, on one GPU): query/out ``[num_seqs, num_heads,
+head_dim]``; pools ``[num_blocks, block_size, num_kv_heads, head_dim]``;
+block_table int32 ``[num_seqs, max_blocks_per_seq]``; seq_lens int32
+``[num_seqs]``; slot_mapping int64 ``[num_tokens]``; block_mapping int64
+``[num_pairs, 2]``.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from ._lib import (PKV_BF16, PKV_F16, PKV_F32, LIB_PATH, PagedKVError,  # noqa: F401
+                   check, lib, status_string)
+
+_DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+
+
+def dtype_code(dtype: torch.dtype) -> int:
+    try:
+        return _DTYPE_CODE[dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {dtype}") from None
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libpagedkv must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor, stream) -> int | None:
+    if stream is not None:
+        return int(getattr(stream, "cuda_stream", stream))
+    if t.is_cuda:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def paged_attn_partition_tokens(num_seqs: int, num_kv_heads: int, block_size: int,
+                                max_seq_len: int, partition_size: int = 0) -> int:
+    r = lib().paged_attn_partition_tokens(num_seqs, num_kv_heads, block_size, max_seq_len,
+                                          partition_size)
+    if r < 0:
+        raise PagedKVError(r, "paged_attn_partition_tokens")
+    return r
+
+
+def paged_attn_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                              block_size: int, max_seq_len: int, partition_size: int = 0) -> int:
+    return int(lib().paged_attn_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                                               block_size, max_seq_len, partition_size))
+
+
+def workspace_for(query: torch.Tensor, key_cache: torch.Tensor, max_seq_len: int,
+                  partition_size: int = 0) -> torch.Tensor | None:
+    """A device buffer big enough for paged_attn_decode with these shapes."""
+    S, H, D = query.shape
+    NB, bs, Hkv, _ = key_cache.shape
+    n = paged_attn_workspace_size(S, H, Hkv, D, bs, max_seq_len, partition_size)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=query.device)
+
+
+def paged_attn_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                      value_cache: torch.Tensor, block_table: torch.Tensor,
+                      seq_lens: torch.Tensor, scale: float, max_seq_len: int,
+                      partition_size: int = 0, workspace: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """Decode attention of one query token per sequence over the paged pool.
+
+    ``workspace`` must hold ``paged_attn_workspace_size(...)`` bytes when a
+    sequence is split; with ``workspace=None`` one is allocated by torch."""
+    _require(query.dim() == 3 and out.shape == query.shape, "query/out must be [S, H, D]")
+    _require(key_cache.dim() == 4 and value_cache.shape == key_cache.shape,
+             "pools must be [num_blocks, block_size, num_kv_heads, head_dim]")
+    _require(block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32,
+             "block_table and seq_lens must be int32")
+    _require(query.dtype == key_cache.dtype == value_cache.dtype, "query and pools share a dtype")
+    S, H, D = query.shape
+    NB, bs, Hkv, D2 = key_cache.shape
+    _require(D2 == D, "head_dim of query and pools differ")
+    _require(block_table.dim() == 2 and block_table.shape[0] == S and seq_lens.shape == (S,),
+             "block_table must be [S, max_blocks] and seq_lens [S]")
+    if workspace is None:
+        workspace = workspace_for(query, key_cache, max_seq_len, partition_size)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().paged_attn_decode(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_table),
+        _ptr(seq_lens), S, H, Hkv, D, bs, NB, block_table.shape[1], int(max_seq_len),
+        float(scale), dtype_code(query.dtype), dtype_code(out.dtype), int(partition_size),
+        _ptr(workspace), ws_bytes, _stream(query, stream))
+    check(st, "paged_attn_decode")
+    return out
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                      value_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                      stream=None) -> None:
+    """Write each new token's K and V into slot_mapping[i] of the pools."""
+    _require(key.dim() == 3 and value.shape == key.shape, "key/value must be [T, Hkv, D]")
+    _require(key_cache.dim() == 4 and value_cache.shape == key_cache.shape, "pool shape")
+    _require(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (key.shape[0],),
+             "slot_mapping must be int64 [T]")
+    _require(key.dtype == key_cache.dtype == value.dtype == value_cache.dtype, "dtypes differ")
+    NB, bs, Hkv, D = key_cache.shape
+    _require(tuple(key.shape[1:]) == (Hkv, D), "key rows must be [num_kv_heads, head_dim]")
+    st = lib().reshape_and_cache(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                                 _ptr(slot_mapping), key.shape[0], Hkv, D, bs, NB,
+                                 dtype_code(key.dtype), _stream(key_cache, stream))
+    check(st, "reshape_and_cache")
+
+
+def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor,
+                block_mapping: torch.Tensor, stream=None) -> None:
+    """Copy whole blocks src -> dst (K and V) for each row (src, dst)."""
+    _require(key_cache.dim() == 4 and value_cache.shape == key_cache.shape, "pool shape")
+    _require(block_mapping.dtype == torch.int64 and block_mapping.dim() == 2
+             and block_mapping.shape[1] == 2, "block_mapping must be int64 [P, 2]")
+    _require(key_cache.dtype == value_cache.dtype, "dtypes differ")
+    NB, bs, Hkv, D = key_cache.shape
+    st = lib().copy_blocks(_ptr(key_cache), _ptr(value_cache), _ptr(block_mapping),
+                           block_mapping.shape[0], NB, bs, Hkv, D, dtype_code(key_cache.dtype),
+                           _stream(key_cache, stream))
+    check(st, "copy_blocks")
+
+
+def check_decode_inputs(block_table: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
+                        num_blocks: int, max_seq_len: int, stream=None) -> tuple[int, int]:
+    """(bad block-table entries, bad lengths), counted on the device; syncs."""
+    counts = torch.empty(2, dtype=torch.int32, device=block_table.device)
+    S = block_table.shape[0]
+    st = lib().pagedkv_check_decode_inputs(_ptr(block_table), _ptr(seq_lens), S, block_size,
+                                           num_blocks, block_table.shape[1], max_seq_len,
+                                           _ptr(counts), _stream(block_table, stream))
+    check(st, "pagedkv_check_decode_inputs")
+    c = counts.cpu()
+    return int(c[0]), int(c[1])

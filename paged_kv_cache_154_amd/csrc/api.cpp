@@ -1,0 +1,185 @@
+// C-ABI entry points (declared in include/pagedkv.h): host-side argument
+// checks, partition and workspace sizing, dispatch to the kernels. Nothing
+// here allocates, synchronises or keeps state.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "pagedkv.h"
+#include "pagedkv_internal.h"
+
+namespace {
+
+constexpr int kDefaultPartition = 512;
+
+int elem_bytes(int dtype) {
+  switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_F16:
+    case PKV_BF16: return 2;
+    default: return 0;
+  }
+}
+
+bool supported_block_size(int bs) { return bs == 8 || bs == 16 || bs == 32; }
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+
+// Partition length for these arguments, or a negative status.
+int resolve_partition(int num_seqs, int num_kv_heads, int block_size, int max_seq_len,
+                      int partition_size) {
+  (void)num_seqs;
+  (void)num_kv_heads;
+  if (partition_size < 0) return PKV_ERR_SHAPE;
+  if (!supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
+  int P = partition_size == 0 ? kDefaultPartition : partition_size;
+  if (P % pkv::kTile != 0 || P % block_size != 0) return PKV_ERR_SHAPE;
+  if (P >= max_seq_len) {
+    // one partition per sequence: its block-table slice must fit in LDS
+    if (max_seq_len > pkv::kMaxPartition) return PKV_ERR_UNSUPPORTED;
+  } else if (P > pkv::kMaxPartition) {
+    return PKV_ERR_UNSUPPORTED;
+  }
+  return P;
+}
+
+int num_partitions(int max_seq_len, int P) {
+  if (max_seq_len <= P) return 1;
+  return (max_seq_len + P - 1) / P;
+}
+
+size_t split_workspace_bytes(int num_seqs, int num_heads, int head_dim, int np) {
+  if (np <= 1) return 0;
+  return (size_t)num_seqs * num_heads * np * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_partition_tokens(int num_seqs, int num_kv_heads, int block_size, int max_seq_len,
+                                int partition_size) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || max_seq_len < 0) return PKV_ERR_SHAPE;
+  return resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
+}
+
+size_t paged_attn_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                 int block_size, int max_seq_len, int partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return 0;
+  if (!supported_head_dim(head_dim)) return 0;
+  const int P = resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
+  if (P <= 0) return 0;
+  return split_workspace_bytes(num_seqs, num_heads, head_dim, num_partitions(max_seq_len, P));
+}
+
+int paged_attn_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                      const int32_t* block_table, const int32_t* seq_lens, int num_seqs,
+                      int num_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, int max_blocks_per_seq, int max_seq_len, float scale,
+                      int kv_dtype, int out_dtype, int partition_size, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  if (num_seqs < 0) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_table || !seq_lens)
+    return PKV_ERR_NULL;
+  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+  const int group = num_heads / num_kv_heads;
+  if (group > 16) return PKV_ERR_UNSUPPORTED;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
+  if (elem_bytes(kv_dtype) == 0) return PKV_ERR_UNSUPPORTED;
+  if (out_dtype != kv_dtype && out_dtype != PKV_F32) return PKV_ERR_UNSUPPORTED;
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0) return PKV_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size < max_seq_len) return PKV_ERR_SHAPE;
+  if (!isfinite(scale)) return PKV_ERR_SHAPE;
+  const int P = resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
+  if (P < 0) return P;
+  const int np = num_partitions(max_seq_len, P);
+  if ((int64_t)num_seqs * num_kv_heads * np > (int64_t)INT32_MAX) return PKV_ERR_SHAPE;
+  const size_t need = split_workspace_bytes(num_seqs, num_heads, head_dim, np);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+
+  pkv::DecodeParams p{};
+  p.out = out;
+  p.q = query;
+  p.k = key_cache;
+  p.v = value_cache;
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.ws_o = need ? static_cast<float*>(workspace) : nullptr;
+  p.ws_ml = need ? static_cast<float*>(workspace) + (size_t)num_seqs * num_heads * np * head_dim
+                 : nullptr;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = group;
+  p.num_blocks = num_blocks;
+  p.max_blocks = max_blocks_per_seq;
+  p.max_seq_len = max_seq_len;
+  p.partition = P;
+  p.num_partitions = np;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
+  const hipError_t e = pkv::launch_decode(p, kv_dtype, head_dim, block_size, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
+                      const int64_t* slot_mapping, int num_tokens, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, int dtype, hipStream_t stream) {
+  if (num_tokens < 0) return PKV_ERR_SHAPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PKV_ERR_NULL;
+  if (num_kv_heads <= 0 || num_blocks <= 0) return PKV_ERR_SHAPE;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return PKV_ERR_UNSUPPORTED;
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * eb;
+  if (row_bytes > INT32_MAX / 2) return PKV_ERR_SHAPE;
+  const hipError_t e = pkv::launch_reshape_and_cache(
+      key, value, key_cache, value_cache, slot_mapping, num_tokens, (int)row_bytes,
+      (int64_t)num_blocks * block_size, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping, int num_pairs,
+                int num_blocks, int block_size, int num_kv_heads, int head_dim, int dtype,
+                hipStream_t stream) {
+  if (num_pairs < 0) return PKV_ERR_SHAPE;
+  if (num_pairs == 0) return PKV_OK;
+  if (!key_cache || !value_cache || !block_mapping) return PKV_ERR_NULL;
+  if (num_kv_heads <= 0 || num_blocks <= 0) return PKV_ERR_SHAPE;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return PKV_ERR_UNSUPPORTED;
+  const int64_t block_bytes = (int64_t)block_size * num_kv_heads * head_dim * eb;
+  const hipError_t e = pkv::launch_copy_blocks(key_cache, value_cache, block_mapping, num_pairs,
+                                               num_blocks, block_bytes, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int pagedkv_check_decode_inputs(const int32_t* block_table, const int32_t* seq_lens, int num_seqs,
+                                int block_size, int num_blocks, int max_blocks_per_seq,
+                                int max_seq_len, int32_t* counts, hipStream_t stream) {
+  if (num_seqs < 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0)
+    return PKV_ERR_SHAPE;
+  if (!counts) return PKV_ERR_NULL;
+  if (num_seqs > 0 && (!block_table || !seq_lens)) return PKV_ERR_NULL;
+  if (!supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
+  const hipError_t e = pkv::launch_check_decode_inputs(block_table, seq_lens, num_seqs, block_size,
+                                                       num_blocks, max_blocks_per_seq, max_seq_len,
+                                                       counts, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+const char* pagedkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_NULL: return "PKV_ERR_NULL: a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "PKV_ERR_SHAPE: inconsistent or negative sizes";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED: dtype, head_dim, block_size or group size not built";
+    case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE: split-K workspace missing or too small";
+    case PKV_ERR_HIP: return "PKV_ERR_HIP: the HIP runtime reported a launch error";
+    default: return "unknown pagedkv status";
+  }
+}
+
+}  // extern "C"

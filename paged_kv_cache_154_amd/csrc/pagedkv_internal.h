@@ -1,0 +1,60 @@
+// Internal declarations shared by the kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Launch parameters of the decode kernels (host-validated).
+struct DecodeParams {
+  void* out;
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* ws_o;   // [S, H, NP, D] weighted-V partial sums (split only)
+  float* ws_ml;  // [S, H, NP, 2] (running max in log2 units, sum of weights)
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int group;           // num_heads / num_kv_heads
+  int num_blocks;
+  int max_blocks;      // block-table row length
+  int max_seq_len;
+  int partition;       // tokens per partition (multiple of 16 and block_size)
+  int num_partitions;  // ceil(max_seq_len / partition), >= 1
+  float scale_log2;    // scale * log2(e)
+  int out_f32;         // 1: out is fp32; 0: out has the KV dtype
+};
+
+// Tokens a wave handles per step (one MFMA tile of keys).
+constexpr int kTile = 16;
+// Waves per decode workgroup.
+constexpr int kWaves = 4;
+// Largest partition whose block-table slice is staged in LDS.
+constexpr int kMaxPartition = 16384;
+
+hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim,
+                         int block_size, hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value,
+                                    void* key_cache, void* value_cache,
+                                    const int64_t* slot_mapping, int num_tokens,
+                                    int row_bytes, int64_t num_slots,
+                                    hipStream_t stream);
+
+hipError_t launch_copy_blocks(void* key_cache, void* value_cache,
+                              const int64_t* block_mapping, int num_pairs,
+                              int num_blocks, int64_t block_bytes,
+                              hipStream_t stream);
+
+hipError_t launch_check_decode_inputs(const int32_t* block_table,
+                                      const int32_t* seq_lens, int num_seqs,
+                                      int block_size, int num_blocks,
+                                      int max_blocks, int max_seq_len,
+                                      int32_t* counts, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,340 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bars: bit-exact for reshape_and_cache and copy_blocks; max-abs error on the
+decode output at most 1e-5 (fp32 KV), 2e-3 (fp16 KV) or 8e-3 (bf16 KV),
+with fp32 or KV-dtype output; bitwise invariants (placement, NaN tails,
+copy-on-write remap, run-to-run); split-K agreement.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_154_amd as pkv
+from paged_kv_cache_154_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-5, torch.float16: 2e-3, torch.bfloat16: 8e-3}
+DEV = "cuda"
+
+
+def say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def to_dev(wl):
+    d = dict(q=wl.query.to(DEV), kc=wl.key_cache.to(DEV), vc=wl.value_cache.to(DEV),
+             bt=torch.from_numpy(wl.block_table).to(DEV),
+             sl=torch.from_numpy(wl.seq_lens).to(DEV))
+    if wl.slot_mapping is not None:
+        d["nk"] = wl.new_key.to(DEV)
+        d["nv"] = wl.new_value.to(DEV)
+        d["slots"] = torch.from_numpy(wl.slot_mapping).to(DEV)
+    if wl.block_mapping is not None:
+        d["pairs"] = torch.from_numpy(wl.block_mapping).to(DEV)
+    return d
+
+
+def gpu_step(wl, d, out_dtype=None, partition_size=None, table=None):
+    """Cache ops of the step (scatter, copy-on-write), then decode."""
+    if "slots" in d:
+        pkv.reshape_and_cache(d["nk"], d["nv"], d["kc"], d["vc"], d["slots"])
+    if "pairs" in d:
+        pkv.copy_blocks(d["kc"], d["vc"], d["pairs"])
+    out = torch.empty(wl.query.shape, dtype=out_dtype or wl.dtype, device=DEV)
+    P = wl.partition_size if partition_size is None else partition_size
+    pkv.paged_attn_decode(out, d["q"], d["kc"], d["vc"], d["bt"] if table is None else table,
+                          d["sl"], wl.scale, wl.max_seq_len, P)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_step(wl, seqs=None):
+    kc, vc = wl.key_cache, wl.value_cache
+    if wl.slot_mapping is not None:
+        kc, vc = oracle.reshape_and_cache(wl.new_key, wl.new_value, kc, vc, wl.slot_mapping)
+    if wl.block_mapping is not None:
+        kc, vc = oracle.copy_blocks(kc, vc, wl.block_mapping)
+    out = oracle.decode(wl.query, kc, vc, wl.block_table, wl.seq_lens, wl.scale, seqs=seqs)
+    return out, kc, vc
+
+
+def max_err(gpu_out, ref, seqs=None):
+    """Max-abs error. For a narrowed (fp16/bf16) output the final rounding to
+    nearest-even of a value of magnitude |ref| may add up to half a unit in
+    the last place of the output type; that share is taken off first, so the
+    bar applies to the fp32-accumulated result in both cases."""
+    g = gpu_out.detach().to("cpu", torch.float64).numpy()
+    if seqs is not None:
+        g, ref = g[seqs], ref[seqs]
+    if not g.size:
+        return 0.0
+    err = np.abs(g - ref)
+    mant = {torch.float16: 10, torch.bfloat16: 7}.get(gpu_out.dtype)
+    if mant is not None:
+        a = np.maximum(np.abs(ref), np.finfo(np.float64).tiny)
+        half_ulp = np.exp2(np.floor(np.log2(a)) - mant - 1)
+        err = np.maximum(err - half_ulp, 0.0)
+    return float(err.max())
+
+
+def bits(t):
+    return t.view({2: torch.int16, 4: torch.int32}[t.element_size()])
+
+
+# ----------------------------------------------------------------------------
+# small and medium shapes: every output element against the oracle
+# ----------------------------------------------------------------------------
+
+SMALL = [
+    # id, dtype, D, bs, H, Hkv, lens, partition
+    ("f32_d64_bs16_mha", torch.float32, 64, 16, 4, 4, [1, 17, 33, 50], 0),
+    ("f32_d128_bs8_g2", torch.float32, 128, 8, 8, 4, [3, 8, 9, 129, 300], 0),
+    ("f16_d128_bs16_g4", torch.float16, 128, 16, 32, 8, [1, 15, 16, 17, 31, 33, 200, 1000], 0),
+    ("f16_d64_bs32_g8", torch.float16, 64, 32, 16, 2, [2, 31, 32, 33, 64, 513], 0),
+    ("bf16_d128_bs16_g4", torch.bfloat16, 128, 16, 32, 8, [5, 16, 100, 511, 512, 513, 2000], 0),
+    ("bf16_d128_bs8_g1", torch.bfloat16, 128, 8, 4, 4, [7, 8, 9, 77, 640], 0),
+    ("bf16_d64_bs16_g16", torch.bfloat16, 64, 16, 16, 1, [1, 40, 300], 0),
+    ("bf16_d128_bs32_g3", torch.bfloat16, 128, 32, 6, 2, [1, 95, 96, 97], 0),
+    ("f16_d128_bs32_g8_split64", torch.float16, 128, 32, 64, 8, [32, 65, 300, 1029], 64),
+    ("bf16_d128_bs8_g4_split128", torch.bfloat16, 128, 8, 32, 8, [8, 127, 128, 129, 1500], 128),
+    ("f32_d64_bs16_split16", torch.float32, 64, 16, 4, 2, [1, 16, 17, 80], 16),
+    ("bf16_d128_bs16_g4_split512", torch.bfloat16, 128, 16, 32, 8, [600, 1024, 1025, 3000], 512),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_cases_match_oracle(case):
+    name, dt, D, bs, H, Hkv, lens, P = case
+    wl = W.custom(zlib.crc32(name.encode()) % 10000 + 100, seq_lens=lens, num_heads=H, num_kv_heads=Hkv,
+                  head_dim=D, block_size=bs, dtype=dt, partition_size=P, new_token=True)
+    ref, _, _ = oracle_step(wl)
+    for out_dt in dict.fromkeys([dt, torch.float32]):
+        say(f"{name} out={out_dt}")
+        d = to_dev(wl)
+        out = gpu_step(wl, d, out_dtype=out_dt)
+        assert torch.isfinite(out).all()
+        err = max_err(out, ref)
+        say(f"{name} out={out_dt} max_abs_err={err:.3g}")
+        assert err <= TOL[dt], (name, out_dt, err)
+
+
+def test_seq_len_one_is_the_v_row_bit_exact():
+    for dt in (torch.float32, torch.float16, torch.bfloat16):
+        wl = W.custom(7, seq_lens=[1, 1, 1, 1], num_heads=8, num_kv_heads=2, head_dim=128,
+                      block_size=16, dtype=dt)
+        say(f"seq_len=1 {dt}")
+        out = gpu_step(wl, to_dev(wl), out_dtype=dt).cpu()
+        for s in range(4):
+            vrow = wl.value_cache[int(wl.block_table[s, 0]), 0]      # [Hkv, D]
+            for h in range(8):
+                assert torch.equal(bits(out[s, h]), bits(vrow[h // 4])), (dt, s, h)
+
+
+def test_zero_length_sequences_give_zero_rows():
+    wl = W.custom(8, seq_lens=[0, 37, 0, 1], num_heads=8, num_kv_heads=8, head_dim=64,
+                  block_size=8, dtype=torch.bfloat16)
+    d = to_dev(wl)
+    ref, _, _ = oracle_step(wl)
+    for P in (0, 16):
+        say(f"zero-length rows P={P}")
+        out = gpu_step(wl, d, out_dtype=torch.float32, partition_size=P)
+        assert torch.equal(out[0], torch.zeros_like(out[0]))
+        assert torch.equal(out[2], torch.zeros_like(out[2]))
+        assert max_err(out, ref) <= TOL[torch.bfloat16]
+
+
+def test_max_seq_len_above_actual_lengths():
+    """The launch is sized from the host bound; partitions past a sequence's
+    end exit early."""
+    wl = W.custom(9, seq_lens=[10, 300, 47], num_heads=16, num_kv_heads=4, head_dim=128,
+                  block_size=16, dtype=torch.float16, max_blocks_per_seq=128)
+    d = to_dev(wl)
+    ref, _, _ = oracle_step(wl)
+    out = torch.empty(wl.query.shape, dtype=torch.float32, device=DEV)
+    say("max_seq_len 2048 over lengths <= 300")
+    pkv.paged_attn_decode(out, d["q"], d["kc"], d["vc"], d["bt"], d["sl"], wl.scale, 2048, 64)
+    torch.cuda.synchronize()
+    assert max_err(out, ref) <= TOL[torch.float16]
+
+
+# ----------------------------------------------------------------------------
+# cache operations: bit-exact
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.float16, torch.bfloat16])
+def test_reshape_and_cache_bit_exact(dt):
+    NB, bs, Hkv, D = 40, 16, 4, 128
+    g = torch.Generator().manual_seed(3)
+    kc = torch.randn(NB, bs, Hkv, D, generator=g).to(dt)
+    vc = torch.randn(NB, bs, Hkv, D, generator=g).to(dt)
+    T = 50
+    slots = torch.randperm(NB * bs, generator=g)[:T].to(torch.int64)
+    slots[::7] = -1                                    # "no slot": skipped
+    key = torch.randn(T, Hkv, D, generator=g).to(dt)
+    value = torch.randn(T, Hkv, D, generator=g).to(dt)
+    key[3, 1, 5] = float("nan")
+    ek, ev = oracle.reshape_and_cache(key, value, kc, vc, slots.numpy())
+    dk, dv = kc.to(DEV), vc.to(DEV)
+    say(f"reshape_and_cache {dt}")
+    pkv.reshape_and_cache(key.to(DEV), value.to(DEV), dk, dv, slots.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(bits(dk.cpu()), bits(ek)) and torch.equal(bits(dv.cpu()), bits(ev))
+
+
+@pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16, torch.float32])
+def test_copy_blocks_bit_exact(dt):
+    NB, bs, Hkv, D = 64, 16, 8, 64
+    g = torch.Generator().manual_seed(4)
+    kc = torch.randn(NB, bs, Hkv, D, generator=g).to(dt)
+    vc = torch.randn(NB, bs, Hkv, D, generator=g).to(dt)
+    perm = torch.randperm(NB, generator=g)
+    pairs = torch.stack([perm[:10], perm[10:20]], dim=1).to(torch.int64)   # disjoint src/dst
+    pairs[3, 0] = pairs[0, 0]                       # one source copied twice
+    ek, ev = oracle.copy_blocks(kc, vc, pairs.numpy())
+    dk, dv = kc.to(DEV), vc.to(DEV)
+    say(f"copy_blocks {dt}")
+    pkv.copy_blocks(dk, dv, pairs.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(bits(dk.cpu()), bits(ek)) and torch.equal(bits(dv.cpu()), bits(ev))
+
+
+def test_check_decode_inputs_counts_violations():
+    bt = torch.tensor([[0, 5, 99, -3], [1, 2, 3, 4], [7, 1000, 0, 0]], dtype=torch.int32)
+    sl = torch.tensor([40, 70, 17], dtype=torch.int32)     # 70 > max_seq_len 64
+    say("check_decode_inputs")
+    bad_blk, bad_len = pkv.check_decode_inputs(bt.to(DEV), sl.to(DEV), block_size=16,
+                                               num_blocks=10, max_seq_len=64)
+    # seq 0 uses 3 blocks: 99 is bad; seq 1 is clamped to 64 tokens = 4 blocks, all
+    # good; seq 2 uses 2 blocks: 1000 is bad
+    assert (bad_blk, bad_len) == (2, 1)
+
+
+# ----------------------------------------------------------------------------
+# invariants (bitwise)
+# ----------------------------------------------------------------------------
+
+def test_placement_permutation_is_bitwise_invariant():
+    wl = W.custom(11, seq_lens=[33, 700, 129, 1], num_heads=32, num_kv_heads=8,
+                  head_dim=128, block_size=16, dtype=torch.bfloat16)
+    d = to_dev(wl)
+    say("placement permutation")
+    out = gpu_step(wl, d, out_dtype=torch.float32)
+    perm = np.random.default_rng(1).permutation(wl.num_blocks)
+    inv = torch.from_numpy(np.argsort(perm))
+    d2 = dict(d)
+    d2["kc"] = wl.key_cache[inv].to(DEV)
+    d2["vc"] = wl.value_cache[inv].to(DEV)
+    d2["bt"] = torch.from_numpy(perm[wl.block_table].astype(np.int32)).to(DEV)
+    out2 = gpu_step(wl, d2, out_dtype=torch.float32)
+    assert torch.equal(bits(out), bits(out2))
+
+
+def test_unused_slots_are_never_read():
+    """NaN in unused tail slots and free blocks vs zeros there: bitwise equal."""
+    wl = W.custom(12, seq_lens=[1, 15, 17, 100, 250], num_heads=16, num_kv_heads=4,
+                  head_dim=64, block_size=32, dtype=torch.float16)
+    d = to_dev(wl)
+    say("NaN tails")
+    out = gpu_step(wl, d, out_dtype=torch.float32)
+    d0 = dict(d)
+    d0["kc"] = torch.nan_to_num(wl.key_cache, nan=0.0).to(DEV)
+    d0["vc"] = torch.nan_to_num(wl.value_cache, nan=0.0).to(DEV)
+    out0 = gpu_step(wl, d0, out_dtype=torch.float32)
+    assert torch.isfinite(out).all()
+    assert torch.equal(bits(out), bits(out0))
+
+
+def test_run_to_run_determinism():
+    wl = W.custom(13, seq_lens=[3000, 17, 1200], num_heads=32, num_kv_heads=8,
+                  head_dim=128, block_size=16, dtype=torch.bfloat16)
+    d = to_dev(wl)
+    say("determinism")
+    a = gpu_step(wl, d, out_dtype=torch.float32, partition_size=256)
+    b = gpu_step(wl, d, out_dtype=torch.float32, partition_size=256)
+    assert torch.equal(bits(a), bits(b))
+
+
+def test_split_partitions_agree_with_unsplit():
+    wl = W.custom(14, seq_lens=[2500, 513, 64, 4000], num_heads=32, num_kv_heads=8,
+                  head_dim=128, block_size=16, dtype=torch.bfloat16)
+    d = to_dev(wl)
+    say("split-K agreement")
+    whole = gpu_step(wl, d, out_dtype=torch.float32, partition_size=4096)
+    for P in (64, 128, 512):
+        part = gpu_step(wl, d, out_dtype=torch.float32, partition_size=P)
+        rel = ((part - whole).abs().max() / whole.abs().max()).item()
+        say(f"split P={P} rel={rel:.3g}")
+        assert rel <= 1e-5
+
+
+def test_copy_on_write_remap_is_bitwise_invariant():
+    """Decode through the private copies made by copy_blocks equals decode
+    through the shared original block."""
+    wl = W.prefix_share(groups=4, n=3, prefix=256, max_suffix=100)
+    d = to_dev(wl)
+    say("copy-on-write remap")
+    after = gpu_step(wl, d, out_dtype=torch.float32)            # copies, remapped table
+    d2 = to_dev(wl)
+    d2.pop("pairs")
+    before_tbl = torch.from_numpy(wl.block_table_before_cow).to(DEV)
+    before = gpu_step(wl, d2, out_dtype=torch.float32, table=before_tbl)
+    assert torch.equal(bits(after), bits(before))
+
+
+# ----------------------------------------------------------------------------
+# the five page-shaped workloads at full size
+# ----------------------------------------------------------------------------
+
+def _sample(wl, n=48):
+    lens = wl.seq_lens
+    order = np.argsort(lens, kind="stable")
+    pick = set(order[:8].tolist()) | set(order[-8:].tolist())
+    rng = np.random.default_rng(wl.seed)
+    rest = [s for s in range(wl.num_seqs) if s not in pick]
+    pick |= set(rng.choice(rest, size=min(len(rest), n - len(pick)), replace=False).tolist())
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("config", [1, 2, 3, 4, 5])
+def test_config_parity(config):
+    wl = W.make(config)
+    say(f"config {config} {wl.name}: S={wl.num_seqs} tokens={wl.num_tokens} "
+        f"max_len={wl.max_seq_len} P={wl.partition_size}")
+    seqs = None if wl.num_seqs <= 8 else _sample(wl)
+    ref, ek, ev = oracle_step(wl, seqs=seqs)
+    for out_dt in (torch.float32, wl.dtype):
+        d = to_dev(wl)
+        out = gpu_step(wl, d, out_dtype=out_dt)
+        if out_dt == torch.float32:
+            # bit-exact cache ops over the whole pool
+            assert torch.equal(bits(d["kc"].cpu()), bits(ek))
+            assert torch.equal(bits(d["vc"].cpu()), bits(ev))
+        assert torch.isfinite(out).all()
+        err = max_err(out, ref, seqs)
+        say(f"config {config} out={out_dt} max_abs_err={err:.3g} on {len(seqs or [])} seqs")
+        assert err <= TOL[wl.dtype], (config, out_dt, err)
+        if out_dt == torch.float32 and seqs is not None:
+            _convex_hull_property(wl, d, out)
+
+
+def _convex_hull_property(wl, d, out):
+    """Every output is a convex combination of its sequence's V rows, so each
+    element lies between that KV head's per-dimension min and max over the
+    sequence (checked for every sequence, on the GPU, with torch)."""
+    bs, G = wl.block_size, wl.num_heads // wl.num_kv_heads
+    vc = d["vc"]
+    for s in range(wl.num_seqs):
+        L = int(wl.seq_lens[s])
+        nb = (L + bs - 1) // bs
+        blocks = d["bt"][s, :nb].long()
+        v = vc[blocks].reshape(nb * bs, wl.num_kv_heads, wl.head_dim)[:L].float()
+        lo = v.amin(0).repeat_interleave(G, 0)
+        hi = v.amax(0).repeat_interleave(G, 0)
+        o = out[s]
+        slack = 1e-5 * (1 + hi.abs())
+        assert bool(((o >= lo - slack) & (o <= hi + slack)).all()), s
