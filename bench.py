@@ -18,6 +18,7 @@ launches on.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import statistics
@@ -30,6 +31,29 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
 METRIC = "paged decode attention: KV GB/s and % of HBM peak; sequences/s per layer"
+
+
+def kernel_source_hash():
+    """sha256 of the decode kernel sources (as in the traffic profile)."""
+    h = hashlib.sha256()
+    for f in ("decode.hip", "pagedkv_internal.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_154_amd", "csrc", f)) as fh:
+            h.update(fh.read().encode())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode call from the committed rocprofv3 counter runs,
+    or None when the kernel sources changed after those runs."""
+    path = os.path.join(ROOT, "profiles", "decode_llama3_8b_bf16_traffic.json")
+    try:
+        with open(path) as fh:
+            doc = json.load(fh)
+    except OSError:
+        return None
+    if doc.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return doc.get("traffic_bytes_per_launch")
 
 
 def log(msg):
@@ -68,6 +92,9 @@ def main():
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (torch), 10 times: the "
+                         "reference for scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -81,6 +108,14 @@ def main():
     from paged_kv_cache_154_amd import workloads as W
 
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied 1 GiB x 10")
+        return
     log("generating workload (Llama-3-8B-shaped layer)")
     wl = W.llama3_8b()
     P = wl.partition_size if args.partition_size is None else args.partition_size
@@ -165,7 +200,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "kernel": "paged_attn_decode (decode_partition_kernel + decode_reduce_kernel)",
         },
         "cpu_baseline": None,

@@ -85,16 +85,18 @@ enum pkv_status {
  *   scale        score scale (the pages use 1/sqrt(head_dim))
  *   kv_dtype     PKV_F32, PKV_F16 or PKV_BF16
  *   out_dtype    kv_dtype or PKV_F32 (narrowing rounds to nearest even)
- *   partition_size  0: the library chooses; otherwise the number of tokens
- *                of one sequence partition (a multiple of 16 and of
- *                block_size, at most 16384 tokens when it does not split the
- *                longest sequence). Sequences longer than one partition are
- *                split; each partition's (max, sum, weighted V) is written to
- *                the workspace and a second kernel merges them.
+ *   partition_size  tokens of one sequence partition, a multiple of 16 and
+ *                of block_size; 0 lets the library choose (see
+ *                paged_attn_partition_tokens). A sequence longer than one
+ *                partition is split; each partition's (max, sum, weighted V)
+ *                is written to the workspace and a second kernel merges them.
+ *                When one partition covers max_seq_len it may hold at most
+ *                16384 tokens; a splitting partition likewise.
  *   workspace    device scratch of at least paged_attn_workspace_size(...)
  *                bytes for the same arguments (may be NULL when that is 0);
  *                its contents need no initialisation and are garbage after.
- * Supported: head_dim 64 or 128; block_size 8, 16 or 32; 1 <= G <= 16.
+ * Supported: head_dim 64 or 128; block_size 8, 16 or 32; 1 <= G <= 16;
+ * num_blocks * block_size < 2^31.
  */
 int paged_attn_decode(void* out, const void* query, const void* key_cache,
                       const void* value_cache, const int32_t* block_table,
@@ -109,6 +111,9 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache,
  * paged_attn_partition_tokens - the partition length paged_attn_decode uses
  * for these arguments (resolving partition_size = 0), or a negative
  * pkv_status for invalid arguments. A value >= max_seq_len means no split.
+ * The choice for 0: no split when there are at least 2048 (sequence, KV
+ * head) pairs and max_seq_len <= 4096; else 512 while that makes at most
+ * 8192 (sequence, KV head, partition) units; else 1024.
  */
 int paged_attn_partition_tokens(int num_seqs, int num_kv_heads, int block_size,
                                 int max_seq_len, int partition_size);

@@ -10,8 +10,6 @@
 
 namespace {
 
-constexpr int kDefaultPartition = 512;
-
 int elem_bytes(int dtype) {
   switch (dtype) {
     case PKV_F32: return 4;
@@ -24,14 +22,30 @@ int elem_bytes(int dtype) {
 bool supported_block_size(int bs) { return bs == 8 || bs == 16 || bs == 32; }
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 
-// Partition length for these arguments, or a negative status.
+// Partition length chosen when partition_size is 0. A workgroup handles one
+// (sequence, KV head, partition); about 1024 fit on the GPU at once (256 CUs,
+// 4 each). Measured on MI355X: when there are already >= 2048 (sequence, KV
+// head) pairs and sequences are at most 4096 tokens, not splitting is best;
+// otherwise 512-token partitions while that gives at most ~8 full rounds of
+// workgroups, then 1024 (fewer partials to write and merge).
+int auto_partition(int num_seqs, int num_kv_heads, int block_size, int max_seq_len) {
+  const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+  const int unit = block_size > pkv::kTile ? block_size : pkv::kTile;
+  if (pairs >= 2048 && max_seq_len <= 4096) {
+    const int P = (max_seq_len + unit - 1) / unit * unit;
+    return P > 0 ? P : unit;
+  }
+  if (pairs * ((max_seq_len + 511) / 512) <= 8192) return 512;
+  return 1024;
+}
+
+// Partition length for these arguments (> 0), or a negative status.
 int resolve_partition(int num_seqs, int num_kv_heads, int block_size, int max_seq_len,
                       int partition_size) {
-  (void)num_seqs;
-  (void)num_kv_heads;
   if (partition_size < 0) return PKV_ERR_SHAPE;
   if (!supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
-  int P = partition_size == 0 ? kDefaultPartition : partition_size;
+  const int P = partition_size == 0 ? auto_partition(num_seqs, num_kv_heads, block_size, max_seq_len)
+                                    : partition_size;
   if (P % pkv::kTile != 0 || P % block_size != 0) return PKV_ERR_SHAPE;
   if (P >= max_seq_len) {
     // one partition per sequence: its block-table slice must fit in LDS
@@ -65,9 +79,10 @@ int paged_attn_partition_tokens(int num_seqs, int num_kv_heads, int block_size, 
 size_t paged_attn_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                                  int block_size, int max_seq_len, int partition_size) {
   if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return 0;
+  if (num_heads % num_kv_heads != 0 || num_heads / num_kv_heads > 16) return 0;
   if (!supported_head_dim(head_dim)) return 0;
   const int P = resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
-  if (P <= 0) return 0;
+  if (P < 0) return 0;
   return split_workspace_bytes(num_seqs, num_heads, head_dim, num_partitions(max_seq_len, P));
 }
 
@@ -89,6 +104,7 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
   if (out_dtype != kv_dtype && out_dtype != PKV_F32) return PKV_ERR_UNSUPPORTED;
   if (num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0) return PKV_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size < max_seq_len) return PKV_ERR_SHAPE;
+  if ((int64_t)num_blocks * block_size > (int64_t)INT32_MAX) return PKV_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return PKV_ERR_SHAPE;
   const int P = resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
   if (P < 0) return P;
@@ -104,9 +120,10 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
   p.v = value_cache;
   p.block_table = block_table;
   p.seq_lens = seq_lens;
-  p.ws_o = need ? static_cast<float*>(workspace) : nullptr;
-  p.ws_ml = need ? static_cast<float*>(workspace) + (size_t)num_seqs * num_heads * np * head_dim
-                 : nullptr;
+  if (need > 0) {
+    p.ws_o = static_cast<float*>(workspace);
+    p.ws_ml = static_cast<float*>(workspace) + (size_t)num_seqs * num_heads * np * head_dim;
+  }
   p.num_seqs = num_seqs;
   p.num_heads = num_heads;
   p.num_kv_heads = num_kv_heads;

@@ -7,29 +7,34 @@
 //   out[s,h] = sum_t softmax_t(scale * q[s,h] . K[t, h/G]) * V[t, h/G].
 //
 // How (an MI355X design, not the pages' kernel):
-//  * One workgroup of 4 waves per (sequence, KV head, partition of the
-//    sequence). The partition's slice of the block-table row is staged in LDS
-//    once ("the block table of a sequence can be loaded into shared memory at
-//    once", PagedAttention principle section 2.2).
-//  * Waves take 16-token key tiles round-robin. Q.K^T of a tile is one MFMA
-//    chain v_mfma_f32_16x16x32_{f16,bf16} per 64 bytes of head_dim (fp32
-//    pools: v_mfma_f32_16x16x4_f32): the A operand is the key tile, 16 tokens
-//    x 32 head-dim elements, loaded straight from the pool as 16-byte chunks;
-//    the B operand is the G query heads of this KV head (columns >= G are
-//    zero). The result tile S[token][head] leaves each lane one head's scores
-//    for 4 tokens, so a head's softmax state (running max, sum) lives in one
-//    lane column and reductions are two cross-lane exchanges.
-//  * P.V runs on v_mfma_f32_16x16x4_f32 with A = V^T (each lane holds
-//    head_dim/16 contiguous elements of one token's V row, widened to fp32)
-//    and B = P^T in fp32: the probabilities never drop below fp32, and the
-//    output tile O^T[d][head] keeps a head in the same lane column as its
-//    softmax state, so the online rescale is lane-local.
+//  * The unit of work is a 16-token key tile of one (sequence, KV head). A
+//    wave processes tiles one at a time: it issues all of the tile's K and V
+//    loads (16-byte chunks) before computing, then
+//      - Q.K^T on v_mfma_f32_16x16x32_{f16,bf16} (fp32 pools:
+//        v_mfma_f32_16x16x4_f32) with the key tile as the A operand (16
+//        tokens x 32 head-dim elements, straight from the pool) and the G
+//        query heads of the KV head as the B operand (columns >= G are 0).
+//        The result S[token][head] leaves each lane one head's scores for 4
+//        tokens, so a head's softmax state lives in one lane column;
+//      - P.V on v_mfma_f32_16x16x4_f32 with A = V^T (each lane holds head_dim
+//        / 16 contiguous elements of one token's V row, widened to fp32) and
+//        B = P^T in fp32: probabilities never drop below fp32, and the output
+//        tile O^T[d][head] keeps a head in the same lane column as its
+//        softmax state, so the online rescale is lane-local.
 //  * Tokens past seq_len in the last tile are never read: their address is
 //    clamped to the last valid token (finite data) and their score is set to
 //    -inf before the exponent, so their weight is exactly 0.
-//  * The 4 waves merge their (max, sum, O) through LDS. A sequence that fits
-//    in one partition is written directly; otherwise each partition writes
-//    (max, sum, O) to the workspace and decode_reduce_kernel merges them.
+//  * One workgroup of 4 waves per (sequence, KV head, partition of the
+//    sequence). The partition's slice of the block table is staged in LDS
+//    ("the block table of a sequence can be loaded into shared memory at
+//    once", PagedAttention principle section 2.2); the 4 waves take the
+//    partition's tiles round-robin and merge their (max, sum, O) through LDS.
+//    A sequence that fits in one partition is written directly; otherwise
+//    each partition writes (max, sum, O) to the workspace and
+//    decode_reduce_kernel merges them.
+//  * Workgroup i runs on XCD i mod 8. Workgroups are numbered partition-major
+//    and KV-head-minor, so the 8 XCDs share every partition index evenly
+//    (short sequences have only the low partition indices).
 
 #include "pagedkv_internal.h"
 
@@ -42,9 +47,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-struct F32Tag {};
-struct F16Tag {};
-struct BF16Tag {};
+struct F32Tag { static constexpr int kBytes = 4; };
+struct F16Tag { static constexpr int kBytes = 2; };
+struct BF16Tag { static constexpr int kBytes = 2; };
 
 template <class Tag>
 struct KV;
@@ -124,36 +129,162 @@ __device__ inline void store_out(const DecodeParams& p, size_t i, float x) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// LDS layout of the partition kernel (bytes): the block-table slice, later
-// reused for the per-wave O tiles, then per-wave (max, sum).
+__device__ inline int clamp_len(int L, int max_len) {
+  return L < 0 ? 0 : (L > max_len ? max_len : L);
+}
+
+// A value known to be equal in every lane of the wave, moved to a scalar
+// register so that the bookkeeping derived from it stays scalar.
+__device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Waves per SIMD the decode kernels are compiled for: 4 (<= 128 VGPRs) for
+// every case except fp32 rows of 128 elements, whose tile buffers need 2.
+template <class Tag, int D>
+struct WavesPerEU {
+  static constexpr int value = (Tag::kBytes == 4 && D == 128) ? 2 : 4;
+};
+// log2 of the largest weight allowed before the running max is moved.
+constexpr float kRescaleSlack = 8.0f;
+
+// Per-lane state of one wave working through the tiles of one (sequence, KV
+// head): the query operand, the softmax state of head `col` and its O^T
+// accumulators.
+template <class Tag, int D, int BS>
+struct TileEngine {
+  using Tr = KV<Tag>;
+  static constexpr int E = Tr::kBytes;
+  static constexpr int RB = D * E;        // bytes of one token row of one KV head
+  static constexpr int NKL = RB / 64;     // 16-byte key chunks per lane per tile
+  static constexpr int VPL = D / 16;      // V elements per lane per token
+  static constexpr int VW = VPL * E / 4;  // 32-bit words per lane per token of V
+  static_assert(RB % 64 == 0, "row must split into 4 lane groups of 16-byte chunks");
+
+  int col;  // MFMA column: head within the group
+  int grp;  // lane group 0..3
+  uint4 qv[NKL];
+  float m;     // running max of head `col` (log2 units)
+  float lsum;  // this lane's share of the running sum of weights
+  f32x4 acc[VPL];  // acc[j][i] = O[head col][VPL * (4 * grp + i) + j]
+
+  __device__ void init(int lane) {
+    col = lane & 15;
+    grp = lane >> 4;
+  }
+
+  // q_group: the row of the first query head of this KV head's group.
+  __device__ void load_q(const unsigned char* q_group, int G) {
+    const unsigned char* qrow = q_group + (size_t)(col < G ? col : 0) * RB;
+#pragma unroll
+    for (int i = 0; i < NKL; ++i) {
+      qv[i] = col < G ? *reinterpret_cast<const uint4*>(qrow + 16 * (4 * i + grp))
+                      : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  __device__ void reset() {
+    m = -INFINITY;
+    lsum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // One tile of tokens cs .. cs+15 (cs a multiple of 16, cs <= t_last).
+  // row_off(t) is the byte offset of token t's row for this KV head (t <= t_last).
+  template <class RowOff>
+  __device__ void step(const unsigned char* kbase, const unsigned char* vbase, int cs, int t_last,
+                       uint32_t slot_bytes, float scale_log2, RowOff row_off) {
+    uint4 kr[NKL];
+    uint32_t vr[4][VW];
+    const unsigned char* kp = kbase + row_off(min(cs + col, t_last)) + 16 * grp;
+#pragma unroll
+    for (int i = 0; i < NKL; ++i) kr[i] = *reinterpret_cast<const uint4*>(kp + 64 * i);
+    // V rows of tokens t4 .. t4+3: a 4-aligned group never crosses a block
+    const int t4 = min(cs + 4 * grp, t_last);
+    const unsigned char* vp = vbase + row_off(t4) + col * (VPL * E);
+    const uint32_t room = (uint32_t)(t_last - t4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      load_words<VW>(vr[r], vp + (uint32_t)((uint32_t)r < room ? r : room) * slot_bytes);
+    __builtin_amdgcn_sched_barrier(0);  // every load of the tile in flight first
+
+    // scores S[token][head]: lane holds tokens cs + 4*grp + r of head col
+    f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NKL; ++i) a = Tr::qk(kr[i], qv[i], a);
+    float s[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = (cs + 4 * grp + r) <= t_last ? a[r] * scale_log2 : -INFINITY;
+
+    // Online softmax with a lazy running max: the max (and the rescale of
+    // lsum and O) moves only when some lane's tile max exceeds it by more than
+    // 2^kRescaleSlack, so weights stay <= 2^kRescaleSlack and the rescale of
+    // the accumulators is rare. Same algebra: every weight and the sum share
+    // the reference m.
+    float cmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    if (__any(cmax > m + kRescaleSlack)) {
+      const float m_new = fmaxf(m, cmax);
+      const float alpha = fast_exp2(m - m_new);
+      lsum *= alpha;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) acc[j] *= alpha;
+      m = m_new;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      s[r] = fast_exp2(s[r] - m);
+      lsum += s[r];
+    }
+
+    // O^T += V^T P^T, 4 tokens per MFMA
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < VPL; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(Tr::elem(vr[r], j), s[r], acc[j], 0, 0, 0);
+  }
+
+  // Sum of weights of head col over all tokens seen (all 4 lane groups).
+  __device__ float total_sum() const {
+    float l = lsum;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    return l;
+  }
+
+  __device__ int d_of(int i, int j) const { return VPL * (4 * grp + i) + j; }
+};
+
+// ============================================================================
+// fixed partitions
+// ============================================================================
+
 __host__ __device__ inline int o_stride(int D) { return D + 4; }
 
-template <class Tag, int D, int BS, int U>
-__global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams p) {
-  using Tr = KV<Tag>;
-  constexpr int E = Tr::kBytes;
-  constexpr int RB = D * E;        // bytes of one token row of one KV head
-  constexpr int NKL = RB / 64;     // 16-byte key chunks per lane per tile
-  constexpr int VPL = D / 16;      // V elements per lane per token
-  constexpr int VW = VPL * E / 4;  // 32-bit words per lane per token of V
-  static_assert(RB % 64 == 0, "row must split into 4 lane groups of 16-byte chunks");
+template <class Tag, int D, int BS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WavesPerEU<Tag, D>::value)))
+void decode_partition_kernel(DecodeParams p) {
+  using Eng = TileEngine<Tag, D, BS>;
+  constexpr int RB = Eng::RB;
+  constexpr int VPL = Eng::VPL;
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int col = lane & 15;  // MFMA column: head within the group
-  const int grp = lane >> 4;  // lane group 0..3
+  const int wave = uniform(threadIdx.x >> 6);
 
+  // Workgroup i runs on XCD i mod 8. The KV head varies fastest and the
+  // partition slowest, so each XCD gets an even share of every partition
+  // index (only low partition indices exist for short sequences).
   int wg = blockIdx.x;
-  const int part = wg % p.num_partitions;
-  wg /= p.num_partitions;
   const int kvh = wg % p.num_kv_heads;
-  const int seq = wg / p.num_kv_heads;
+  wg /= p.num_kv_heads;
+  const int seq = wg % p.num_seqs;
+  const int part = wg / p.num_seqs;
   const int G = p.group;
   const int head0 = kvh * G;
 
-  int L = p.seq_lens[seq];
-  L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+  const int L = clamp_len(p.seq_lens[seq], p.max_seq_len);
   const int t_begin = part * p.partition;
 
   if (L == 0) {  // nothing to attend to: a zero row
@@ -179,100 +310,27 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams p) {
     }
   }
 
-  // ---- query operand: head (head0 + col), 16-byte chunks 4*i + grp -------
-  uint4 qv[NKL];
-  {
-    const unsigned char* qrow = static_cast<const unsigned char*>(p.q) +
-                                ((size_t)seq * p.num_heads + head0 + (col < G ? col : 0)) * RB;
-#pragma unroll
-    for (int i = 0; i < NKL; ++i) {
-      qv[i] = col < G ? *reinterpret_cast<const uint4*>(qrow + 16 * (4 * i + grp))
-                      : make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
+  TileEngine<Tag, D, BS> eng;
+  eng.init(lane);
+  eng.load_q(static_cast<const unsigned char*>(p.q) + ((size_t)seq * p.num_heads + head0) * RB, G);
+  eng.reset();
   __syncthreads();
 
-  const size_t slot_bytes = (size_t)p.num_kv_heads * RB;  // bytes between slots
+  const uint32_t slot_bytes = (uint32_t)p.num_kv_heads * RB;  // bytes between slots
   const unsigned char* kbase = static_cast<const unsigned char*>(p.k) + (size_t)kvh * RB;
   const unsigned char* vbase = static_cast<const unsigned char*>(p.v) + (size_t)kvh * RB;
-
-  // byte offset of token t's row (this KV head), clamped to the last valid token
-  auto row_offset = [&](int t) -> size_t {
-    const int tt = t < t_end ? t : t_end - 1;
-    const int phys = s_bt[tt / BS - lb0];
-    return ((size_t)phys * BS + (tt % BS)) * slot_bytes;
+  // The slot index phys * BS + offset fits in 32 bits (checked on the host),
+  // so the byte offset is a single 32x32->64 multiply.
+  auto row_off = [&](int tt) -> uint64_t {
+    const uint32_t u = (uint32_t)tt;
+    const uint32_t phys = (uint32_t)s_bt[u / BS - (uint32_t)lb0];
+    return (uint64_t)(phys * BS + (u % BS)) * slot_bytes;
   };
-
-  float m = -INFINITY;  // running max of this lane's head (log2 units)
-  float lsum = 0.0f;    // this lane's share of the running sum of weights
-  f32x4 acc[VPL];       // O^T tiles: acc[j][i] = O[head col][VPL*(4*grp+i)+j]
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int c0 = t_begin + wave * (kTile * U); c0 < t_end; c0 += kWaves * kTile * U) {
-    uint4 kr[U][NKL];
-    uint32_t vr[U][4][VW];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int cs = c0 + u * kTile;
-      const unsigned char* kp = kbase + row_offset(cs + col);
-#pragma unroll
-      for (int i = 0; i < NKL; ++i) kr[u][i] = *reinterpret_cast<const uint4*>(kp + 16 * (4 * i + grp));
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        load_words<VW>(vr[u][r], vbase + row_offset(cs + 4 * grp + r) + col * (VPL * E));
-    }
-
-    // scores S[token][head]: lane holds tokens cs + 4*grp + r of head col
-    float s[U][4];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < NKL; ++i) a = Tr::qk(kr[u][i], qv[i], a);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = c0 + u * kTile + 4 * grp + r;
-        s[u][r] = t < t_end ? a[r] * p.scale_log2 : -INFINITY;
-      }
-    }
-
-    // online softmax over this step's tokens
-    float cmax = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) cmax = fmaxf(cmax, s[u][r]);
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m, cmax);
-    const float alpha = fast_exp2(m - m_new);
-    float ps = 0.0f;
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s[u][r] = fast_exp2(s[u][r] - m_new);
-        ps += s[u][r];
-      }
-    lsum = lsum * alpha + ps;
-    m = m_new;
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) acc[j] *= alpha;
-
-    // O^T += V^T P^T, 4 tokens per MFMA
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int j = 0; j < VPL; ++j)
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(Tr::elem(vr[u][r], j), s[u][r], acc[j], 0, 0, 0);
-  }
+  for (int cs = t_begin + wave * kTile; cs < t_end; cs += kWaves * kTile)
+    eng.step(kbase, vbase, cs, t_end - 1, slot_bytes, p.scale_log2, row_off);
 
   // ---- merge the 4 waves -------------------------------------------------
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  const float lsum = eng.total_sum();
   __syncthreads();  // block-table slice no longer needed: reuse its LDS
   const int OST = o_stride(D);
   float* s_o = reinterpret_cast<float*>(smem);
@@ -281,16 +339,16 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams p) {
   const int base = ((o_bytes_all > bt_bytes ? o_bytes_all : bt_bytes) + 15) & ~15;
   float* s_m = reinterpret_cast<float*>(smem + base);
   float* s_l = s_m + kWaves * 16;
-  if (col < G) {
-    if (grp == 0) {
-      s_m[wave * 16 + col] = m;
-      s_l[wave * 16 + col] = lsum;
+  if (eng.col < G) {
+    if (eng.grp == 0) {
+      s_m[wave * 16 + eng.col] = eng.m;
+      s_l[wave * 16 + eng.col] = lsum;
     }
-    float* orow = s_o + (size_t)(wave * G + col) * OST;
+    float* orow = s_o + (size_t)(wave * G + eng.col) * OST;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < VPL; ++j) orow[VPL * (4 * grp + i) + j] = acc[j][i];
+      for (int j = 0; j < VPL; ++j) orow[eng.d_of(i, j)] = eng.acc[j][i];
   }
   __syncthreads();
 
@@ -321,49 +379,119 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeParams p) {
   }
 }
 
-// Merge the partitions of each split sequence:
-//   M = max_p m_p,  out = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p.
-template <class Tag, int D>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams p) {
-  const int kvh = blockIdx.x % p.num_kv_heads;
-  const int seq = blockIdx.x / p.num_kv_heads;
-  int L = p.seq_lens[seq];
-  L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
-  const int nparts = (L + p.partition - 1) / p.partition;
-  if (nparts <= 1) return;  // written by the partition kernel
-  const int G = p.group;
+// Merge the pieces of a split sequence:
+//   M = max_q m_q,  out = sum_q 2^(m_q - M) O_q / sum_q 2^(m_q - M) l_q.
+// ml_of(h, q) gives the (m, l) pair and o_of(h, q) the O row of piece q of
+// head h. The (m, l) pairs of the G heads are staged in LDS, each head's
+// weights and denominator are formed once, then every output element sums
+// its pieces' O with independent loads.
+constexpr int kReduceLdsBytes = 32768;
+
+__host__ __device__ inline size_t merge_lds_bytes(int G, int npieces) {
+  return (size_t)G * npieces * 2 * sizeof(float) + G * sizeof(float);
+}
+
+// LDS given to a merge workgroup: enough to stage up to max_pieces pieces,
+// capped; a workgroup with more pieces than fit merges without staging.
+inline size_t reduce_lds_bytes(int G, int max_pieces) {
+  const size_t need = merge_lds_bytes(G, max_pieces);
+  return need < (size_t)kReduceLdsBytes ? need : (size_t)kReduceLdsBytes;
+}
+
+template <class Tag, int D, class PieceML, class PieceO>
+__device__ void merge_pieces(const DecodeParams& p, float* s_red, size_t out_row0, int G,
+                             int npieces, PieceML ml_of, PieceO o_of) {
+  if (merge_lds_bytes(G, npieces) <= (size_t)p.red_lds_bytes) {
+    float* s_w = s_red;                // [G][npieces]: m, then the weight 2^(m - M)
+    float* s_l = s_red + G * npieces;  // [G][npieces]: l
+    float* s_den = s_l + G * npieces;  // [G]
+    for (int idx = threadIdx.x; idx < G * npieces; idx += 256) {
+      const int h = idx / npieces;
+      const int q = idx - h * npieces;
+      const float2 ml = ml_of(h, q);
+      s_w[idx] = ml.x;
+      s_l[idx] = ml.y;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < G) {
+      const int h = threadIdx.x;
+      float M = -INFINITY;
+      for (int q = 0; q < npieces; ++q) M = fmaxf(M, s_w[h * npieces + q]);
+      float den = 0.0f;
+      for (int q = 0; q < npieces; ++q) {
+        const float w = fast_exp2(s_w[h * npieces + q] - M);
+        s_w[h * npieces + q] = w;
+        den += w * s_l[h * npieces + q];
+      }
+      s_den[h] = den;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+      const int h = idx / D;
+      const int d = idx - h * D;
+      const float* w = s_w + h * npieces;
+      float num = 0.0f;
+#pragma unroll 4
+      for (int q = 0; q < npieces; ++q) num += w[q] * o_of(h, q)[d];
+      store_out<Tag>(p, (out_row0 + h) * D + d, num / s_den[h]);
+    }
+    return;
+  }
+  // many pieces: no staging
   for (int idx = threadIdx.x; idx < G * D; idx += 256) {
     const int h = idx / D;
     const int d = idx - h * D;
-    const size_t row = (size_t)seq * p.num_heads + kvh * G + h;
-    const float* ml = p.ws_ml + row * p.num_partitions * 2;
-    const float* o = p.ws_o + row * p.num_partitions * D + d;
     float M = -INFINITY;
-    for (int q = 0; q < nparts; ++q) M = fmaxf(M, ml[2 * q]);
+    for (int q = 0; q < npieces; ++q) M = fmaxf(M, ml_of(h, q).x);
     float den = 0.0f, num = 0.0f;
-    for (int q = 0; q < nparts; ++q) {
-      const float sc = fast_exp2(ml[2 * q] - M);
-      den += sc * ml[2 * q + 1];
-      num += sc * o[(size_t)q * D];
+    for (int q = 0; q < npieces; ++q) {
+      const float2 ml = ml_of(h, q);
+      const float sc = fast_exp2(ml.x - M);
+      den += sc * ml.y;
+      num += sc * o_of(h, q)[d];
     }
-    store_out<Tag>(p, row * D + d, num / den);
+    store_out<Tag>(p, (out_row0 + h) * D + d, num / den);
   }
 }
 
+// One workgroup per (sequence, KV head) of the fixed-partition path.
+template <class Tag, int D>
+__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams p) {
+  extern __shared__ __align__(16) float s_red[];
+  const int kvh = blockIdx.x % p.num_kv_heads;
+  const int seq = blockIdx.x / p.num_kv_heads;
+  const int L = clamp_len(p.seq_lens[seq], p.max_seq_len);
+  const int nparts = (L + p.partition - 1) / p.partition;
+  if (nparts <= 1) return;  // written by the partition kernel
+  const int G = p.group;
+  const size_t row0 = (size_t)seq * p.num_heads + (size_t)kvh * G;
+  const int NP = p.num_partitions;
+  merge_pieces<Tag, D>(
+      p, s_red, row0, G, nparts,
+      [&](int h, int q) { return reinterpret_cast<const float2*>(p.ws_ml)[(row0 + h) * NP + q]; },
+      [&](int h, int q) { return p.ws_o + ((row0 + h) * NP + q) * D; });
+}
+
+// ============================================================================
+// launchers
+// ============================================================================
+
 template <class Tag, int D, int BS>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
-  constexpr int U = 2;
   const int span = p.partition < p.max_seq_len ? p.partition : p.max_seq_len;
   const int bt_bytes = (span / BS + 1) * 4;
   const int o_bytes = kWaves * p.group * o_stride(D) * 4;
   const int base = ((o_bytes > bt_bytes ? o_bytes : bt_bytes) + 15) & ~15;
   const size_t lds = (size_t)base + 2 * kWaves * 16 * 4;
   const unsigned grid = (unsigned)((size_t)p.num_seqs * p.num_kv_heads * p.num_partitions);
-  decode_partition_kernel<Tag, D, BS, U><<<dim3(grid), dim3(256), lds, stream>>>(p);
+  decode_partition_kernel<Tag, D, BS><<<dim3(grid), dim3(256), lds, stream>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.num_partitions > 1) {
-    decode_reduce_kernel<Tag, D><<<dim3((unsigned)(p.num_seqs * p.num_kv_heads)), dim3(256), 0, stream>>>(p);
+    DecodeParams rp = p;
+    rp.red_lds_bytes = (int)reduce_lds_bytes(p.group, p.num_partitions);
+    decode_reduce_kernel<Tag, D>
+        <<<dim3((unsigned)(p.num_seqs * p.num_kv_heads)), dim3(256), rp.red_lds_bytes, stream>>>(rp);
     e = hipGetLastError();
   }
   return e;

@@ -28,6 +28,7 @@ struct DecodeParams {
   int num_partitions;  // ceil(max_seq_len / partition), >= 1
   float scale_log2;    // scale * log2(e)
   int out_f32;         // 1: out is fp32; 0: out has the KV dtype
+  int red_lds_bytes;  // LDS of a merge workgroup (set by the launcher)
 };
 
 // Tokens a wave handles per step (one MFMA tile of keys).

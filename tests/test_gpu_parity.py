@@ -148,7 +148,8 @@ def test_zero_length_sequences_give_zero_rows():
         assert max_err(out, ref) <= TOL[torch.bfloat16]
 
 
-def test_max_seq_len_above_actual_lengths():
+@pytest.mark.parametrize("P", [64, 0])
+def test_max_seq_len_above_actual_lengths(P):
     """The launch is sized from the host bound; partitions past a sequence's
     end exit early."""
     wl = W.custom(9, seq_lens=[10, 300, 47], num_heads=16, num_kv_heads=4, head_dim=128,
@@ -156,10 +157,22 @@ def test_max_seq_len_above_actual_lengths():
     d = to_dev(wl)
     ref, _, _ = oracle_step(wl)
     out = torch.empty(wl.query.shape, dtype=torch.float32, device=DEV)
-    say("max_seq_len 2048 over lengths <= 300")
-    pkv.paged_attn_decode(out, d["q"], d["kc"], d["vc"], d["bt"], d["sl"], wl.scale, 2048, 64)
+    say(f"max_seq_len 2048 over lengths <= 300, P={P}")
+    pkv.paged_attn_decode(out, d["q"], d["kc"], d["vc"], d["bt"], d["sl"], wl.scale, 2048, P)
     torch.cuda.synchronize()
     assert max_err(out, ref) <= TOL[torch.float16]
+
+
+@pytest.mark.parametrize("L,G,P", [(65536, 16, 64), (65536, 4, 64), (8192, 4, 16)])
+def test_many_partitions_of_one_long_sequence(L, G, P):
+    """One sequence split into hundreds or thousands of partitions (more
+    (max, sum) pairs than the merge kernel stages in LDS for L=65536)."""
+    wl = W.custom(16, seq_lens=[L], num_heads=G, num_kv_heads=1, head_dim=64,
+                  block_size=16, dtype=torch.bfloat16)
+    ref, _, _ = oracle_step(wl)
+    say(f"one sequence of {L} tokens, G={G}, P={P}")
+    out = gpu_step(wl, to_dev(wl), out_dtype=torch.float32, partition_size=P)
+    assert max_err(out, ref) <= TOL[torch.bfloat16]
 
 
 # ----------------------------------------------------------------------------
@@ -300,16 +313,35 @@ def _sample(wl, n=48):
     return sorted(pick)
 
 
-@pytest.mark.parametrize("config", [1, 2, 3, 4, 5])
-def test_config_parity(config):
-    wl = W.make(config)
+_WORKLOADS = {}
+
+
+def _workload(config):
+    """Each full-size workload is generated once per test session."""
+    if config not in _WORKLOADS:
+        _WORKLOADS.clear()
+        _WORKLOADS[config] = W.make(config)
+    return _WORKLOADS[config]
+
+
+# (config, partition_size): None is the workload's own launch (the library's
+# choice, or 512-token partitions for the mixed batch); the other entry splits
+# the same inputs differently.
+CONFIG_RUNS = [(1, None), (1, 16), (2, None), (2, 1024), (3, None), (3, 512),
+               (4, None), (4, 512), (5, None), (5, 0)]
+
+
+@pytest.mark.parametrize("config,part", CONFIG_RUNS, ids=[f"cfg{c}-P{p}" for c, p in CONFIG_RUNS])
+def test_config_parity(config, part):
+    wl = _workload(config)
+    P = wl.partition_size if part is None else part
     say(f"config {config} {wl.name}: S={wl.num_seqs} tokens={wl.num_tokens} "
-        f"max_len={wl.max_seq_len} P={wl.partition_size}")
+        f"max_len={wl.max_seq_len} P={P}")
     seqs = None if wl.num_seqs <= 8 else _sample(wl)
     ref, ek, ev = oracle_step(wl, seqs=seqs)
     for out_dt in (torch.float32, wl.dtype):
         d = to_dev(wl)
-        out = gpu_step(wl, d, out_dtype=out_dt)
+        out = gpu_step(wl, d, out_dtype=out_dt, partition_size=P)
         if out_dt == torch.float32:
             # bit-exact cache ops over the whole pool
             assert torch.equal(bits(d["kc"].cpu()), bits(ek))
