@@ -112,8 +112,8 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache,
  * for these arguments (resolving partition_size = 0), or a negative
  * pkv_status for invalid arguments. A value >= max_seq_len means no split.
  * The choice for 0: no split when there are at least 2048 (sequence, KV
- * head) pairs and max_seq_len <= 4096; else 512 while that makes at most
- * 8192 (sequence, KV head, partition) units; else 1024.
+ * head) pairs and max_seq_len <= 4096; else 1024 while that makes at most
+ * 4096 (sequence, KV head, partition) units; else 2048.
  */
 int paged_attn_partition_tokens(int num_seqs, int num_kv_heads, int block_size,
                                 int max_seq_len, int partition_size);

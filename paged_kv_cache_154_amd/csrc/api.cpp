@@ -22,12 +22,12 @@ int elem_bytes(int dtype) {
 bool supported_block_size(int bs) { return bs == 8 || bs == 16 || bs == 32; }
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 
-// Partition length chosen when partition_size is 0. A workgroup handles one
-// (sequence, KV head, partition); about 1024 fit on the GPU at once (256 CUs,
-// 4 each). Measured on MI355X: when there are already >= 2048 (sequence, KV
-// head) pairs and sequences are at most 4096 tokens, not splitting is best;
-// otherwise 512-token partitions while that gives at most ~8 full rounds of
-// workgroups, then 1024 (fewer partials to write and merge).
+// Partition length chosen when partition_size is 0. A workgroup (8 waves)
+// handles one (sequence, KV head, partition); 512 fit on the GPU at once (256
+// CUs, 2 each). Measured on MI355X: with >= 2048 (sequence, KV head) pairs and
+// sequences of at most 4096 tokens, not splitting is best; otherwise 1024-token
+// partitions while that gives at most 4096 (sequence, KV head, partition)
+// units, else 2048 (fewer partials to write and merge).
 int auto_partition(int num_seqs, int num_kv_heads, int block_size, int max_seq_len) {
   const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
   const int unit = block_size > pkv::kTile ? block_size : pkv::kTile;
@@ -35,8 +35,8 @@ int auto_partition(int num_seqs, int num_kv_heads, int block_size, int max_seq_l
     const int P = (max_seq_len + unit - 1) / unit * unit;
     return P > 0 ? P : unit;
   }
-  if (pairs * ((max_seq_len + 511) / 512) <= 8192) return 512;
-  return 1024;
+  if (pairs * ((max_seq_len + 1023) / 1024) <= 4096) return 1024;
+  return 2048;
 }
 
 // Partition length for these arguments (> 0), or a negative status.

@@ -143,6 +143,9 @@ template <class Tag, int D>
 struct WavesPerEU {
   static constexpr int value = (Tag::kBytes == 4 && D == 128) ? 2 : 4;
 };
+#ifndef PKV_LPT_ORDER
+#define PKV_LPT_ORDER 1
+#endif
 // log2 of the largest weight allowed before the running max is moved.
 constexpr float kRescaleSlack = 8.0f;
 
@@ -263,7 +266,7 @@ struct TileEngine {
 __host__ __device__ inline int o_stride(int D) { return D + 4; }
 
 template <class Tag, int D, int BS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WavesPerEU<Tag, D>::value)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEU<Tag, D>::value)))
 void decode_partition_kernel(DecodeParams p) {
   using Eng = TileEngine<Tag, D, BS>;
   constexpr int RB = Eng::RB;
@@ -280,23 +283,35 @@ void decode_partition_kernel(DecodeParams p) {
   const int kvh = wg % p.num_kv_heads;
   wg /= p.num_kv_heads;
   const int seq = wg % p.num_seqs;
+#if PKV_LPT_ORDER
+  const int part = p.num_partitions - 1 - wg / p.num_seqs;
+#else
   const int part = wg / p.num_seqs;
+#endif
   const int G = p.group;
   const int head0 = kvh * G;
 
   const int L = clamp_len(p.seq_lens[seq], p.max_seq_len);
-  const int t_begin = part * p.partition;
-
   if (L == 0) {  // nothing to attend to: a zero row
     if (part == 0) {
-      for (int idx = threadIdx.x; idx < G * D; idx += 256)
+      for (int idx = threadIdx.x; idx < G * D; idx += kThreads)
         store_out<Tag>(p, ((size_t)seq * p.num_heads + head0) * D + idx, 0.0f);
     }
     return;
   }
-  if (t_begin >= L) return;
-  const int t_end = min(L, t_begin + p.partition);
   const int nparts = (L + p.partition - 1) / p.partition;
+  if (part >= nparts) return;
+#if PKV_LPT_ORDER
+  // Partition 0 is the short one: [0, first) with first in (0, P], a multiple
+  // of 16; partitions 1.. are full. Workgroups run from the highest partition
+  // index down, so the long partitions start first and the short ones last.
+  const int first = (L + kTile - 1) / kTile * kTile - (nparts - 1) * p.partition;
+  const int t_begin = part == 0 ? 0 : first + (part - 1) * p.partition;
+  const int t_end = min(L, part == 0 ? first : t_begin + p.partition);
+#else
+  const int t_begin = part * p.partition;
+  const int t_end = min(L, t_begin + p.partition);
+#endif
 
   // ---- stage this partition's slice of the block-table row --------------
   int* s_bt = reinterpret_cast<int*>(smem);
@@ -304,7 +319,7 @@ void decode_partition_kernel(DecodeParams p) {
   const int nlb = (t_end + BS - 1) / BS - lb0;
   {
     const int32_t* row = p.block_table + (size_t)seq * p.max_blocks + lb0;
-    for (int i = threadIdx.x; i < nlb; i += 256) {
+    for (int i = threadIdx.x; i < nlb; i += kThreads) {
       const int b = row[i];
       s_bt[i] = ((unsigned)b < (unsigned)p.num_blocks) ? b : 0;  // never leave the pool
     }
@@ -352,7 +367,7 @@ void decode_partition_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int h = idx / D;
     const int d = idx - h * D;
     float M = -INFINITY;
@@ -379,97 +394,57 @@ void decode_partition_kernel(DecodeParams p) {
   }
 }
 
-// Merge the pieces of a split sequence:
-//   M = max_q m_q,  out = sum_q 2^(m_q - M) O_q / sum_q 2^(m_q - M) l_q.
-// ml_of(h, q) gives the (m, l) pair and o_of(h, q) the O row of piece q of
-// head h. The (m, l) pairs of the G heads are staged in LDS, each head's
-// weights and denominator are formed once, then every output element sums
-// its pieces' O with independent loads.
-constexpr int kReduceLdsBytes = 32768;
-
-__host__ __device__ inline size_t merge_lds_bytes(int G, int npieces) {
-  return (size_t)G * npieces * 2 * sizeof(float) + G * sizeof(float);
-}
-
-// LDS given to a merge workgroup: enough to stage up to max_pieces pieces,
-// capped; a workgroup with more pieces than fit merges without staging.
-inline size_t reduce_lds_bytes(int G, int max_pieces) {
-  const size_t need = merge_lds_bytes(G, max_pieces);
-  return need < (size_t)kReduceLdsBytes ? need : (size_t)kReduceLdsBytes;
-}
-
-template <class Tag, int D, class PieceML, class PieceO>
-__device__ void merge_pieces(const DecodeParams& p, float* s_red, size_t out_row0, int G,
-                             int npieces, PieceML ml_of, PieceO o_of) {
-  if (merge_lds_bytes(G, npieces) <= (size_t)p.red_lds_bytes) {
-    float* s_w = s_red;                // [G][npieces]: m, then the weight 2^(m - M)
-    float* s_l = s_red + G * npieces;  // [G][npieces]: l
-    float* s_den = s_l + G * npieces;  // [G]
-    for (int idx = threadIdx.x; idx < G * npieces; idx += 256) {
-      const int h = idx / npieces;
-      const int q = idx - h * npieces;
-      const float2 ml = ml_of(h, q);
-      s_w[idx] = ml.x;
-      s_l[idx] = ml.y;
-    }
-    __syncthreads();
-    if ((int)threadIdx.x < G) {
-      const int h = threadIdx.x;
-      float M = -INFINITY;
-      for (int q = 0; q < npieces; ++q) M = fmaxf(M, s_w[h * npieces + q]);
-      float den = 0.0f;
-      for (int q = 0; q < npieces; ++q) {
-        const float w = fast_exp2(s_w[h * npieces + q] - M);
-        s_w[h * npieces + q] = w;
-        den += w * s_l[h * npieces + q];
-      }
-      s_den[h] = den;
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-      const int h = idx / D;
-      const int d = idx - h * D;
-      const float* w = s_w + h * npieces;
-      float num = 0.0f;
-#pragma unroll 4
-      for (int q = 0; q < npieces; ++q) num += w[q] * o_of(h, q)[d];
-      store_out<Tag>(p, (out_row0 + h) * D + d, num / s_den[h]);
-    }
-    return;
-  }
-  // many pieces: no staging
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int h = idx / D;
-    const int d = idx - h * D;
-    float M = -INFINITY;
-    for (int q = 0; q < npieces; ++q) M = fmaxf(M, ml_of(h, q).x);
-    float den = 0.0f, num = 0.0f;
-    for (int q = 0; q < npieces; ++q) {
-      const float2 ml = ml_of(h, q);
-      const float sc = fast_exp2(ml.x - M);
-      den += sc * ml.y;
-      num += sc * o_of(h, q)[d];
-    }
-    store_out<Tag>(p, (out_row0 + h) * D + d, num / den);
-  }
-}
-
-// One workgroup per (sequence, KV head) of the fixed-partition path.
+// One wave per (sequence, query head) of a split sequence, 4 waves per
+// workgroup. Lane q loads (m_q, l_q) of partition q and the partial O loads
+// do not wait for the weights, so the merge costs about one memory round
+// trip; the weights 2^(m_q - M) are broadcast from their lanes.
 template <class Tag, int D>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams p) {
-  extern __shared__ __align__(16) float s_red[];
-  const int kvh = blockIdx.x % p.num_kv_heads;
-  const int seq = blockIdx.x / p.num_kv_heads;
+  constexpr int DPL = D / 64;  // output elements per lane
+  const int lane = threadIdx.x & 63;
+  const size_t rowid = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // seq * H + head
+  if (rowid >= (size_t)p.num_seqs * p.num_heads) return;
+  const int seq = (int)(rowid / p.num_heads);
   const int L = clamp_len(p.seq_lens[seq], p.max_seq_len);
   const int nparts = (L + p.partition - 1) / p.partition;
   if (nparts <= 1) return;  // written by the partition kernel
-  const int G = p.group;
-  const size_t row0 = (size_t)seq * p.num_heads + (size_t)kvh * G;
   const int NP = p.num_partitions;
-  merge_pieces<Tag, D>(
-      p, s_red, row0, G, nparts,
-      [&](int h, int q) { return reinterpret_cast<const float2*>(p.ws_ml)[(row0 + h) * NP + q]; },
-      [&](int h, int q) { return p.ws_o + ((row0 + h) * NP + q) * D; });
+  const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + rowid * NP;
+  const float* o = p.ws_o + rowid * NP * D;
+
+  float num[DPL];
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) num[k] = 0.0f;
+  float M = -INFINITY, den = 0.0f;
+  // partitions in chunks of 64: lane q of the chunk holds partition base + q
+  for (int base = 0; base < nparts; base += 64) {
+    const int q = base + lane;
+    const float2 mlq = q < nparts ? ml[q] : make_float2(-INFINITY, 0.0f);
+    float cm = mlq.x;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
+    const float M_new = fmaxf(M, cm);
+    const float alpha = fast_exp2(M - M_new);  // rescale of the earlier chunks
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) num[k] *= alpha;
+    den *= alpha;
+    M = M_new;
+    const float w = q < nparts ? fast_exp2(mlq.x - M) : 0.0f;
+    float dw = w * mlq.y;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) dw += __shfl_xor(dw, off);
+    den += dw;
+    const int n = min(64, nparts - base);
+#pragma unroll 8
+    for (int j = 0; j < n; ++j) {
+      const float wj = __shfl(w, j);
+      const float* oj = o + (size_t)(base + j) * D + lane;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) num[k] += wj * oj[64 * k];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) store_out<Tag>(p, rowid * D + lane + 64 * k, num[k] / den);
 }
 
 // ============================================================================
@@ -484,14 +459,12 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   const int base = ((o_bytes > bt_bytes ? o_bytes : bt_bytes) + 15) & ~15;
   const size_t lds = (size_t)base + 2 * kWaves * 16 * 4;
   const unsigned grid = (unsigned)((size_t)p.num_seqs * p.num_kv_heads * p.num_partitions);
-  decode_partition_kernel<Tag, D, BS><<<dim3(grid), dim3(256), lds, stream>>>(p);
+  decode_partition_kernel<Tag, D, BS><<<dim3(grid), dim3(kThreads), lds, stream>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.num_partitions > 1) {
-    DecodeParams rp = p;
-    rp.red_lds_bytes = (int)reduce_lds_bytes(p.group, p.num_partitions);
-    decode_reduce_kernel<Tag, D>
-        <<<dim3((unsigned)(p.num_seqs * p.num_kv_heads)), dim3(256), rp.red_lds_bytes, stream>>>(rp);
+    const size_t rows = (size_t)p.num_seqs * p.num_heads;
+    decode_reduce_kernel<Tag, D><<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream>>>(p);
     e = hipGetLastError();
   }
   return e;

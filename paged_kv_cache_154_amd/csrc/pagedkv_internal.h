@@ -28,13 +28,16 @@ struct DecodeParams {
   int num_partitions;  // ceil(max_seq_len / partition), >= 1
   float scale_log2;    // scale * log2(e)
   int out_f32;         // 1: out is fp32; 0: out has the KV dtype
-  int red_lds_bytes;  // LDS of a merge workgroup (set by the launcher)
 };
 
 // Tokens a wave handles per step (one MFMA tile of keys).
 constexpr int kTile = 16;
 // Waves per decode workgroup.
-constexpr int kWaves = 4;
+#ifndef PKV_DECODE_WAVES
+#define PKV_DECODE_WAVES 8
+#endif
+constexpr int kWaves = PKV_DECODE_WAVES;
+constexpr int kThreads = 64 * kWaves;
 // Largest partition whose block-table slice is staged in LDS.
 constexpr int kMaxPartition = 16384;
 

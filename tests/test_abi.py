@@ -78,8 +78,8 @@ def test_decode_host_checks(kw, code):
 def test_partition_and_workspace_sizing():
     L = _lib.lib()
     # partition_size 0: the library's choice
-    assert L.paged_attn_partition_tokens(64, 8, 16, 4039, 0) == 512      # few (seq, KV head) pairs
-    assert L.paged_attn_partition_tokens(256, 8, 32, 8192, 0) == 1024    # many, long
+    assert L.paged_attn_partition_tokens(64, 8, 16, 4039, 0) == 1024     # few (seq, KV head) pairs
+    assert L.paged_attn_partition_tokens(256, 8, 32, 8192, 0) == 2048    # many, long
     assert L.paged_attn_partition_tokens(384, 8, 16, 2560, 0) == 2560    # many, short: no split
     assert L.paged_attn_partition_tokens(64, 8, 8, 10000, 512) == 512
     assert L.paged_attn_partition_tokens(64, 8, 32, 100, 48) == SHAPE    # not a multiple of 32
@@ -90,7 +90,7 @@ def test_partition_and_workspace_sizing():
     assert n == 256 * 32 * 20 * (128 + 2) * 4
     assert L.paged_attn_workspace_size(4, 4, 4, 64, 16, 50, 16) == 4 * 4 * 4 * 66 * 4
     assert L.paged_attn_workspace_size(384, 32, 8, 128, 16, 2560, 0) == 0
-    assert L.paged_attn_workspace_size(64, 32, 8, 128, 16, 4039, 0) == 64 * 32 * 8 * 130 * 4
+    assert L.paged_attn_workspace_size(64, 32, 8, 128, 16, 4039, 0) == 64 * 32 * 4 * 130 * 4
 
 
 @pytest.mark.parametrize("call,code", [
