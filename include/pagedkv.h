@@ -93,8 +93,13 @@ enum pkv_status {
  *                When one partition covers max_seq_len it may hold at most
  *                16384 tokens; a splitting partition likewise.
  *   workspace    device scratch of at least paged_attn_workspace_size(...)
- *                bytes for the same arguments (may be NULL when that is 0);
- *                its contents need no initialisation and are garbage after.
+ *                bytes for the same arguments (always needed: its first 256
+ *                bytes hold the decode kernel's item counter, which the call
+ *                resets on the stream itself; the rest holds the split-K
+ *                partials). Its contents need no initialisation and are
+ *                garbage after. Calls that may run at the same time need
+ *                separate workspaces; calls in order on one stream can share
+ *                one.
  * Supported: head_dim 64 or 128; block_size 8, 16 or 32; 1 <= G <= 16;
  * num_blocks * block_size < 2^31.
  */
@@ -119,10 +124,12 @@ int paged_attn_partition_tokens(int num_seqs, int num_kv_heads, int block_size,
                                 int max_seq_len, int partition_size);
 
 /*
- * paged_attn_workspace_size - bytes of split-K workspace paged_attn_decode
- * needs for these arguments: fp32 (max, sum) pairs and head_dim weighted-V
- * partial sums per (sequence, head, partition); 0 when no sequence is split
- * or the arguments are invalid.
+ * paged_attn_workspace_size - bytes of workspace paged_attn_decode needs for
+ * these arguments: a 256-byte header and, when sequences are split, fp32
+ * (max, sum) pairs and head_dim weighted-V partial sums per (sequence, head,
+ * partition) for min(num_seqs, 2048) sequences (larger batches run as
+ * several launches of at most 2048 sequences that reuse them). 0 when the
+ * arguments are invalid or num_seqs is 0.
  */
 size_t paged_attn_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
                                  int head_dim, int block_size, int max_seq_len,

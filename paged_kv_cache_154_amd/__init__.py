@@ -89,8 +89,10 @@ def paged_attn_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.T
                       stream=None) -> torch.Tensor:
     """Decode attention of one query token per sequence over the paged pool.
 
-    ``workspace`` must hold ``paged_attn_workspace_size(...)`` bytes when a
-    sequence is split; with ``workspace=None`` one is allocated by torch."""
+    ``workspace`` must hold ``paged_attn_workspace_size(...)`` bytes (the
+    item counter and split-K partials; no initialisation needed); later calls
+    on the same stream can reuse it. With ``workspace=None`` one is allocated
+    by torch."""
     _require(query.dim() == 3 and out.shape == query.shape, "query/out must be [S, H, D]")
     _require(key_cache.dim() == 4 and value_cache.shape == key_cache.shape,
              "pools must be [num_blocks, block_size, num_kv_heads, head_dim]")

@@ -5,6 +5,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <chrono>
+
 #include "pagedkv.h"
 #include "pagedkv_internal.h"
 
@@ -20,6 +23,7 @@ int elem_bytes(int dtype) {
 }
 
 bool supported_block_size(int bs) { return bs == 8 || bs == 16 || bs == 32; }
+
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 
 // Partition length chosen when partition_size is 0. A workgroup (8 waves)
@@ -56,14 +60,36 @@ int resolve_partition(int num_seqs, int num_kv_heads, int block_size, int max_se
   return P;
 }
 
-int num_partitions(int max_seq_len, int P) {
-  if (max_seq_len <= P) return 1;
-  return (max_seq_len + P - 1) / P;
+// Partitions for these arguments: `partition` tokens (when one covers
+// max_seq_len, the shortest multiple of the tile and block size that does)
+// and `np` partitions per sequence at most.
+struct Cutting {
+  int partition, np;
+};
+
+Cutting cutting_for(int max_seq_len, int block_size, int P) {
+  Cutting c;
+  const int unit = block_size > pkv::kTile ? block_size : pkv::kTile;
+  if (P >= max_seq_len) P = max_seq_len > 0 ? (max_seq_len + unit - 1) / unit * unit : unit;
+  c.partition = P;
+  c.np = max_seq_len > P ? (max_seq_len + P - 1) / P : 1;
+  return c;
 }
+
+// Workspace layout: a 256-byte header (the partition kernel's item counter,
+// tagged with the launch's epoch), then, when sequences are split, fp32 O partials
+// [S', H, NP, D] and (m, l) pairs [S', H, NP, 2] for S' = min(S, the
+// sequences of one launch); launches run in order and reuse them.
+constexpr size_t kHeaderBytes = 256;
 
 size_t split_workspace_bytes(int num_seqs, int num_heads, int head_dim, int np) {
   if (np <= 1) return 0;
-  return (size_t)num_seqs * num_heads * np * (size_t)(head_dim + 2) * sizeof(float);
+  const int s = num_seqs < pkv::kMaxSeqsPerLaunch ? num_seqs : pkv::kMaxSeqsPerLaunch;
+  return (size_t)s * num_heads * np * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+size_t workspace_bytes_for(int num_seqs, int num_heads, int head_dim, int np) {
+  return kHeaderBytes + split_workspace_bytes(num_seqs, num_heads, head_dim, np);
 }
 
 }  // namespace
@@ -83,7 +109,7 @@ size_t paged_attn_workspace_size(int num_seqs, int num_heads, int num_kv_heads, 
   if (!supported_head_dim(head_dim)) return 0;
   const int P = resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
   if (P < 0) return 0;
-  return split_workspace_bytes(num_seqs, num_heads, head_dim, num_partitions(max_seq_len, P));
+  return workspace_bytes_for(num_seqs, num_heads, head_dim, cutting_for(max_seq_len, block_size, P).np);
 }
 
 int paged_attn_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -108,10 +134,14 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
   if (!isfinite(scale)) return PKV_ERR_SHAPE;
   const int P = resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
   if (P < 0) return P;
-  const int np = num_partitions(max_seq_len, P);
-  if ((int64_t)num_seqs * num_kv_heads * np > (int64_t)INT32_MAX) return PKV_ERR_SHAPE;
-  const size_t need = split_workspace_bytes(num_seqs, num_heads, head_dim, np);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  const Cutting cut = cutting_for(max_seq_len, block_size, P);
+  const int np = cut.np;
+  // the items of one launch and its item counter (which overshoots by up to
+  // the grid) stay in int32
+  const int s_launch = num_seqs < pkv::kMaxSeqsPerLaunch ? num_seqs : pkv::kMaxSeqsPerLaunch;
+  if ((int64_t)s_launch * num_kv_heads * np > (int64_t)INT32_MAX - (1 << 24)) return PKV_ERR_SHAPE;
+  const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, np);
+  if (workspace == nullptr || workspace_bytes < need) return PKV_ERR_WORKSPACE;
 
   pkv::DecodeParams p{};
   p.out = out;
@@ -120,9 +150,12 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
   p.v = value_cache;
   p.block_table = block_table;
   p.seq_lens = seq_lens;
-  if (need > 0) {
-    p.ws_o = static_cast<float*>(workspace);
-    p.ws_ml = static_cast<float*>(workspace) + (size_t)num_seqs * num_heads * np * head_dim;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  p.work = reinterpret_cast<unsigned long long*>(ws);
+  if (np > 1) {
+    const int s = num_seqs < pkv::kMaxSeqsPerLaunch ? num_seqs : pkv::kMaxSeqsPerLaunch;
+    p.ws_o = reinterpret_cast<float*>(ws + kHeaderBytes);
+    p.ws_ml = p.ws_o + (size_t)s * num_heads * np * head_dim;
   }
   p.num_seqs = num_seqs;
   p.num_heads = num_heads;
@@ -131,11 +164,11 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
   p.num_blocks = num_blocks;
   p.max_blocks = max_blocks_per_seq;
   p.max_seq_len = max_seq_len;
-  p.partition = P;
+  p.partition = cut.partition;
   p.num_partitions = np;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
-  const hipError_t e = pkv::launch_decode(p, kv_dtype, head_dim, block_size, stream);
+    const hipError_t e = pkv::launch_decode(p, kv_dtype, head_dim, block_size, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -200,3 +233,20 @@ const char* pagedkv_status_string(int status) {
 }
 
 }  // extern "C"
+
+namespace pkv {
+
+// Epochs of decode launches: distinct for every launch of the process and
+// unlikely to match what a workspace header held before (a time-derived
+// start), never 0.
+uint32_t next_launch_epoch() {
+  static std::atomic<uint32_t> counter{(uint32_t)(
+      std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u)};
+  uint32_t e;
+  do {
+    e = counter.fetch_add(1, std::memory_order_relaxed);
+  } while (e == 0);
+  return e;
+}
+
+}  // namespace pkv

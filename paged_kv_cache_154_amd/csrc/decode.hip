@@ -24,21 +24,27 @@
 //  * Tokens past seq_len in the last tile are never read: their address is
 //    clamped to the last valid token (finite data) and their score is set to
 //    -inf before the exponent, so their weight is exactly 0.
-//  * One workgroup of 4 waves per (sequence, KV head, partition of the
-//    sequence). The partition's slice of the block table is staged in LDS
-//    ("the block table of a sequence can be loaded into shared memory at
-//    once", PagedAttention principle section 2.2); the 4 waves take the
-//    partition's tiles round-robin and merge their (max, sum, O) through LDS.
-//    A sequence that fits in one partition is written directly; otherwise
-//    each partition writes (max, sum, O) to the workspace and
-//    decode_reduce_kernel merges them.
-//  * Workgroup i runs on XCD i mod 8. Workgroups are numbered partition-major
-//    and KV-head-minor, so the 8 XCDs share every partition index evenly
-//    (short sequences have only the low partition indices).
+//  * Work items are (sequence, partition of P tokens, KV head). A persistent
+//    grid (as many 8-wave workgroups as fit on the GPU) works through them;
+//    each workgroup builds the launch's schedule in LDS from seq_lens (long
+//    partitions first, each sequence's short first partition last) and
+//    stages an item's slice of the block table in LDS (the page suggests
+//    keeping a sequence's block table in shared memory: PagedAttention
+//    principle, section 2.2). Its 8 waves take the item's tiles round-robin
+//    and merge their (max, sum, O) through LDS. A sequence in one partition
+//    is written directly; otherwise each partition writes (max, sum, O) to
+//    the workspace and decode_reduce_kernel merges them.
+//  * Items are dealt to workgroups in static rounds that keep each KV head on
+//    one XCD, and (unless the batch is of near-uniform length) all items
+//    after the first round are taken from an atomic counter, which evens out
+//    XCDs of different speeds and sequences of different lengths.
 
 #include "pagedkv_internal.h"
 
 #include <math.h>
+
+#include <mutex>
+#include <vector>
 
 namespace pkv {
 namespace {
@@ -143,9 +149,6 @@ template <class Tag, int D>
 struct WavesPerEU {
   static constexpr int value = (Tag::kBytes == 4 && D == 128) ? 2 : 4;
 };
-#ifndef PKV_LPT_ORDER
-#define PKV_LPT_ORDER 1
-#endif
 // log2 of the largest weight allowed before the running max is moved.
 constexpr float kRescaleSlack = 8.0f;
 
@@ -260,58 +263,290 @@ struct TileEngine {
 };
 
 // ============================================================================
-// fixed partitions
+// work list and partition kernel
 // ============================================================================
 
 __host__ __device__ inline int o_stride(int D) { return D + 4; }
 
+// How a sequence of L > 0 tokens is cut into partitions of P tokens (a
+// multiple of 16): n = ceil(L / P) partitions; partition 0 is the short one,
+// [0, r) with r = roundup16(L) - (n-1) P in [16, P]; partitions 1 .. n-1
+// follow, each [r + (j-1) P, r + j P) (the last one ends at L). A sequence in
+// one partition is written out directly; the others are merged by
+// decode_reduce_kernel. The short partitions 0 are scheduled last.
+struct Cut {
+  int n, r;
+};
+
+__device__ inline Cut cut_of(int L, int P) {
+  Cut c;
+  c.n = (L + P - 1) / P;
+  c.r = (L + kTile - 1) / kTile * kTile - (c.n - 1) * P;
+  return c;
+}
+
+// The work list of one launch (at most kMaxSeqsPerLaunch sequences), built
+// by every workgroup in its own LDS from seq_lens when it starts. Entries are
+// (sequence, partition):
+//   * first the full partitions n-1 .. 1 of every split sequence, in batch
+//     order: sequence s owns entries [full[s], full[s+1]) (an exclusive scan
+//     of n_s - 1);
+//   * then the partition 0 of every sequence, stably sorted into kClasses
+//     length classes, longest first; sequences of length 0 (one empty entry
+//     that writes the zero row) last.
+// Item w is entry w / num_kv_heads with KV head w % num_kv_heads. Long items
+// first and short ones last even out the end of the launch; the stable order
+// keeps sequences that sit next to each other in the batch (such as samples
+// of one prompt sharing its blocks) next to each other in time.
+constexpr int kClasses = 4;
+constexpr int kClassBits = 12;  // packed per-class counts: kMaxSeqsPerLaunch < 2^12
+static_assert(kMaxSeqsPerLaunch < (1 << kClassBits), "class counts must fit their field");
+static_assert((kClasses + 1) * kClassBits <= 64, "class counts must pack into 64 bits");
+constexpr int kSeqsPerThread = (kMaxSeqsPerLaunch + kThreads - 1) / kThreads;
+
+__host__ __device__ inline int plan_bytes(int S) { return ((S + 1) * 4 + S * 2 + 15) & ~15; }
+
+struct Plan {
+  int* full;         // [S + 1]
+  uint16_t* first;   // [S]: partitions 0, sorted
+  int S;
+  int n_full;        // entries of full partitions
+  int n_long;        // entries in the longest class (full partitions included)
+};
+
+__device__ inline Plan plan_at(unsigned char* base, int S) {
+  Plan pl;
+  pl.full = reinterpret_cast<int*>(base);
+  pl.first = reinterpret_cast<uint16_t*>(pl.full + S + 1);
+  pl.S = S;
+  pl.n_full = pl.n_long = 0;
+  return pl;
+}
+
+// Class of a partition 0 of `len` tokens (1 .. P): 0 (longest) ..
+// kClasses-1; kClasses for an empty sequence (len 0).
+__device__ inline int length_class(int len, int P) {
+  if (len == 0) return kClasses;
+  return (kClasses - 1) - (int)(((int64_t)(len - 1) * kClasses) / P);
+}
+
+__device__ inline uint64_t shfl_up_u64(uint64_t v, int o) {
+  const int lo = __shfl_up((int)(uint32_t)v, o);
+  const int hi = __shfl_up((int)(uint32_t)(v >> 32), o);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Builds the plan in LDS. Thread t takes the consecutive sequences
+// [t K, t K + K); one block-wide exclusive scan of (full partitions, packed
+// per-class counts) gives every sequence its entries. `xw` is LDS scratch
+// for 2 * kWaves 64-bit values. Ends with a barrier.
+__device__ void build_plan(const DecodeParams& p, Plan& pl, uint64_t* xw) {
+  const int S = pl.S;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int K = (S + kThreads - 1) / kThreads;
+  const int s0 = threadIdx.x * K;
+  int a_of[kSeqsPerThread], c_of[kSeqsPerThread];
+  int na = 0;
+  uint64_t cls = 0;
+#pragma unroll
+  for (int k = 0; k < kSeqsPerThread; ++k) {
+    a_of[k] = c_of[k] = 0;
+    const int s = s0 + k;
+    if (k < K && s < S) {
+      const int L = clamp_len(p.seq_lens[s], p.max_seq_len);
+      if (L == 0) {
+        c_of[k] = kClasses;
+      } else {
+        const Cut c = cut_of(L, p.partition);
+        a_of[k] = c.n - 1;
+        c_of[k] = length_class(c.r, p.partition);
+      }
+      na += a_of[k];
+      cls += 1ull << (kClassBits * c_of[k]);
+    }
+  }
+  uint64_t ia = (uint32_t)na, ic = cls;  // inclusive scans in the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t ta = shfl_up_u64(ia, o);
+    const uint64_t tc = shfl_up_u64(ic, o);
+    if (lane >= o) {
+      ia += ta;
+      ic += tc;
+    }
+  }
+  if (lane == 63) {
+    xw[2 * wave] = ia;
+    xw[2 * wave + 1] = ic;
+  }
+  __syncthreads();
+  uint64_t ba = 0, bc = 0, ta = 0, tc = 0;  // before this wave; totals
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint64_t xa = xw[2 * w], xc = xw[2 * w + 1];
+    if (w < wave) {
+      ba += xa;
+      bc += xc;
+    }
+    ta += xa;
+    tc += xc;
+  }
+  int pa = (int)(ba + ia) - na;
+  const uint64_t pc = bc + ic - cls;
+  int cbase[kClasses + 1];
+  int run = 0;
+#pragma unroll
+  for (int c = 0; c <= kClasses; ++c) {
+    cbase[c] = run + (int)((pc >> (kClassBits * c)) & ((1u << kClassBits) - 1));
+    run += (int)((tc >> (kClassBits * c)) & ((1u << kClassBits) - 1));
+  }
+#pragma unroll
+  for (int k = 0; k < kSeqsPerThread; ++k) {
+    const int s = s0 + k;
+    if (k < K && s < S) {
+      pl.full[s] = pa;
+      pa += a_of[k];
+#pragma unroll
+      for (int c = 0; c <= kClasses; ++c)
+        if (c == c_of[k]) pl.first[cbase[c]++] = (uint16_t)s;
+    }
+  }
+  if (threadIdx.x == 0) pl.full[S] = (int)ta;
+  __syncthreads();
+  pl.n_full = uniform(pl.full[S]);
+  pl.n_long = pl.n_full + (int)(tc & ((1u << kClassBits) - 1));
+}
+
+// Entry e of the plan: (sequence, partition), both wave-uniform.
+__device__ inline void plan_entry(const Plan& pl, int e, int& seq, int& part) {
+  if (e < pl.n_full) {
+    int lo = 0, hi = pl.S;  // full[lo] <= e < full[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (uniform(pl.full[mid]) <= e) lo = mid; else hi = mid;
+    }
+    seq = lo;
+    part = uniform(pl.full[lo + 1]) - e;  // highest partition first
+  } else {
+    seq = uniform(pl.first[e - pl.n_full]);
+    part = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Schedule of one launch over a persistent grid of `grid` workgroups (a
+// multiple of 8). Items below a split point are dealt statically in rounds of
+// `grid`: workgroup b takes item b of round 0, and of each later round item b
+// or, on odd rounds, item grid-1-b (alternating directions even out the
+// long-first items). Workgroup b runs on XCD b mod 8, so with items numbered
+// KV head fastest each XCD keeps to a fixed set of KV heads within a round,
+// and the KV heads of the same tokens are worked on at the same time on
+// different XCDs; on MI355X numbering the same work sequence-fastest instead
+// is 8-20% slower, and a shared prompt's blocks are reused from the XCD's L2.
+// The items from the split point on are taken one at a time from a counter,
+// which evens out workgroups and XCDs that run at different speeds and
+// items of different lengths. When nearly all entries are of the longest
+// class (a batch of similar lengths) every item is dealt statically (kept on
+// its XCD, which helps most when sequences share blocks); otherwise all
+// items after the first round go through the counter.
+// The counter is the first 64-bit word of the workspace (see take_ticket).
+
+__device__ inline int static_end(int total, int grid, bool uniform_batch) {
+  if (uniform_batch) return total;
+  return total < grid ? total : grid;  // every workgroup's first item is static
+}
+
+// LDS budget of one workgroup when two share a CU (160 KiB each).
+constexpr int kLdsPerWorkgroup = 80 * 1024;
+
+// Ticket for the next counter item of launch `epoch`. The counter is one
+// 64-bit word of the workspace, (epoch << 32) | items taken. A word left by
+// an earlier launch (or any other contents: the workspace needs no
+// initialisation) carries another epoch; the first workgroup to meet it
+// installs (epoch, 1) with a compare-and-swap and takes ticket 0, and every
+// later take sees the launch's epoch. Each failed compare-and-swap means that
+// another workgroup changed the word, so the loop ends within a few rounds;
+// should it not within kTicketTries, the workgroup returns -1 and takes its
+// counter items statically instead (items taken twice are computed twice
+// with identical results, so the output never depends on the header).
+constexpr int kTicketTries = 64;
+
+__device__ inline int take_ticket(unsigned long long* word, uint32_t epoch) {
+  const unsigned long long tag = (unsigned long long)epoch << 32;
+  unsigned long long old = atomicAdd(word, 1ull);
+#pragma unroll 1
+  for (int i = 0; i < kTicketTries; ++i) {
+    if ((old >> 32) == epoch) return (int)(uint32_t)old;
+    const unsigned long long seen = atomicCAS(word, old + 1, tag | 1ull);
+    if (seen == old + 1) return 0;
+    if ((seen >> 32) == epoch) {
+      old = atomicAdd(word, 1ull);
+    } else {
+      old = seen - 1;  // compare against what is there now
+    }
+  }
+  return -1;
+}
+
+// Puts the counter at (epoch, 0) unless it already carries the epoch: done
+// by workgroup 0 as it starts, so that the first takes of the other
+// workgroups (after a whole item each) find the epoch installed and cost a
+// single atomic each. take_ticket stays correct without it.
+__device__ inline void install_epoch(unsigned long long* word, uint32_t epoch) {
+  const unsigned long long tag = (unsigned long long)epoch << 32;
+  unsigned long long cur = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll 1
+  for (int i = 0; i < kTicketTries && (cur >> 32) != epoch; ++i) {
+    const unsigned long long seen = atomicCAS(word, cur, tag);
+    if (seen == cur) break;
+    cur = seen;
+  }
+}
+
+// LDS of the partition kernel: the partition's block-table slice, reused for
+// the waves' O rows (and at the start for the plan's scan); then the waves'
+// (m, l); then the next item; then the plan.
+__host__ __device__ inline int lds_main_bytes(int D, int G, int span, int BS) {
+  const int o_bytes = kWaves * G * o_stride(D) * 4;
+  const int bt_bytes = (span / BS + 1) * 4;
+  return ((o_bytes > bt_bytes ? o_bytes : bt_bytes) + 15) & ~15;
+}
+__host__ __device__ inline int lds_total_bytes(int D, int G, int span, int BS, int S) {
+  return lds_main_bytes(D, G, span, BS) + 2 * kWaves * 16 * 4 + 16 + plan_bytes(S);
+}
+
+// One work item: KV head kvh of partition `part` of sequence `seq`, by the
+// whole workgroup. Waves take its 16-token tiles round-robin and merge
+// (m, l, O) through LDS; a sequence in one partition is normalised and
+// written to out, the others write partials to the workspace. With `draw`,
+// thread 0 takes a ticket from the counter for the workgroup's next item.
 template <class Tag, int D, int BS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEU<Tag, D>::value)))
-void decode_partition_kernel(DecodeParams p) {
+__device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char* smem, int lds_main,
+                                            int seq, int kvh, int part, int tid, int wave,
+                                            bool draw, int& ticket) {
+  const int lane = tid & 63;
   using Eng = TileEngine<Tag, D, BS>;
   constexpr int RB = Eng::RB;
   constexpr int VPL = Eng::VPL;
-
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
-
-  // Workgroup i runs on XCD i mod 8. The KV head varies fastest and the
-  // partition slowest, so each XCD gets an even share of every partition
-  // index (only low partition indices exist for short sequences).
-  int wg = blockIdx.x;
-  const int kvh = wg % p.num_kv_heads;
-  wg /= p.num_kv_heads;
-  const int seq = wg % p.num_seqs;
-#if PKV_LPT_ORDER
-  const int part = p.num_partitions - 1 - wg / p.num_seqs;
-#else
-  const int part = wg / p.num_seqs;
-#endif
   const int G = p.group;
   const int head0 = kvh * G;
 
   const int L = clamp_len(p.seq_lens[seq], p.max_seq_len);
   if (L == 0) {  // nothing to attend to: a zero row
-    if (part == 0) {
-      for (int idx = threadIdx.x; idx < G * D; idx += kThreads)
-        store_out<Tag>(p, ((size_t)seq * p.num_heads + head0) * D + idx, 0.0f);
-    }
+    if (draw && tid == 0) ticket = take_ticket(p.work, p.epoch);
+    for (int idx = tid; idx < G * D; idx += kThreads)
+      store_out<Tag>(p, ((size_t)seq * p.num_heads + head0) * D + idx, 0.0f);
     return;
   }
-  const int nparts = (L + p.partition - 1) / p.partition;
-  if (part >= nparts) return;
-#if PKV_LPT_ORDER
-  // Partition 0 is the short one: [0, first) with first in (0, P], a multiple
-  // of 16; partitions 1.. are full. Workgroups run from the highest partition
-  // index down, so the long partitions start first and the short ones last.
-  const int first = (L + kTile - 1) / kTile * kTile - (nparts - 1) * p.partition;
-  const int t_begin = part == 0 ? 0 : first + (part - 1) * p.partition;
-  const int t_end = min(L, part == 0 ? first : t_begin + p.partition);
-#else
-  const int t_begin = part * p.partition;
-  const int t_end = min(L, t_begin + p.partition);
-#endif
+  const Cut c = cut_of(L, p.partition);
+  const int nparts = c.n;
+  const int t_begin = part == 0 ? 0 : c.r + (part - 1) * p.partition;
+  const int t_end = min(L, part == 0 ? c.r : t_begin + p.partition);
+  if (t_begin >= t_end) {  // only for a seq_lens entry changed under the launch
+    if (draw && tid == 0) ticket = take_ticket(p.work, p.epoch);
+    return;
+  }
 
   // ---- stage this partition's slice of the block-table row --------------
   int* s_bt = reinterpret_cast<int*>(smem);
@@ -319,13 +554,13 @@ void decode_partition_kernel(DecodeParams p) {
   const int nlb = (t_end + BS - 1) / BS - lb0;
   {
     const int32_t* row = p.block_table + (size_t)seq * p.max_blocks + lb0;
-    for (int i = threadIdx.x; i < nlb; i += kThreads) {
+    for (int i = tid; i < nlb; i += kThreads) {
       const int b = row[i];
       s_bt[i] = ((unsigned)b < (unsigned)p.num_blocks) ? b : 0;  // never leave the pool
     }
   }
 
-  TileEngine<Tag, D, BS> eng;
+  Eng eng;
   eng.init(lane);
   eng.load_q(static_cast<const unsigned char*>(p.q) + ((size_t)seq * p.num_heads + head0) * RB, G);
   eng.reset();
@@ -344,15 +579,17 @@ void decode_partition_kernel(DecodeParams p) {
   for (int cs = t_begin + wave * kTile; cs < t_end; cs += kWaves * kTile)
     eng.step(kbase, vbase, cs, t_end - 1, slot_bytes, p.scale_log2, row_off);
 
-  // ---- merge the 4 waves -------------------------------------------------
+  // ---- merge the waves ---------------------------------------------------
   const float lsum = eng.total_sum();
   __syncthreads();  // block-table slice no longer needed: reuse its LDS
+  // Every wave is done with its tiles: a workgroup in the dynamic part of the
+  // schedule draws the ticket for its next item now, while it merges, so that
+  // items taken one after the other (the KV heads of the same tokens) start
+  // close together in time.
+  if (draw && tid == 0) ticket = take_ticket(p.work, p.epoch);
   const int OST = o_stride(D);
   float* s_o = reinterpret_cast<float*>(smem);
-  const int o_bytes_all = kWaves * G * OST * 4;
-  const int bt_bytes = ((p.partition < p.max_seq_len ? p.partition : p.max_seq_len) / BS + 1) * 4;
-  const int base = ((o_bytes_all > bt_bytes ? o_bytes_all : bt_bytes) + 15) & ~15;
-  float* s_m = reinterpret_cast<float*>(smem + base);
+  float* s_m = reinterpret_cast<float*>(smem + lds_main);
   float* s_l = s_m + kWaves * 16;
   if (eng.col < G) {
     if (eng.grp == 0) {
@@ -367,7 +604,7 @@ void decode_partition_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+  for (int idx = tid; idx < G * D; idx += kThreads) {
     const int h = idx / D;
     const int d = idx - h * D;
     float M = -INFINITY;
@@ -394,6 +631,67 @@ void decode_partition_kernel(DecodeParams p) {
   }
 }
 
+// Persistent: a grid of as many workgroups as fit on the GPU at once (a
+// multiple of 8), each working through its items of the schedule above. A
+// workgroup whose next item is a counter one draws a ticket while it merges
+// its current item; every ticket advances the counter, and a workgroup
+// without ticket steps through its static share of the counter items, so
+// every workgroup ends.
+template <class Tag, int D, int BS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEU<Tag, D>::value)))
+void decode_partition_kernel(DecodeParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int wave = uniform(threadIdx.x >> 6);
+  const int span = p.partition < p.max_seq_len ? p.partition : p.max_seq_len;
+  const int lds_main = lds_main_bytes(D, p.group, span, BS);
+  // Two slots for the next item, used alternately: an item may pass no
+  // barrier (a zero-length sequence), and a slot is rewritten only after the
+  // barrier that follows every wave's read of it.
+  int* s_next = reinterpret_cast<int*>(smem + lds_main + 2 * kWaves * 16 * 4);
+  if (blockIdx.x == 0 && threadIdx.x == 0) install_epoch(p.work, p.epoch);
+  Plan pl = plan_at(reinterpret_cast<unsigned char*>(s_next + 4), p.num_seqs);
+  build_plan(p, pl, reinterpret_cast<uint64_t*>(smem));
+  const int entries = pl.n_full + pl.S;
+  const int total = entries * p.num_kv_heads;
+  const int grid = (int)gridDim.x;
+  const int ws = static_end(total, grid, 8 * pl.n_long >= 7 * entries);
+  const int b = (int)blockIdx.x;
+
+  int parity = 0;
+  int round = 0;          // static round of the current item
+  bool fallback = false;  // thread 0: taking counter items statically
+  for (int w = b; (unsigned)w < (unsigned)total; parity ^= 1) {
+    const int e = w / p.num_kv_heads;
+    const int kvh = w - e * p.num_kv_heads;
+    int seq, part;
+    plan_entry(pl, e, seq, part);
+    ++round;
+    const int nxt_static = round * grid + ((round & 1) ? grid - 1 - b : b);
+    const bool draw = w >= ws || nxt_static >= ws;  // the next item is a counter one
+    int ticket = 0;
+    // The thread index passes through an empty asm statement so that the
+    // lane-dependent addressing is recomputed per item instead of being
+    // hoisted out of this loop and held in registers across the tiles.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    decode_item<Tag, D, BS>(p, smem, lds_main, seq, kvh, part, tid, wave, draw, ticket);
+    if (threadIdx.x == 0) {
+      int64_t nx;
+      if (!draw) {
+        nx = nxt_static;
+      } else if (ticket >= 0 && !fallback) {
+        nx = (int64_t)ws + ticket;
+      } else {  // no ticket: the counter items ws + b, ws + b + grid, ...
+        nx = fallback ? (int64_t)w + grid : (int64_t)ws + b;
+        fallback = true;
+      }
+      s_next[parity] = (nx >= 0 && nx < total) ? (int)nx : total;
+    }
+    __syncthreads();
+    w = uniform(s_next[parity]);
+  }
+}
+
 // One wave per (sequence, query head) of a split sequence, 4 waves per
 // workgroup. Lane q loads (m_q, l_q) of partition q and the partial O loads
 // do not wait for the weights, so the merge costs about one memory round
@@ -406,7 +704,8 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams p) {
   if (rowid >= (size_t)p.num_seqs * p.num_heads) return;
   const int seq = (int)(rowid / p.num_heads);
   const int L = clamp_len(p.seq_lens[seq], p.max_seq_len);
-  const int nparts = (L + p.partition - 1) / p.partition;
+  if (L == 0) return;  // written by the partition kernel
+  const int nparts = cut_of(L, p.partition).n;
   if (nparts <= 1) return;  // written by the partition kernel
   const int NP = p.num_partitions;
   const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + rowid * NP;
@@ -451,23 +750,70 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams p) {
 // launchers
 // ============================================================================
 
+// Workgroups of the partition kernel that fit on the device at once (the
+// persistent grid), cached per (device, kernel, LDS bytes).
+int resident_workgroups(const void* kernel, size_t lds) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  struct Entry { int dev; const void* k; size_t lds; int n; };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    for (const Entry& c : cache)
+      if (c.dev == dev && c.k == kernel && c.lds == lds) return c.n;
+  }
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kThreads, lds) != hipSuccess || per <= 0)
+    per = 1;
+  const int n = cus * per;
+  std::lock_guard<std::mutex> g(mu);
+  cache.push_back(Entry{dev, kernel, lds, n});
+  return n;
+}
+
 template <class Tag, int D, int BS>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   const int span = p.partition < p.max_seq_len ? p.partition : p.max_seq_len;
-  const int bt_bytes = (span / BS + 1) * 4;
-  const int o_bytes = kWaves * p.group * o_stride(D) * 4;
-  const int base = ((o_bytes > bt_bytes ? o_bytes : bt_bytes) + 15) & ~15;
-  const size_t lds = (size_t)base + 2 * kWaves * 16 * 4;
-  const unsigned grid = (unsigned)((size_t)p.num_seqs * p.num_kv_heads * p.num_partitions);
-  decode_partition_kernel<Tag, D, BS><<<dim3(grid), dim3(kThreads), lds, stream>>>(p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (p.num_partitions > 1) {
-    const size_t rows = (size_t)p.num_seqs * p.num_heads;
-    decode_reduce_kernel<Tag, D><<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream>>>(p);
-    e = hipGetLastError();
+  const void* kfn = reinterpret_cast<const void*>(&decode_partition_kernel<Tag, D, BS>);
+  const size_t q_row = (size_t)p.num_heads * D;
+  const size_t out_elem = p.out_f32 ? 4 : (size_t)Tag::kBytes;
+  // Launches of at most `chunk` sequences each, in order on the stream; they
+  // share the workspace (header, partials). The chunk keeps the LDS of a
+  // workgroup (its plan grows with the sequences) within half a CU's 160 KiB,
+  // so that two workgroups fit per CU, when the rest of it leaves room.
+  int chunk = kMaxSeqsPerLaunch;
+  {
+    const int fixed = lds_total_bytes(D, p.group, span, BS, 0);
+    const int room = (kLdsPerWorkgroup - fixed - 32) / 10;
+    if (room < chunk) chunk = room > 256 ? room : 256;
   }
-  return e;
+  for (int s0 = 0; s0 < p.num_seqs; s0 += chunk) {
+    DecodeParams c = p;
+    c.epoch = next_launch_epoch();  // each launch tags its own item counter
+    c.num_seqs = p.num_seqs - s0 < chunk ? p.num_seqs - s0 : chunk;
+    c.q = static_cast<const unsigned char*>(p.q) + (size_t)s0 * q_row * Tag::kBytes;
+    c.out = static_cast<unsigned char*>(p.out) + (size_t)s0 * q_row * out_elem;
+    c.block_table = p.block_table + (size_t)s0 * p.max_blocks;
+    c.seq_lens = p.seq_lens + s0;
+    const size_t lds = (size_t)lds_total_bytes(D, c.group, span, BS, c.num_seqs);
+    const int64_t max_items = (int64_t)c.num_seqs * c.num_kv_heads * c.num_partitions;
+    int64_t grid = resident_workgroups(kfn, lds);
+    if (grid > max_items) grid = max_items;
+    if (grid >= 8) grid = grid / 8 * 8;  // whole rounds over the 8 XCDs
+    decode_partition_kernel<Tag, D, BS><<<dim3((unsigned)grid), dim3(kThreads), lds, stream>>>(c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (c.num_partitions > 1) {
+      const size_t rows = (size_t)c.num_seqs * c.num_heads;
+      decode_reduce_kernel<Tag, D><<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream>>>(c);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }
 
 template <class Tag, int D>

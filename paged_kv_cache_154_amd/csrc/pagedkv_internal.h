@@ -15,8 +15,10 @@ struct DecodeParams {
   const void* v;
   const int32_t* block_table;
   const int32_t* seq_lens;
-  float* ws_o;   // [S, H, NP, D] weighted-V partial sums (split only)
-  float* ws_ml;  // [S, H, NP, 2] (running max in log2 units, sum of weights)
+  unsigned long long* work;  // item counter: (epoch << 32) | items taken
+  uint32_t epoch;            // set per launch: nonzero, distinct within the process
+  float* ws_o;    // [S, H, NP, D] weighted-V partial sums (split only)
+  float* ws_ml;   // [S, H, NP, 2] (running max in log2 units, sum of weights)
   int num_seqs;
   int num_heads;
   int num_kv_heads;
@@ -25,7 +27,7 @@ struct DecodeParams {
   int max_blocks;      // block-table row length
   int max_seq_len;
   int partition;       // tokens per partition (multiple of 16 and block_size)
-  int num_partitions;  // ceil(max_seq_len / partition), >= 1
+  int num_partitions;  // partitions per sequence at most (ceil(max_seq_len / partition)), >= 1
   float scale_log2;    // scale * log2(e)
   int out_f32;         // 1: out is fp32; 0: out has the KV dtype
 };
@@ -40,6 +42,11 @@ constexpr int kWaves = PKV_DECODE_WAVES;
 constexpr int kThreads = 64 * kWaves;
 // Largest partition whose block-table slice is staged in LDS.
 constexpr int kMaxPartition = 16384;
+// Sequences per launch of the partition kernel (its schedule lives in LDS).
+constexpr int kMaxSeqsPerLaunch = 2048;
+
+// A fresh epoch for one launch of the decode kernel (see DecodeParams::work).
+uint32_t next_launch_epoch();
 
 hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim,
                          int block_size, hipStream_t stream);

@@ -68,7 +68,8 @@ def _decode(**kw):
     (dict(scale=float("nan")), SHAPE),
     (dict(P=24), SHAPE),                       # not a multiple of 16
     (dict(P=-16), SHAPE),
-    (dict(maxlen=4096, MB=256, P=64), WS),     # split needs a workspace
+    (dict(maxlen=4096, MB=256, P=64), WS),     # a workspace is always needed
+    (dict(maxlen=256, P=256), WS),
     (dict(maxlen=20000, MB=2000, P=20000), UNSUP),  # one partition too long for LDS
 ])
 def test_decode_host_checks(kw, code):
@@ -83,14 +84,18 @@ def test_partition_and_workspace_sizing():
     assert L.paged_attn_partition_tokens(384, 8, 16, 2560, 0) == 2560    # many, short: no split
     assert L.paged_attn_partition_tokens(64, 8, 8, 10000, 512) == 512
     assert L.paged_attn_partition_tokens(64, 8, 32, 100, 48) == SHAPE    # not a multiple of 32
-    # no split when one partition covers the longest sequence
-    assert L.paged_attn_workspace_size(64, 32, 8, 128, 16, 512, 512) == 0
-    # split: fp32 (max, sum) + head_dim partial sums per (seq, head, partition)
+    # a 256-byte header (the item counters) and, when sequences are split, fp32
+    # (max, sum) + head_dim partial sums per (seq, head, partition) for at most
+    # 2048 sequences (larger batches run as several launches that reuse them)
+    hdr = 256
+    assert L.paged_attn_workspace_size(64, 32, 8, 128, 16, 512, 512) == hdr   # no split
     n = L.paged_attn_workspace_size(256, 32, 8, 128, 8, 10000, 512)
-    assert n == 256 * 32 * 20 * (128 + 2) * 4
-    assert L.paged_attn_workspace_size(4, 4, 4, 64, 16, 50, 16) == 4 * 4 * 4 * 66 * 4
-    assert L.paged_attn_workspace_size(384, 32, 8, 128, 16, 2560, 0) == 0
-    assert L.paged_attn_workspace_size(64, 32, 8, 128, 16, 4039, 0) == 64 * 32 * 4 * 130 * 4
+    assert n == hdr + 256 * 32 * 20 * (128 + 2) * 4
+    assert L.paged_attn_workspace_size(4, 4, 4, 64, 16, 50, 16) == hdr + 4 * 4 * 4 * 66 * 4
+    assert L.paged_attn_workspace_size(384, 32, 8, 128, 16, 2560, 0) == hdr
+    assert L.paged_attn_workspace_size(64, 32, 8, 128, 16, 4039, 0) == hdr + 64 * 32 * 4 * 130 * 4
+    assert L.paged_attn_workspace_size(5000, 8, 8, 64, 16, 4096, 1024) == hdr + 2048 * 8 * 4 * 66 * 4
+    assert L.paged_attn_workspace_size(0, 32, 8, 128, 16, 4039, 0) == 0
 
 
 @pytest.mark.parametrize("call,code", [

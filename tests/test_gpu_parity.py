@@ -300,6 +300,78 @@ def test_copy_on_write_remap_is_bitwise_invariant():
 
 
 # ----------------------------------------------------------------------------
+# the workspace and the persistent kernel's schedule
+# ----------------------------------------------------------------------------
+
+def _decode_into(wl, d, ws, P, out_dtype=torch.float32):
+    out = torch.empty(wl.query.shape, dtype=out_dtype, device=DEV)
+    pkv.paged_attn_decode(out, d["q"], d["kc"], d["vc"], d["bt"], d["sl"], wl.scale,
+                          wl.max_seq_len, P, workspace=ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_one_workspace_serves_many_calls():
+    """The workspace needs no initialisation: filled with garbage before each
+    call (the item counter included), one buffer serves calls of different
+    shapes and partitions in turn."""
+    a = W.custom(21, seq_lens=[5, 700, 1300, 64, 2], num_heads=16, num_kv_heads=4, head_dim=128,
+                 block_size=16, dtype=torch.bfloat16)
+    b = W.custom(22, seq_lens=list(range(1, 301, 7)), num_heads=8, num_kv_heads=8, head_dim=64,
+                 block_size=8, dtype=torch.float16)
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device=DEV)
+    runs = [(a, 64), (b, 0), (a, 0), (b, 32), (a, 64)]
+    refs = {id(a): oracle_step(a)[0], id(b): oracle_step(b)[0]}
+    devs = {id(a): to_dev(a), id(b): to_dev(b)}
+    g = torch.Generator(device=DEV).manual_seed(5)
+    for i, (wl, P) in enumerate(runs):
+        need = pkv.paged_attn_workspace_size(wl.num_seqs, wl.num_heads, wl.num_kv_heads,
+                                             wl.head_dim, wl.block_size, wl.max_seq_len, P)
+        assert need <= ws.numel()
+        if i % 2:
+            ws.fill_(0xFF)
+        else:
+            ws.copy_(torch.randint(0, 256, ws.shape, generator=g, device=DEV, dtype=torch.uint8))
+        say(f"shared workspace: S={wl.num_seqs} P={P}")
+        out = _decode_into(wl, devs[id(wl)], ws, P)
+        assert max_err(out, refs[id(wl)]) <= TOL[wl.dtype]
+
+
+def test_more_sequences_than_one_launch():
+    """4500 sequences run as launches of at most 2048 (each with its own
+    schedule); rows on both sides of each launch boundary are checked."""
+    rng = np.random.default_rng(23)
+    lens = rng.integers(1, 121, size=4500).tolist()
+    lens[2047], lens[2048], lens[4095], lens[4096] = 300, 1, 0, 250
+    wl = W.custom(23, seq_lens=lens, num_heads=4, num_kv_heads=2, head_dim=64, block_size=16,
+                  dtype=torch.bfloat16)
+    seqs = sorted(set([0, 1, 2046, 2047, 2048, 2049, 4094, 4095, 4096, 4097, 4499]
+                      + rng.choice(4500, size=40, replace=False).tolist()))
+    ref, _, _ = oracle_step(wl, seqs=seqs)
+    d = to_dev(wl)
+    for P in (0, 128):
+        say(f"4500 sequences, P={P}")
+        out = gpu_step(wl, d, out_dtype=torch.float32, partition_size=P)
+        assert torch.isfinite(out).all()
+        assert max_err(out, ref, seqs) <= TOL[torch.bfloat16]
+        assert torch.equal(out[4095], torch.zeros_like(out[4095]))
+
+
+def test_schedule_order_does_not_change_results():
+    """Reversing the batch changes every sequence's place in the schedule
+    (and which workgroup runs it) but not its output bits."""
+    wl = W.custom(24, seq_lens=[3000, 17, 1200, 1, 0, 640, 2049, 96], num_heads=32,
+                  num_kv_heads=8, head_dim=128, block_size=16, dtype=torch.bfloat16)
+    d = to_dev(wl)
+    say("schedule order")
+    out = gpu_step(wl, d, out_dtype=torch.float32, partition_size=512)
+    r = torch.arange(wl.num_seqs - 1, -1, -1, device=DEV)
+    d2 = dict(d, q=d["q"][r].contiguous(), bt=d["bt"][r].contiguous(), sl=d["sl"][r].contiguous())
+    out2 = gpu_step(wl, d2, out_dtype=torch.float32, partition_size=512)
+    assert torch.equal(bits(out[r]), bits(out2))
+
+
+# ----------------------------------------------------------------------------
 # the five page-shaped workloads at full size
 # ----------------------------------------------------------------------------
 
