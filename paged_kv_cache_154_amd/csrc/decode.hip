@@ -304,10 +304,11 @@ static_assert(kMaxSeqsPerLaunch < (1 << kClassBits), "class counts must fit thei
 static_assert((kClasses + 1) * kClassBits <= 64, "class counts must pack into 64 bits");
 constexpr int kSeqsPerThread = (kMaxSeqsPerLaunch + kThreads - 1) / kThreads;
 
-__host__ __device__ inline int plan_bytes(int S) { return ((S + 1) * 4 + S * 2 + 15) & ~15; }
+__host__ __device__ inline int plan_bytes(int S) { return ((S + 1) * 4 + S * 4 + S * 2 + 15) & ~15; }
 
 struct Plan {
   int* full;         // [S + 1]
+  int* len;          // [S]: sequence lengths, clamped to max_seq_len
   uint16_t* first;   // [S]: partitions 0, sorted
   int S;
   int n_full;        // entries of full partitions
@@ -317,7 +318,8 @@ struct Plan {
 __device__ inline Plan plan_at(unsigned char* base, int S) {
   Plan pl;
   pl.full = reinterpret_cast<int*>(base);
-  pl.first = reinterpret_cast<uint16_t*>(pl.full + S + 1);
+  pl.len = pl.full + S + 1;
+  pl.first = reinterpret_cast<uint16_t*>(pl.len + S);
   pl.S = S;
   pl.n_full = pl.n_long = 0;
   return pl;
@@ -355,6 +357,7 @@ __device__ void build_plan(const DecodeParams& p, Plan& pl, uint64_t* xw) {
     const int s = s0 + k;
     if (k < K && s < S) {
       const int L = clamp_len(p.seq_lens[s], p.max_seq_len);
+      pl.len[s] = L;
       if (L == 0) {
         c_of[k] = kClasses;
       } else {
@@ -523,7 +526,7 @@ __host__ __device__ inline int lds_total_bytes(int D, int G, int span, int BS, i
 // thread 0 takes a ticket from the counter for the workgroup's next item.
 template <class Tag, int D, int BS>
 __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char* smem, int lds_main,
-                                            int seq, int kvh, int part, int tid, int wave,
+                                            int seq, int L, int kvh, int part, int tid, int wave,
                                             bool draw, int& ticket) {
   const int lane = tid & 63;
   using Eng = TileEngine<Tag, D, BS>;
@@ -532,7 +535,6 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   const int G = p.group;
   const int head0 = kvh * G;
 
-  const int L = clamp_len(p.seq_lens[seq], p.max_seq_len);
   if (L == 0) {  // nothing to attend to: a zero row
     if (draw && tid == 0) ticket = take_ticket(p.work, p.epoch);
     for (int idx = tid; idx < G * D; idx += kThreads)
@@ -674,7 +676,7 @@ void decode_partition_kernel(DecodeParams p) {
     // hoisted out of this loop and held in registers across the tiles.
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    decode_item<Tag, D, BS>(p, smem, lds_main, seq, kvh, part, tid, wave, draw, ticket);
+    decode_item<Tag, D, BS>(p, smem, lds_main, seq, uniform(pl.len[seq]), kvh, part, tid, wave, draw, ticket);
     if (threadIdx.x == 0) {
       int64_t nx;
       if (!draw) {
