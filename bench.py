@@ -14,7 +14,18 @@ time. The roofline entry is for the decode call (partition kernel plus the
 split-K merge kernel), timed with HIP events on the stream the library
 launches on.
 
-    python bench.py [--steps K] [--warmup W] [--layers N] [--no-cpu-baseline]
+The line also carries the streaming-read rate the same GPU reaches (the
+library's stream-read kernel over a 4 GiB buffer, best of a few grid sizes)
+and the decode call's share of it, and p10/p50/p90 of the decode call.
+``--secondary`` adds the measurements the pages give context for: a
+block-size sweep (8, 16, 32) of the same lengths and paged vs contiguous
+placement of the same blocks. ``--per-config`` adds every page-shaped
+workload (the Llama-3-8B and Llama-2-70B layers, the prefix-sharing batch
+and the mixed batch with split sequences): decode calls timed cold, with
+p10/p50/p90, and the scatter and block copy of each step.
+
+    python bench.py [--steps K] [--warmup W] [--layers N] [--no-cpu-baseline] [--secondary]
+                    [--per-config]
 """
 
 import argparse
@@ -60,6 +71,224 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def stream_read_peak(dev, gib=4, reps=8):
+    """Best median streaming-read rate (GB/s) of the library's stream-read
+    kernel over a buffer much larger than L2 and the Infinity Cache."""
+    import torch
+
+    import paged_kv_cache_154_amd as pkv
+    buf = torch.empty(gib << 28, dtype=torch.float32, device=dev)
+    buf.fill_(1.0)
+    nbytes = buf.numel() * 4
+    best = 0.0
+    for grid in (2048, 4096, 8192, 16384):
+        sink = torch.empty(grid, dtype=torch.int32, device=dev)
+        pkv.stream_read(buf, sink, grid)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            pkv.stream_read(buf, sink, grid)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        rate = nbytes / (statistics.median(ts) * 1e-3) / 1e9
+        log(f"stream read, grid {grid}: {rate:.0f} GB/s")
+        best = max(best, rate)
+    del buf
+    return best
+
+
+def time_decode(pkv, wl, dev, layers=2, calls=20, P=0):
+    """Median decode-call time (us) of a workload: calls queued back to back
+    (as in the timed steps), rotating over layer copies of the pools."""
+    import torch
+    q = wl.query.to(dev)
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    sl = torch.from_numpy(wl.seq_lens).to(dev)
+    kc0, vc0 = wl.key_cache.to(dev), wl.value_cache.to(dev)
+    if wl.new_key is not None:        # fill the slot this step's token occupies
+        pkv.reshape_and_cache(wl.new_key.to(dev), wl.new_value.to(dev), kc0, vc0,
+                              torch.from_numpy(wl.slot_mapping).to(dev))
+    pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(layers - 1)]
+    out = torch.empty(wl.query.shape, dtype=wl.dtype, device=dev)
+    ws = pkv.workspace_for(q, kc0, wl.max_seq_len, P)
+    for i in range(4):
+        kc, vc = pools[i % layers]
+        pkv.paged_attn_decode(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    torch.cuda.synchronize()
+    for i in range(calls):
+        kc, vc = pools[i % layers]
+        ev[i][0].record()
+        pkv.paged_attn_decode(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    del pools
+    return statistics.median(a.elapsed_time(b) * 1e3 for a, b in ev)
+
+
+def secondary(pkv, W, base, dev):
+    """Block-size sweep and paged vs contiguous placement on the same lengths
+    (context from the pages: bs 16 best; paged placement within a few
+    percent of contiguous)."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+    lens = base.seq_lens.tolist()
+    out = {"block_size_sweep": {}, "placement": {}}
+    for bs in (8, 16, 32):
+        wl = W.custom(1542, seq_lens=lens, num_heads=32, num_kv_heads=8, head_dim=128,
+                      block_size=bs, dtype=torch.bfloat16)
+        t = time_decode(pkv, wl, dev)
+        out["block_size_sweep"][str(bs)] = {"decode_us": round(t, 1),
+                                            "kv_GBps": round(wl.kv_bytes() / t / 1e3, 1)}
+        log(f"block_size {bs}: {t:.1f} us")
+        del wl
+    # contiguous: relabel the blocks so each sequence's are consecutive
+    wl = base
+    order, seen = [], set()
+    for s_ in range(wl.num_seqs):
+        nb_ = (int(wl.seq_lens[s_]) + wl.block_size - 1) // wl.block_size
+        for b_ in wl.block_table[s_, :nb_]:
+            if int(b_) not in seen:
+                seen.add(int(b_))
+                order.append(int(b_))
+    order = np.array(order + [b_ for b_ in range(wl.num_blocks) if b_ not in seen])
+    newid = np.empty_like(order)
+    newid[order] = np.arange(order.size)
+    t_paged = time_decode(pkv, wl, dev)
+    perm = torch.from_numpy(order)
+    contig = dataclasses.replace(wl, key_cache=wl.key_cache[perm].contiguous(),
+                                 value_cache=wl.value_cache[perm].contiguous(),
+                                 block_table=newid[wl.block_table].astype(np.int32))
+    t_contig = time_decode(pkv, contig, dev)
+    out["placement"] = {"paged_us": round(t_paged, 1), "contiguous_us": round(t_contig, 1),
+                        "paged_over_contiguous": round(t_paged / t_contig, 4)}
+    log(f"placement: paged {t_paged:.1f} us, contiguous {t_contig:.1f} us")
+    return out
+
+
+def _events(n):
+    import torch
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n)]
+
+
+def _us(ev):
+    return [a.elapsed_time(b) * 1e3 for a, b in ev]
+
+
+def _pcts(xs):
+    q = statistics.quantiles(xs, n=10)
+    return round(q[0], 2), round(statistics.median(xs), 2), round(q[-1], 2)
+
+
+def layout_stats(wl):
+    """Slots the pool holds for the batch vs tokens it stores, and (when
+    blocks are shared) logical vs distinct blocks and bytes."""
+    import numpy as np
+    bs = wl.block_size
+    logical_blocks = int(sum((int(L) + bs - 1) // bs for L in wl.seq_lens))
+    slots = []
+    for s_, L in enumerate(wl.seq_lens.tolist()):
+        t = np.arange(L, dtype=np.int64)
+        slots.append(wl.block_table[s_, t // bs].astype(np.int64) * bs + t % bs)
+    uniq_slots = int(np.unique(np.concatenate(slots)).size) if slots else 0
+    return {
+        "logical_blocks": logical_blocks,
+        "distinct_blocks": int(wl.unique_blocks),
+        "slot_utilisation": round(uniq_slots / max(1, wl.unique_blocks * bs), 4),
+        "block_saving_from_sharing": round(1 - wl.unique_blocks / max(1, logical_blocks), 4),
+        "kv_bytes_distinct": uniq_slots * 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes,
+    }
+
+
+def per_config(pkv, W, dev, calls=200, warm=20):
+    """Every page-shaped workload (configs 2-5): each decode call timed cold
+    (a 1 GiB streaming read evicts L2 and the Infinity Cache before it,
+    outside the events; a read, because a write flush leaves dirty lines
+    whose write-back would be charged to the call), median and p10/p90, a
+    warm back-to-back mean, and the cache ops of the step (mean of
+    back-to-back calls: one event pair per call would dwarf a few-us kernel)."""
+    import torch
+    fbuf = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    fsink = torch.empty(8192, dtype=torch.int32, device=dev)
+
+    def flush():
+        pkv.stream_read(fbuf, fsink, 8192)
+
+    def mean_us(fn, n=50):
+        fn()
+        a, b = _events(1)[0]
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return round(a.elapsed_time(b) * 1e3 / n, 2)
+
+    res = {}
+    for c in (2, 3, 4, 5):
+        log(f"config {c}: generating")
+        wl = W.make(c)
+        q = wl.query.to(dev)
+        bt = torch.from_numpy(wl.block_table).to(dev)
+        sl = torch.from_numpy(wl.seq_lens).to(dev)
+        kc, vc = wl.key_cache.to(dev), wl.value_cache.to(dev)
+        out = torch.empty(wl.query.shape, dtype=wl.dtype, device=dev)
+        S, H, D = wl.query.shape
+        row = {"workload": wl.name, "num_seqs": S, "num_heads": H, "num_kv_heads": wl.num_kv_heads,
+               "head_dim": D, "block_size": wl.block_size, "tokens": wl.num_tokens,
+               "kv_bytes": wl.kv_bytes(), **layout_stats(wl)}
+        if wl.new_key is not None:
+            nk, nv = wl.new_key.to(dev), wl.new_value.to(dev)
+            slots = torch.from_numpy(wl.slot_mapping).to(dev)
+            t = mean_us(lambda: pkv.reshape_and_cache(nk, nv, kc, vc, slots))
+            nbytes = 4 * nk.numel() * nk.element_size()
+            row["reshape_and_cache"] = {"mean_us": t, "bytes": nbytes}
+        if wl.block_mapping is not None:
+            bm = torch.from_numpy(wl.block_mapping).to(dev)
+            t = mean_us(lambda: pkv.copy_blocks(kc, vc, bm))
+            nbytes = 4 * bm.shape[0] * kc[0].numel() * kc.element_size()
+            row["copy_blocks"] = {"mean_us": t, "bytes": nbytes, "pairs": int(bm.shape[0])}
+        row["decode"] = {}
+        for P in sorted({wl.partition_size, 0}):
+            ws = pkv.workspace_for(q, kc, wl.max_seq_len, P)
+            for _ in range(warm):
+                pkv.paged_attn_decode(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
+            ev = _events(calls)
+            for a, b in ev:
+                flush()
+                a.record()
+                pkv.paged_attn_decode(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
+                b.record()
+            w0, w1 = _events(1)[0]
+            w0.record()
+            for _ in range(warm):
+                pkv.paged_attn_decode(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
+            w1.record()
+            torch.cuda.synchronize()
+            p10, p50, p90 = _pcts(_us(ev))
+            gbs = wl.kv_bytes() / p50 / 1e3
+            part = pkv.paged_attn_partition_tokens(S, wl.num_kv_heads, wl.block_size,
+                                                   wl.max_seq_len, P)
+            row["decode"][f"partition_size={P}"] = {
+                "partition_tokens": part, "cold_us_p10_p50_p90": [p10, p50, p90],
+                "warm_mean_us": round(w0.elapsed_time(w1) * 1e3 / warm, 2),
+                "kv_GBps": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                "seqs_per_s": round(S / (p50 * 1e-6), 1)}
+            log(f"config {c} P={P} ({part} tokens): cold median {p50:.1f} us, {gbs:.0f} GB/s")
+        res[str(c)] = row
+        del wl, q, bt, sl, kc, vc, out
+        torch.cuda.empty_cache()
+    del fbuf
+    return res
+
+
 def cpu_baseline(wl, budget_s=20.0):
     """The CPU oracle on the same step (scatter + decode of every sequence),
     wall clock, median over repeats within about budget_s seconds."""
@@ -92,6 +321,12 @@ def main():
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream-peak", action="store_true",
+                    help="skip measuring the streaming-read rate")
+    ap.add_argument("--secondary", action="store_true",
+                    help="add the block-size sweep and the placement comparison")
+    ap.add_argument("--per-config", action="store_true",
+                    help="add cold-cache timings of every page-shaped workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (torch), 10 times: the "
                          "reference for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -164,6 +399,7 @@ def main():
     ms_step = t_start.elapsed_time(t_stop) / args.steps
     dec_ms = [a.elapsed_time(b) for a, b in ev]
     dec_avg = sum(dec_ms) / len(dec_ms)
+    dec_q = statistics.quantiles(dec_ms, n=10) if len(dec_ms) >= 2 else dec_ms * 9
     log(f"{args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f}), "
         f"decode call avg {dec_avg * 1e3:.1f} us, median {statistics.median(dec_ms) * 1e3:.1f} us")
 
@@ -194,6 +430,8 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seqs_per_s_per_layer": round(S / (ms_step * 1e-3), 1),
         "decode_us": round(dec_avg * 1e3, 2),
+        "decode_us_p10_p50_p90": [round(dec_q[0] * 1e3, 2), round(statistics.median(dec_ms) * 1e3, 2),
+                                  round(dec_q[-1] * 1e3, 2)],
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -205,6 +443,17 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not args.no_stream_peak:
+        log("measuring the streaming-read rate")
+        peak = stream_read_peak(dev)
+        res["measured_stream_read_GBps"] = round(peak, 1)
+        res["roofline"]["frac_of_measured_stream_read"] = round(achieved / peak, 4)
+    if args.secondary:
+        del layers
+        torch.cuda.empty_cache()
+        res["secondary"] = secondary(pkv, W, wl, dev)
+    if args.per_config:
+        res["per_config"] = per_config(pkv, W, dev)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the same step")
         res["cpu_baseline"] = cpu_baseline(wl)

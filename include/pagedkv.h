@@ -187,6 +187,20 @@ int pagedkv_check_decode_inputs(const int32_t* block_table,
                                 int max_blocks_per_seq, int max_seq_len,
                                 int32_t* counts, hipStream_t stream);
 
+/*
+ * pagedkv_stream_read - measurement aid, not part of the decode path: reads
+ * `bytes` (a multiple of 16) from device buffer `src` once with 16-byte loads
+ * per lane, 4 loads in flight per lane, `grid` workgroups of 256 threads in
+ * a grid-stride loop, and writes one XOR fold per workgroup to sink[0 ..
+ * grid) (device uint32, so the loads cannot be dropped). Timed on a buffer
+ * much larger than the caches it gives the streaming-read rate the device
+ * reaches, which the decode call's bandwidth is compared with (the pages
+ * call decode memory-bound: "LLM inference optimisation in practice",
+ * arithmetic-intensity section). bytes = 0 is a no-op; grid must be > 0.
+ */
+int pagedkv_stream_read(const void* src, size_t bytes, uint32_t* sink, int grid,
+                        hipStream_t stream);
+
 /* pagedkv_status_string - a static, NUL-terminated name for a status code. */
 const char* pagedkv_status_string(int status);
 

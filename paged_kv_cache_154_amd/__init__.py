@@ -158,3 +158,16 @@ def check_decode_inputs(block_table: torch.Tensor, seq_lens: torch.Tensor, block
     check(st, "pagedkv_check_decode_inputs")
     c = counts.cpu()
     return int(c[0]), int(c[1])
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, grid: int, stream=None) -> None:
+    """Read ``buf`` once with the streaming-read kernel (measurement aid; see
+    pagedkv_stream_read in include/pagedkv.h). ``sink`` is int32/uint32 with
+    at least ``grid`` elements."""
+    _require(buf.is_contiguous() and buf.numel() * buf.element_size() % 16 == 0,
+             "buffer must be contiguous, a multiple of 16 bytes")
+    _require(sink.numel() >= grid and sink.element_size() == 4, "sink needs grid 32-bit words")
+    st = lib().pagedkv_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                   int(grid), _stream(buf, stream))
+    check(st, "pagedkv_stream_read")
+

@@ -10,6 +10,7 @@
 
 #include "pagedkv.h"
 #include "pagedkv_internal.h"
+#include "stream_read.h"
 
 namespace {
 
@@ -217,6 +218,16 @@ int pagedkv_check_decode_inputs(const int32_t* block_table, const int32_t* seq_l
   const hipError_t e = pkv::launch_check_decode_inputs(block_table, seq_lens, num_seqs, block_size,
                                                        num_blocks, max_blocks_per_seq, max_seq_len,
                                                        counts, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int pagedkv_stream_read(const void* src, size_t bytes, uint32_t* sink, int grid,
+                        hipStream_t stream) {
+  if (grid < 0) return PKV_ERR_SHAPE;
+  if (bytes == 0) return PKV_OK;
+  if (!src || !sink) return PKV_ERR_NULL;
+  if (bytes % 16 != 0 || grid == 0) return PKV_ERR_SHAPE;
+  const hipError_t e = pkv::launch_stream_read(src, bytes, sink, grid, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

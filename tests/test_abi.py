@@ -110,6 +110,11 @@ def test_partition_and_workspace_sizing():
     (lambda L: L.copy_blocks(FAKE, FAKE, FAKE, 3, 10, 12, 8, 128, 2, None), UNSUP),
     (lambda L: L.pagedkv_check_decode_inputs(FAKE, FAKE, 4, 16, 10, 8, 128, None, None), NULL),
     (lambda L: L.pagedkv_check_decode_inputs(FAKE, FAKE, 4, 16, 10, 8, -1, FAKE, None), SHAPE),
+    (lambda L: L.pagedkv_stream_read(FAKE, 0, FAKE, 16, None), OK),          # nothing to read
+    (lambda L: L.pagedkv_stream_read(None, 1024, FAKE, 16, None), NULL),
+    (lambda L: L.pagedkv_stream_read(FAKE, 1000, FAKE, 16, None), SHAPE),   # not a multiple of 16
+    (lambda L: L.pagedkv_stream_read(FAKE, 1024, FAKE, 0, None), SHAPE),
+    (lambda L: L.pagedkv_stream_read(FAKE, 1024, FAKE, -2, None), SHAPE),
 ])
 def test_cache_op_host_checks(call, code):
     assert call(_lib.lib()) == code
