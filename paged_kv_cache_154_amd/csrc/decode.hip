@@ -9,7 +9,13 @@
 // How (an MI355X design, not the pages' kernel):
 //  * The unit of work is a 16-token key tile of one (sequence, KV head). A
 //    wave processes tiles one at a time: it issues all of the tile's K and V
-//    loads (16-byte chunks) before computing, then
+//    loads (16-byte chunks) before computing. Each load instruction reads
+//    whole rows (16 lanes cover one token's 256-byte row of the KV head), the
+//    shape in which HBM streams fastest, and the loads are non-temporal
+//    unless the blocks look shared (see decode_item): on MI355X that reads
+//    ~6.6 TB/s where 16 rows x 64 bytes per instruction, the layout the MFMA
+//    operand wants, reads ~5.7 (and worse when non-temporal). K is therefore
+//    reordered through a per-wave LDS tile into the operand layout. Then
 //      - Q.K^T on v_mfma_f32_16x16x32_{f16,bf16} (fp32 pools:
 //        v_mfma_f32_16x16x4_f32) with the key tile as the A operand (16
 //        tokens x 32 head-dim elements, straight from the pool) and the G
@@ -110,15 +116,27 @@ struct KV<BF16Tag> {
   }
 };
 
-template <int NW>
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// Loads that stream past the caches (true) or are cached as usual (false).
+template <bool NT> struct NTL;
+template <> struct NTL<true> {
+  template <class T> __device__ static inline T ld(const T* p) { return __builtin_nontemporal_load(p); }
+};
+template <> struct NTL<false> {
+  template <class T> __device__ static inline T ld(const T* p) { return *p; }
+};
+template <bool nt, int NW>
 __device__ inline void load_words(uint32_t (&w)[NW], const unsigned char* ptr) {
   if constexpr (NW == 2) {
-    const uint2 a = *reinterpret_cast<const uint2*>(ptr);
+    const u32x2* a2 = reinterpret_cast<const u32x2*>(ptr);
+    const u32x2 a = NTL<nt>::ld(a2);
     w[0] = a.x; w[1] = a.y;
   } else {
 #pragma unroll
     for (int c = 0; c < NW / 4; ++c) {
-      const uint4 a = *reinterpret_cast<const uint4*>(ptr + 16 * c);
+      const u32x4* a4 = reinterpret_cast<const u32x4*>(ptr + 16 * c);
+      const u32x4 a = NTL<nt>::ld(a4);
       w[4 * c + 0] = a.x; w[4 * c + 1] = a.y; w[4 * c + 2] = a.z; w[4 * c + 3] = a.w;
     }
   }
@@ -164,6 +182,12 @@ struct TileEngine {
   static constexpr int VPL = D / 16;      // V elements per lane per token
   static constexpr int VW = VPL * E / 4;  // 32-bit words per lane per token of V
   static_assert(RB % 64 == 0, "row must split into 4 lane groups of 16-byte chunks");
+  // Rows of >= 256 bytes load K like V (whole rows) and reorder it through
+  // LDS; 128-byte rows (head_dim 64, 16-bit) load it in the operand layout.
+  static constexpr bool kKLds = RB >= 256;
+  static constexpr int KCL = RB / 256;     // 16-byte chunks per lane per token (K rows whole)
+  static constexpr int KTS = RB + 16;      // LDS row stride of the K tile
+  static constexpr int KT_BYTES = kKLds ? 16 * KTS : 0;  // one wave's K tile
 
   int col;  // MFMA column: head within the group
   int grp;  // lane group 0..3
@@ -195,23 +219,53 @@ struct TileEngine {
   }
 
   // One tile of tokens cs .. cs+15 (cs a multiple of 16, cs <= t_last).
-  // row_off(t) is the byte offset of token t's row for this KV head (t <= t_last).
-  template <class RowOff>
+  // row_off(t) is the byte offset of token t's row for this KV head (t <= t_last);
+  // kt is the wave's LDS tile (KT_BYTES); nt selects non-temporal loads.
+  template <bool nt, class RowOff>
   __device__ void step(const unsigned char* kbase, const unsigned char* vbase, int cs, int t_last,
-                       uint32_t slot_bytes, float scale_log2, RowOff row_off) {
+                       uint32_t slot_bytes, float scale_log2, RowOff row_off, unsigned char* kt) {
     uint4 kr[NKL];
     uint32_t vr[4][VW];
-    const unsigned char* kp = kbase + row_off(min(cs + col, t_last)) + 16 * grp;
-#pragma unroll
-    for (int i = 0; i < NKL; ++i) kr[i] = *reinterpret_cast<const uint4*>(kp + 64 * i);
-    // V rows of tokens t4 .. t4+3: a 4-aligned group never crosses a block
+    // rows of tokens t4 .. t4+3: a 4-aligned group never crosses a block
     const int t4 = min(cs + 4 * grp, t_last);
-    const unsigned char* vp = vbase + row_off(t4) + col * (VPL * E);
+    const uint64_t off4 = row_off(t4);
     const uint32_t room = (uint32_t)(t_last - t4);
+    if constexpr (kKLds) {
+      // K rows whole: 16 lanes read a token's row (256 contiguous bytes per
+      // instruction and row), like V
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const unsigned char* kp = kbase + off4 + (uint32_t)((uint32_t)r < room ? r : room) * slot_bytes;
+#pragma unroll
+        for (int u = 0; u < KCL; ++u) {
+          const u32x4* a4 = reinterpret_cast<const u32x4*>(kp + 16 * (col + 16 * u));
+          const u32x4 a = NTL<nt>::ld(a4);
+          kr[r * KCL + u] = make_uint4(a.x, a.y, a.z, a.w);
+        }
+      }
+    } else {
+      const unsigned char* kp = kbase + row_off(min(cs + col, t_last)) + 16 * grp;
+#pragma unroll
+      for (int i = 0; i < NKL; ++i) kr[i] = *reinterpret_cast<const uint4*>(kp + 64 * i);
+    }
+    const unsigned char* vp = vbase + off4 + col * (VPL * E);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      load_words<VW>(vr[r], vp + (uint32_t)((uint32_t)r < room ? r : room) * slot_bytes);
+      load_words<nt, VW>(vr[r], vp + (uint32_t)((uint32_t)r < room ? r : room) * slot_bytes);
     __builtin_amdgcn_sched_barrier(0);  // every load of the tile in flight first
+    if constexpr (kKLds) {
+      // through the wave's LDS tile (rows padded by 16 bytes: both the row
+      // writes and the column reads below hit every bank once) into the
+      // MFMA layout: lane (col, grp) takes chunk 4i + grp of token cs + col
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int u = 0; u < KCL; ++u)
+          *reinterpret_cast<uint4*>(kt + (4 * grp + r) * KTS + 16 * (col + 16 * u)) = kr[r * KCL + u];
+#pragma unroll
+      for (int i = 0; i < NKL; ++i)
+        kr[i] = *reinterpret_cast<const uint4*>(kt + col * KTS + 16 * (4 * i + grp));
+    }
 
     // scores S[token][head]: lane holds tokens cs + 4*grp + r of head col
     f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -507,16 +561,17 @@ __device__ inline void install_epoch(unsigned long long* word, uint32_t epoch) {
   }
 }
 
-// LDS of the partition kernel: the partition's block-table slice, reused for
-// the waves' O rows (and at the start for the plan's scan); then the waves'
-// (m, l); then the next item; then the plan.
-__host__ __device__ inline int lds_main_bytes(int D, int G, int span, int BS) {
+// LDS of the partition kernel: the partition's block-table slice and the
+// waves' K tiles, reused for the waves' O rows (and at the start for the
+// plan's scan); then the waves' (m, l); then the next item; then the plan.
+__host__ __device__ inline int bt_lds_bytes(int span, int BS) { return ((span / BS + 1) * 4 + 15) & ~15; }
+__host__ __device__ inline int lds_main_bytes(int D, int G, int span, int BS, int kt_bytes) {
   const int o_bytes = kWaves * G * o_stride(D) * 4;
-  const int bt_bytes = (span / BS + 1) * 4;
-  return ((o_bytes > bt_bytes ? o_bytes : bt_bytes) + 15) & ~15;
+  const int tile_bytes = bt_lds_bytes(span, BS) + kWaves * kt_bytes;
+  return ((o_bytes > tile_bytes ? o_bytes : tile_bytes) + 15) & ~15;
 }
-__host__ __device__ inline int lds_total_bytes(int D, int G, int span, int BS, int S) {
-  return lds_main_bytes(D, G, span, BS) + 2 * kWaves * 16 * 4 + 16 + plan_bytes(S);
+__host__ __device__ inline int lds_total_bytes(int D, int G, int span, int BS, int kt_bytes, int S) {
+  return lds_main_bytes(D, G, span, BS, kt_bytes) + 2 * kWaves * 16 * 4 + 16 + plan_bytes(S);
 }
 
 // One work item: KV head kvh of partition `part` of sequence `seq`, by the
@@ -562,12 +617,26 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
     }
   }
 
+  // Blocks shared with the neighbouring sequences of the batch (samples
+  // forked from one prompt sit next to each other) are read with caching
+  // loads so that the neighbours find them in L2; everything else streams
+  // with non-temporal loads. Only the speed depends on this guess.
+  bool shared = false;
+  {
+    const int32_t* mine = p.block_table + (size_t)seq * p.max_blocks + lb0;
+    const int b0 = mine[0];
+    if (seq > 0) shared |= mine[-p.max_blocks] == b0;
+    if (seq + 1 < p.num_seqs) shared |= mine[p.max_blocks] == b0;
+  }
+
   Eng eng;
   eng.init(lane);
   eng.load_q(static_cast<const unsigned char*>(p.q) + ((size_t)seq * p.num_heads + head0) * RB, G);
   eng.reset();
   __syncthreads();
 
+  unsigned char* kt = smem + bt_lds_bytes(p.partition < p.max_seq_len ? p.partition : p.max_seq_len, BS) +
+                     wave * Eng::KT_BYTES;
   const uint32_t slot_bytes = (uint32_t)p.num_kv_heads * RB;  // bytes between slots
   const unsigned char* kbase = static_cast<const unsigned char*>(p.k) + (size_t)kvh * RB;
   const unsigned char* vbase = static_cast<const unsigned char*>(p.v) + (size_t)kvh * RB;
@@ -578,8 +647,13 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
     const uint32_t phys = (uint32_t)s_bt[u / BS - (uint32_t)lb0];
     return (uint64_t)(phys * BS + (u % BS)) * slot_bytes;
   };
-  for (int cs = t_begin + wave * kTile; cs < t_end; cs += kWaves * kTile)
-    eng.step(kbase, vbase, cs, t_end - 1, slot_bytes, p.scale_log2, row_off);
+  if (shared) {
+    for (int cs = t_begin + wave * kTile; cs < t_end; cs += kWaves * kTile)
+      eng.template step<false>(kbase, vbase, cs, t_end - 1, slot_bytes, p.scale_log2, row_off, kt);
+  } else {
+    for (int cs = t_begin + wave * kTile; cs < t_end; cs += kWaves * kTile)
+      eng.template step<true>(kbase, vbase, cs, t_end - 1, slot_bytes, p.scale_log2, row_off, kt);
+  }
 
   // ---- merge the waves ---------------------------------------------------
   const float lsum = eng.total_sum();
@@ -645,7 +719,7 @@ void decode_partition_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int wave = uniform(threadIdx.x >> 6);
   const int span = p.partition < p.max_seq_len ? p.partition : p.max_seq_len;
-  const int lds_main = lds_main_bytes(D, p.group, span, BS);
+  const int lds_main = lds_main_bytes(D, p.group, span, BS, TileEngine<Tag, D, BS>::KT_BYTES);
   // Two slots for the next item, used alternately: an item may pass no
   // barrier (a zero-length sequence), and a slot is rewritten only after the
   // barrier that follows every wave's read of it.
@@ -788,7 +862,7 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   // so that two workgroups fit per CU, when the rest of it leaves room.
   int chunk = kMaxSeqsPerLaunch;
   {
-    const int fixed = lds_total_bytes(D, p.group, span, BS, 0);
+    const int fixed = lds_total_bytes(D, p.group, span, BS, TileEngine<Tag, D, BS>::KT_BYTES, 0);
     const int room = (kLdsPerWorkgroup - fixed - 32) / 10;
     if (room < chunk) chunk = room > 256 ? room : 256;
   }
@@ -800,7 +874,7 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
     c.out = static_cast<unsigned char*>(p.out) + (size_t)s0 * q_row * out_elem;
     c.block_table = p.block_table + (size_t)s0 * p.max_blocks;
     c.seq_lens = p.seq_lens + s0;
-    const size_t lds = (size_t)lds_total_bytes(D, c.group, span, BS, c.num_seqs);
+    const size_t lds = (size_t)lds_total_bytes(D, c.group, span, BS, TileEngine<Tag, D, BS>::KT_BYTES, c.num_seqs);
     const int64_t max_items = (int64_t)c.num_seqs * c.num_kv_heads * c.num_partitions;
     int64_t grid = resident_workgroups(kfn, lds);
     if (grid > max_items) grid = max_items;
