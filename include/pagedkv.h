@@ -89,15 +89,17 @@ enum pkv_status {
  *                of block_size; 0 lets the library choose (see
  *                paged_attn_partition_tokens). A sequence longer than one
  *                partition is split; each partition's (max, sum, weighted V)
- *                is written to the workspace and a second kernel merges them.
+ *                is written to the workspace, and the last partition of a
+ *                (sequence, KV head) to finish merges them (one kernel).
  *                When one partition covers max_seq_len it may hold at most
  *                16384 tokens; a splitting partition likewise.
  *   workspace    device scratch of at least paged_attn_workspace_size(...)
  *                bytes for the same arguments (always needed: its first 256
- *                bytes hold the decode kernel's item counter, which the call
- *                resets on the stream itself; the rest holds the split-K
- *                partials). Its contents need no initialisation and are
- *                garbage after. Calls that may run at the same time need
+ *                bytes hold the decode kernel's item counter; the rest holds
+ *                the split-K partials and one arrival word per (sequence, KV
+ *                head); the counter and the arrival words carry a per-call
+ *                tag, so stale contents are recognised). Its contents need
+ *                no initialisation and are garbage after. Calls that may run at the same time need
  *                separate workspaces; calls in order on one stream can share
  *                one.
  * Supported: head_dim 64 or 128; block_size 8, 16 or 32; 1 <= G <= 16;
@@ -127,9 +129,10 @@ int paged_attn_partition_tokens(int num_seqs, int num_kv_heads, int block_size,
  * paged_attn_workspace_size - bytes of workspace paged_attn_decode needs for
  * these arguments: a 256-byte header and, when sequences are split, fp32
  * (max, sum) pairs and head_dim weighted-V partial sums per (sequence, head,
- * partition) for min(num_seqs, 2048) sequences (larger batches run as
- * several launches of at most 2048 sequences that reuse them). 0 when the
- * arguments are invalid or num_seqs is 0.
+ * partition) and a 64-bit arrival word per (sequence, KV head), for
+ * min(num_seqs, 2048) sequences (larger batches run as several launches of
+ * at most 2048 sequences that reuse them). 0 when the arguments are invalid
+ * or num_seqs is 0.
  */
 size_t paged_attn_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
                                  int head_dim, int block_size, int max_seq_len,

@@ -79,18 +79,20 @@ Cutting cutting_for(int max_seq_len, int block_size, int P) {
 
 // Workspace layout: a 256-byte header (the partition kernel's item counter,
 // tagged with the launch's epoch), then, when sequences are split, fp32 O partials
-// [S', H, NP, D] and (m, l) pairs [S', H, NP, 2] for S' = min(S, the
+// [S', H, NP, D], (m, l) pairs [S', H, NP, 2] and one 64-bit arrival word per
+// (sequence, KV head) [S', Hkv] (also epoch-tagged), for S' = min(S, the
 // sequences of one launch); launches run in order and reuse them.
 constexpr size_t kHeaderBytes = 256;
 
-size_t split_workspace_bytes(int num_seqs, int num_heads, int head_dim, int np) {
+size_t split_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int np) {
   if (np <= 1) return 0;
   const int s = num_seqs < pkv::kMaxSeqsPerLaunch ? num_seqs : pkv::kMaxSeqsPerLaunch;
-  return (size_t)s * num_heads * np * (size_t)(head_dim + 2) * sizeof(float);
+  return (size_t)s * num_heads * np * (size_t)(head_dim + 2) * sizeof(float) +
+         (size_t)s * num_kv_heads * sizeof(unsigned long long);
 }
 
-size_t workspace_bytes_for(int num_seqs, int num_heads, int head_dim, int np) {
-  return kHeaderBytes + split_workspace_bytes(num_seqs, num_heads, head_dim, np);
+size_t workspace_bytes_for(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int np) {
+  return kHeaderBytes + split_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, np);
 }
 
 }  // namespace
@@ -110,7 +112,8 @@ size_t paged_attn_workspace_size(int num_seqs, int num_heads, int num_kv_heads, 
   if (!supported_head_dim(head_dim)) return 0;
   const int P = resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
   if (P < 0) return 0;
-  return workspace_bytes_for(num_seqs, num_heads, head_dim, cutting_for(max_seq_len, block_size, P).np);
+  return workspace_bytes_for(num_seqs, num_heads, num_kv_heads, head_dim,
+                             cutting_for(max_seq_len, block_size, P).np);
 }
 
 int paged_attn_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -141,7 +144,7 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
   // the grid) stay in int32
   const int s_launch = num_seqs < pkv::kMaxSeqsPerLaunch ? num_seqs : pkv::kMaxSeqsPerLaunch;
   if ((int64_t)s_launch * num_kv_heads * np > (int64_t)INT32_MAX - (1 << 24)) return PKV_ERR_SHAPE;
-  const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, np);
+  const size_t need = workspace_bytes_for(num_seqs, num_heads, num_kv_heads, head_dim, np);
   if (workspace == nullptr || workspace_bytes < need) return PKV_ERR_WORKSPACE;
 
   pkv::DecodeParams p{};
@@ -157,6 +160,7 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
     const int s = num_seqs < pkv::kMaxSeqsPerLaunch ? num_seqs : pkv::kMaxSeqsPerLaunch;
     p.ws_o = reinterpret_cast<float*>(ws + kHeaderBytes);
     p.ws_ml = p.ws_o + (size_t)s * num_heads * np * head_dim;
+    p.arrive = reinterpret_cast<unsigned long long*>(p.ws_ml + (size_t)s * num_heads * np * 2);
   }
   p.num_seqs = num_seqs;
   p.num_heads = num_heads;

@@ -39,7 +39,8 @@
 //    principle, section 2.2). Its 8 waves take the item's tiles round-robin
 //    and merge their (max, sum, O) through LDS. A sequence in one partition
 //    is written directly; otherwise each partition writes (max, sum, O) to
-//    the workspace and decode_reduce_kernel merges them.
+//    the workspace and the last partition of the (sequence, KV head) to
+//    finish merges them all and writes the output (see decode_item).
 //  * Items are dealt to workgroups in static rounds that keep each KV head on
 //    one XCD, and (unless the batch is of near-uniform length) all items
 //    after the first round are taken from an atomic counter, which evens out
@@ -326,8 +327,8 @@ __host__ __device__ inline int o_stride(int D) { return D + 4; }
 // multiple of 16): n = ceil(L / P) partitions; partition 0 is the short one,
 // [0, r) with r = roundup16(L) - (n-1) P in [16, P]; partitions 1 .. n-1
 // follow, each [r + (j-1) P, r + j P) (the last one ends at L). A sequence in
-// one partition is written out directly; the others are merged by
-// decode_reduce_kernel. The short partitions 0 are scheduled last.
+// one partition is written out directly; the others are merged by whichever
+// of their partitions finishes last. The short partitions 0 are scheduled last.
 struct Cut {
   int n, r;
 };
@@ -523,11 +524,11 @@ constexpr int kLdsPerWorkgroup = 80 * 1024;
 // initialisation) carries another epoch; the first workgroup to meet it
 // installs (epoch, 1) with a compare-and-swap and takes ticket 0, and every
 // later take sees the launch's epoch. Each failed compare-and-swap means that
-// another workgroup changed the word, so the loop ends within a few rounds;
-// should it not within kTicketTries, the workgroup returns -1 and takes its
-// counter items statically instead (items taken twice are computed twice
-// with identical results, so the output never depends on the header).
-constexpr int kTicketTries = 64;
+// another workgroup changed the word in between, so the loop ends within a
+// few rounds; the bound kTicketTries only keeps it finite. A workgroup that
+// gets -1 stops taking items (an item must never be taken twice: each
+// partition of a split sequence arrives once at its merge word).
+constexpr int kTicketTries = 1 << 20;
 
 __device__ inline int take_ticket(unsigned long long* word, uint32_t epoch) {
   const unsigned long long tag = (unsigned long long)epoch << 32;
@@ -542,6 +543,25 @@ __device__ inline int take_ticket(unsigned long long* word, uint32_t epoch) {
     } else {
       old = seen - 1;  // compare against what is there now
     }
+  }
+  return -1;
+}
+
+// Arrival of one partition at its (sequence, KV head) word, (epoch << 32) |
+// partitions done in this launch; returns how many arrived before it. A word
+// of another epoch (an earlier launch, or any contents) is replaced by
+// (epoch, 1). Every failed compare-and-swap means that another partition of
+// the same word arrived, so the loop ends within nparts rounds; -1 only if
+// calls that share the workspace overlap, which the API excludes.
+__device__ inline int arrive(unsigned long long* word, uint32_t epoch, int nparts) {
+  const unsigned long long tag = (unsigned long long)epoch << 32;
+  unsigned long long cur = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll 1
+  for (int i = 0; i < nparts + 8; ++i) {
+    const unsigned long long next = ((cur >> 32) == epoch) ? cur + 1 : (tag | 1ull);
+    const unsigned long long seen = atomicCAS(word, cur, next);
+    if (seen == cur) return (int)(uint32_t)next - 1;
+    cur = seen;
   }
   return -1;
 }
@@ -577,7 +597,9 @@ __host__ __device__ inline int lds_total_bytes(int D, int G, int span, int BS, i
 // One work item: KV head kvh of partition `part` of sequence `seq`, by the
 // whole workgroup. Waves take its 16-token tiles round-robin and merge
 // (m, l, O) through LDS; a sequence in one partition is normalised and
-// written to out, the others write partials to the workspace. With `draw`,
+// written to out. A partition of a split sequence writes its (m, l, O) to
+// the workspace and arrives at the (sequence, KV head) word; the last to
+// arrive merges every partition's partials and writes out. With `draw`,
 // thread 0 takes a ticket from the counter for the workgroup's next item.
 template <class Tag, int D, int BS>
 __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char* smem, int lds_main,
@@ -697,22 +719,54 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
     if (nparts <= 1) {
       store_out<Tag>(p, row * D + d, num / den);
     } else {
+      // agent-scope stores: written through to where every XCD reads them
       const size_t pi = row * p.num_partitions + part;
-      p.ws_o[pi * D + d] = num;
+      __hip_atomic_store(&p.ws_o[pi * D + d], num, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (d == 0) {
-        p.ws_ml[2 * pi] = M;
-        p.ws_ml[2 * pi + 1] = den;
+        __hip_atomic_store(&p.ws_ml[2 * pi], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.ws_ml[2 * pi + 1], den, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
+  }
+  if (nparts <= 1) return;
+
+  // ---- the last partition of (seq, kvh) to finish merges them all ---------
+  // Every thread's partial stores have completed (agent scope) before the
+  // barrier, the arrival then orders them before the merging workgroup's
+  // loads, and those are agent-scope too: no cache-wide release or acquire
+  // (L2 write-back or invalidate) is needed. The merge combines the
+  // partitions in index order: M = max m_q, then sums of 2^(m_q - M) l_q and
+  // 2^(m_q - M) O_q.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int* s_last = reinterpret_cast<int*>(smem + lds_main + 2 * kWaves * 16 * 4) + 2;
+  if (tid == 0) *s_last = arrive(p.arrive + (size_t)seq * p.num_kv_heads + kvh, p.epoch, nparts) == nparts - 1;
+  __syncthreads();
+  if (!*s_last) return;
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int h = idx / D;
+    const int d = idx - h * D;
+    const size_t row = (size_t)seq * p.num_heads + head0 + h;
+    const float* ml = p.ws_ml + 2 * row * p.num_partitions;
+    const float* o = p.ws_o + row * p.num_partitions * D + d;
+    float M = -INFINITY;
+    for (int q = 0; q < nparts; ++q)
+      M = fmaxf(M, __hip_atomic_load(&ml[2 * q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    float den = 0.0f, num = 0.0f;
+    for (int q = 0; q < nparts; ++q) {
+      const float wq = fast_exp2(__hip_atomic_load(&ml[2 * q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M);
+      den += wq * __hip_atomic_load(&ml[2 * q + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      num += wq * __hip_atomic_load(&o[(size_t)q * D], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    store_out<Tag>(p, row * D + d, num / den);
   }
 }
 
 // Persistent: a grid of as many workgroups as fit on the GPU at once (a
 // multiple of 8), each working through its items of the schedule above. A
 // workgroup whose next item is a counter one draws a ticket while it merges
-// its current item; every ticket advances the counter, and a workgroup
-// without ticket steps through its static share of the counter items, so
-// every workgroup ends.
+// its current item; every ticket advances the counter, so every workgroup
+// ends.
 template <class Tag, int D, int BS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEU<Tag, D>::value)))
 void decode_partition_kernel(DecodeParams p) {
@@ -722,7 +776,8 @@ void decode_partition_kernel(DecodeParams p) {
   const int lds_main = lds_main_bytes(D, p.group, span, BS, TileEngine<Tag, D, BS>::KT_BYTES);
   // Two slots for the next item, used alternately: an item may pass no
   // barrier (a zero-length sequence), and a slot is rewritten only after the
-  // barrier that follows every wave's read of it.
+  // barrier that follows every wave's read of it. The third int is the
+  // merge flag of decode_item, the fourth is free.
   int* s_next = reinterpret_cast<int*>(smem + lds_main + 2 * kWaves * 16 * 4);
   if (blockIdx.x == 0 && threadIdx.x == 0) install_epoch(p.work, p.epoch);
   Plan pl = plan_at(reinterpret_cast<unsigned char*>(s_next + 4), p.num_seqs);
@@ -734,8 +789,7 @@ void decode_partition_kernel(DecodeParams p) {
   const int b = (int)blockIdx.x;
 
   int parity = 0;
-  int round = 0;          // static round of the current item
-  bool fallback = false;  // thread 0: taking counter items statically
+  int round = 0;  // static round of the current item
   for (int w = b; (unsigned)w < (unsigned)total; parity ^= 1) {
     const int e = w / p.num_kv_heads;
     const int kvh = w - e * p.num_kv_heads;
@@ -752,74 +806,12 @@ void decode_partition_kernel(DecodeParams p) {
     asm volatile("" : "+v"(tid));
     decode_item<Tag, D, BS>(p, smem, lds_main, seq, uniform(pl.len[seq]), kvh, part, tid, wave, draw, ticket);
     if (threadIdx.x == 0) {
-      int64_t nx;
-      if (!draw) {
-        nx = nxt_static;
-      } else if (ticket >= 0 && !fallback) {
-        nx = (int64_t)ws + ticket;
-      } else {  // no ticket: the counter items ws + b, ws + b + grid, ...
-        nx = fallback ? (int64_t)w + grid : (int64_t)ws + b;
-        fallback = true;
-      }
+      const int64_t nx = !draw ? (int64_t)nxt_static : (ticket >= 0 ? (int64_t)ws + ticket : (int64_t)total);
       s_next[parity] = (nx >= 0 && nx < total) ? (int)nx : total;
     }
     __syncthreads();
     w = uniform(s_next[parity]);
   }
-}
-
-// One wave per (sequence, query head) of a split sequence, 4 waves per
-// workgroup. Lane q loads (m_q, l_q) of partition q and the partial O loads
-// do not wait for the weights, so the merge costs about one memory round
-// trip; the weights 2^(m_q - M) are broadcast from their lanes.
-template <class Tag, int D>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams p) {
-  constexpr int DPL = D / 64;  // output elements per lane
-  const int lane = threadIdx.x & 63;
-  const size_t rowid = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // seq * H + head
-  if (rowid >= (size_t)p.num_seqs * p.num_heads) return;
-  const int seq = (int)(rowid / p.num_heads);
-  const int L = clamp_len(p.seq_lens[seq], p.max_seq_len);
-  if (L == 0) return;  // written by the partition kernel
-  const int nparts = cut_of(L, p.partition).n;
-  if (nparts <= 1) return;  // written by the partition kernel
-  const int NP = p.num_partitions;
-  const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + rowid * NP;
-  const float* o = p.ws_o + rowid * NP * D;
-
-  float num[DPL];
-#pragma unroll
-  for (int k = 0; k < DPL; ++k) num[k] = 0.0f;
-  float M = -INFINITY, den = 0.0f;
-  // partitions in chunks of 64: lane q of the chunk holds partition base + q
-  for (int base = 0; base < nparts; base += 64) {
-    const int q = base + lane;
-    const float2 mlq = q < nparts ? ml[q] : make_float2(-INFINITY, 0.0f);
-    float cm = mlq.x;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
-    const float M_new = fmaxf(M, cm);
-    const float alpha = fast_exp2(M - M_new);  // rescale of the earlier chunks
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) num[k] *= alpha;
-    den *= alpha;
-    M = M_new;
-    const float w = q < nparts ? fast_exp2(mlq.x - M) : 0.0f;
-    float dw = w * mlq.y;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) dw += __shfl_xor(dw, off);
-    den += dw;
-    const int n = min(64, nparts - base);
-#pragma unroll 8
-    for (int j = 0; j < n; ++j) {
-      const float wj = __shfl(w, j);
-      const float* oj = o + (size_t)(base + j) * D + lane;
-#pragma unroll
-      for (int k = 0; k < DPL; ++k) num[k] += wj * oj[64 * k];
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < DPL; ++k) store_out<Tag>(p, rowid * D + lane + 64 * k, num[k] / den);
 }
 
 // ============================================================================
@@ -857,7 +849,7 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   const size_t q_row = (size_t)p.num_heads * D;
   const size_t out_elem = p.out_f32 ? 4 : (size_t)Tag::kBytes;
   // Launches of at most `chunk` sequences each, in order on the stream; they
-  // share the workspace (header, partials). The chunk keeps the LDS of a
+  // share the workspace (header, partials, arrival words). The chunk keeps the LDS of a
   // workgroup (its plan grows with the sequences) within half a CU's 160 KiB,
   // so that two workgroups fit per CU, when the rest of it leaves room.
   int chunk = kMaxSeqsPerLaunch;
@@ -880,14 +872,8 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
     if (grid > max_items) grid = max_items;
     if (grid >= 8) grid = grid / 8 * 8;  // whole rounds over the 8 XCDs
     decode_partition_kernel<Tag, D, BS><<<dim3((unsigned)grid), dim3(kThreads), lds, stream>>>(c);
-    hipError_t e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (c.num_partitions > 1) {
-      const size_t rows = (size_t)c.num_seqs * c.num_heads;
-      decode_reduce_kernel<Tag, D><<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream>>>(c);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
   }
   return hipSuccess;
 }

@@ -19,6 +19,7 @@ struct DecodeParams {
   uint32_t epoch;            // set per launch: nonzero, distinct within the process
   float* ws_o;    // [S, H, NP, D] weighted-V partial sums (split only)
   float* ws_ml;   // [S, H, NP, 2] (running max in log2 units, sum of weights)
+  unsigned long long* arrive;  // [S, Hkv] (epoch << 32) | partitions done (split only)
   int num_seqs;
   int num_heads;
   int num_kv_heads;

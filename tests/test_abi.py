@@ -84,17 +84,19 @@ def test_partition_and_workspace_sizing():
     assert L.paged_attn_partition_tokens(384, 8, 16, 2560, 0) == 2560    # many, short: no split
     assert L.paged_attn_partition_tokens(64, 8, 8, 10000, 512) == 512
     assert L.paged_attn_partition_tokens(64, 8, 32, 100, 48) == SHAPE    # not a multiple of 32
-    # a 256-byte header (the item counters) and, when sequences are split, fp32
-    # (max, sum) + head_dim partial sums per (seq, head, partition) for at most
-    # 2048 sequences (larger batches run as several launches that reuse them)
+    # a 256-byte header (the item counter) and, when sequences are split, fp32
+    # (max, sum) + head_dim partial sums per (seq, head, partition) and one
+    # 8-byte arrival word per (seq, KV head), for at most 2048 sequences
+    # (larger batches run as several launches that reuse them)
     hdr = 256
     assert L.paged_attn_workspace_size(64, 32, 8, 128, 16, 512, 512) == hdr   # no split
     n = L.paged_attn_workspace_size(256, 32, 8, 128, 8, 10000, 512)
-    assert n == hdr + 256 * 32 * 20 * (128 + 2) * 4
-    assert L.paged_attn_workspace_size(4, 4, 4, 64, 16, 50, 16) == hdr + 4 * 4 * 4 * 66 * 4
+    assert n == hdr + 256 * 32 * 20 * (128 + 2) * 4 + 256 * 8 * 8
+    assert L.paged_attn_workspace_size(4, 4, 4, 64, 16, 50, 16) == hdr + 4 * 4 * 4 * 66 * 4 + 4 * 4 * 8
     assert L.paged_attn_workspace_size(384, 32, 8, 128, 16, 2560, 0) == hdr
-    assert L.paged_attn_workspace_size(64, 32, 8, 128, 16, 4039, 0) == hdr + 64 * 32 * 4 * 130 * 4
-    assert L.paged_attn_workspace_size(5000, 8, 8, 64, 16, 4096, 1024) == hdr + 2048 * 8 * 4 * 66 * 4
+    assert L.paged_attn_workspace_size(64, 32, 8, 128, 16, 4039, 0) == hdr + 64 * 32 * 4 * 130 * 4 + 64 * 8 * 8
+    assert (L.paged_attn_workspace_size(5000, 8, 8, 64, 16, 4096, 1024)
+            == hdr + 2048 * 8 * 4 * 66 * 4 + 2048 * 8 * 8)
     assert L.paged_attn_workspace_size(0, 32, 8, 128, 16, 4039, 0) == 0
 
 

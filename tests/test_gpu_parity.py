@@ -165,8 +165,8 @@ def test_max_seq_len_above_actual_lengths(P):
 
 @pytest.mark.parametrize("L,G,P", [(65536, 16, 64), (65536, 4, 64), (8192, 4, 16)])
 def test_many_partitions_of_one_long_sequence(L, G, P):
-    """One sequence split into hundreds or thousands of partitions (more
-    (max, sum) pairs than the merge kernel stages in LDS for L=65536)."""
+    """One sequence split into hundreds or thousands of partitions: hundreds
+    of arrivals at one (sequence, KV head) word, and a merge over them all."""
     wl = W.custom(16, seq_lens=[L], num_heads=G, num_kv_heads=1, head_dim=64,
                   block_size=16, dtype=torch.bfloat16)
     ref, _, _ = oracle_step(wl)
