@@ -547,23 +547,19 @@ __device__ inline int take_ticket(unsigned long long* word, uint32_t epoch) {
   return -1;
 }
 
-// Arrival of one partition at its (sequence, KV head) word, (epoch << 32) |
-// partitions done in this launch; returns how many arrived before it. A word
-// of another epoch (an earlier launch, or any contents) is replaced by
-// (epoch, 1). Every failed compare-and-swap means that another partition of
-// the same word arrived, so the loop ends within nparts rounds; -1 only if
-// calls that share the workspace overlap, which the API excludes.
-__device__ inline int arrive(unsigned long long* word, uint32_t epoch, int nparts) {
-  const unsigned long long tag = (unsigned long long)epoch << 32;
-  unsigned long long cur = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll 1
-  for (int i = 0; i < nparts + 8; ++i) {
-    const unsigned long long next = ((cur >> 32) == epoch) ? cur + 1 : (tag | 1ull);
-    const unsigned long long seen = atomicCAS(word, cur, next);
-    if (seen == cur) return (int)(uint32_t)next - 1;
-    cur = seen;
-  }
-  return -1;
+// Arrival words: one per (sequence, KV head) of a split sequence,
+// (epoch << 32) | partitions done in this launch. Every workgroup tags a
+// slice of them with the launch's epoch as it starts (an atomic max:
+// (epoch, 0) replaces a word of an earlier launch, whose epoch is smaller,
+// and leaves one that already counts arrivals of this launch), so that an
+// arrival is a single atomic add (take_ticket); a word that still carries
+// another epoch (contents that were never a word of this process) is
+// repaired by take_ticket's compare-and-swap.
+__device__ inline void tag_arrival_words(const DecodeParams& p) {
+  const unsigned long long tag = (unsigned long long)p.epoch << 32;
+  const size_t n = (size_t)p.num_seqs * p.num_kv_heads;
+  for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kThreads)
+    atomicMax(p.arrive + i, tag);
 }
 
 // Puts the counter at (epoch, 0) unless it already carries the epoch: done
@@ -732,7 +728,8 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
 
   // ---- the last partition of (seq, kvh) to finish merges them all ---------
   // Every thread's partial stores have completed (agent scope) before the
-  // barrier, the arrival then orders them before the merging workgroup's
+  // barrier, the arrival (an atomic add on the (seq, kvh) word, see
+  // tag_arrival_words) then orders them before the merging workgroup's
   // loads, and those are agent-scope too: no cache-wide release or acquire
   // (L2 write-back or invalidate) is needed. The merge combines the
   // partitions in index order: M = max m_q, then sums of 2^(m_q - M) l_q and
@@ -740,7 +737,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int* s_last = reinterpret_cast<int*>(smem + lds_main + 2 * kWaves * 16 * 4) + 2;
-  if (tid == 0) *s_last = arrive(p.arrive + (size_t)seq * p.num_kv_heads + kvh, p.epoch, nparts) == nparts - 1;
+  if (tid == 0) *s_last = take_ticket(p.arrive + (size_t)seq * p.num_kv_heads + kvh, p.epoch) == nparts - 1;
   __syncthreads();
   if (!*s_last) return;
   for (int idx = tid; idx < G * D; idx += kThreads) {
@@ -780,6 +777,7 @@ void decode_partition_kernel(DecodeParams p) {
   // merge flag of decode_item, the fourth is free.
   int* s_next = reinterpret_cast<int*>(smem + lds_main + 2 * kWaves * 16 * 4);
   if (blockIdx.x == 0 && threadIdx.x == 0) install_epoch(p.work, p.epoch);
+  if (p.num_partitions > 1) tag_arrival_words(p);
   Plan pl = plan_at(reinterpret_cast<unsigned char*>(s_next + 4), p.num_seqs);
   build_plan(p, pl, reinterpret_cast<uint64_t*>(smem));
   const int entries = pl.n_full + pl.S;
