@@ -530,22 +530,36 @@ constexpr int kLdsPerWorkgroup = 80 * 1024;
 // partition of a split sequence arrives once at its merge word).
 constexpr int kTicketTries = 1 << 20;
 
-__device__ inline int take_ticket(unsigned long long* word, uint32_t epoch) {
+// take_ticket for a caller whose atomic add on the word returned `old`: the
+// ticket if `old` carries the epoch. Otherwise that add landed on a word of
+// another epoch, so the caller installs (epoch, 1) in place of what the word
+// holds now and is ticket 0, or, if another caller installed the epoch
+// first, takes a fresh ticket. Every failed compare-and-swap is another
+// caller's change of the word.
+__device__ inline int take_ticket_after(unsigned long long* word, uint32_t epoch, unsigned long long old) {
   const unsigned long long tag = (unsigned long long)epoch << 32;
-  unsigned long long old = atomicAdd(word, 1ull);
+  int tries = 0;
 #pragma unroll 1
-  for (int i = 0; i < kTicketTries; ++i) {
-    if ((old >> 32) == epoch) return (int)(uint32_t)old;
-    const unsigned long long seen = atomicCAS(word, old + 1, tag | 1ull);
-    if (seen == old + 1) return 0;
-    if ((seen >> 32) == epoch) {
-      old = atomicAdd(word, 1ull);
-    } else {
-      old = seen - 1;  // compare against what is there now
+  while ((old >> 32) != epoch) {
+    unsigned long long cur = old + 1;  // what this caller's add left
+    for (;;) {
+      if (++tries > kTicketTries) return -1;
+      const unsigned long long seen = atomicCAS(word, cur, tag | 1ull);
+      if (seen == cur) return 0;
+      if ((seen >> 32) == epoch) break;
+      cur = seen;  // another add on the old contents in between
     }
+    old = atomicAdd(word, 1ull);
   }
-  return -1;
+  return (int)(uint32_t)old;
 }
+
+__device__ inline int take_ticket(unsigned long long* word, uint32_t epoch) {
+  return take_ticket_after(word, epoch, atomicAdd(word, 1ull));
+}
+
+// Partitions a merge reads per round trip.
+constexpr int kMergeBatch = 8;
 
 // Arrival words: one per (sequence, KV head) of a split sequence,
 // (epoch << 32) | partitions done in this launch. Every workgroup tags a
@@ -733,7 +747,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   // loads, and those are agent-scope too: no cache-wide release or acquire
   // (L2 write-back or invalidate) is needed. The merge combines the
   // partitions in index order: M = max m_q, then sums of 2^(m_q - M) l_q and
-  // 2^(m_q - M) O_q.
+  // 2^(m_q - M) O_q (with the running max moved between batches of loads).
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   int* s_last = reinterpret_cast<int*>(smem + lds_main + 2 * kWaves * 16 * 4) + 2;
@@ -744,16 +758,40 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
     const int h = idx / D;
     const int d = idx - h * D;
     const size_t row = (size_t)seq * p.num_heads + head0 + h;
-    const float* ml = p.ws_ml + 2 * row * p.num_partitions;
+    const unsigned long long* ml =
+        reinterpret_cast<const unsigned long long*>(p.ws_ml + 2 * row * p.num_partitions);
     const float* o = p.ws_o + row * p.num_partitions * D + d;
-    float M = -INFINITY;
-    for (int q = 0; q < nparts; ++q)
-      M = fmaxf(M, __hip_atomic_load(&ml[2 * q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    float den = 0.0f, num = 0.0f;
-    for (int q = 0; q < nparts; ++q) {
-      const float wq = fast_exp2(__hip_atomic_load(&ml[2 * q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M);
-      den += wq * __hip_atomic_load(&ml[2 * q + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      num += wq * __hip_atomic_load(&o[(size_t)q * D], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // kMergeBatch partitions per round trip: every load of a batch is issued
+    // before any is used; the running max moves between batches
+    float M = -INFINITY, den = 0.0f, num = 0.0f;
+    for (int q0 = 0; q0 < nparts; q0 += kMergeBatch) {
+      float mq[kMergeBatch], lq[kMergeBatch], oq[kMergeBatch];
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const int q = q0 + j;
+        mq[j] = -INFINITY;
+        lq[j] = oq[j] = 0.0f;
+        if (q < nparts) {
+          const unsigned long long pair = __hip_atomic_load(&ml[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          mq[j] = __uint_as_float((uint32_t)pair);
+          lq[j] = __uint_as_float((uint32_t)(pair >> 32));
+          oq[j] = __hip_atomic_load(&o[(size_t)q * D], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      float cm = mq[0];
+#pragma unroll
+      for (int j = 1; j < kMergeBatch; ++j) cm = fmaxf(cm, mq[j]);
+      const float M_new = fmaxf(M, cm);
+      const float alpha = fast_exp2(M - M_new);  // 0 for the first batch
+      den *= alpha;
+      num *= alpha;
+      M = M_new;
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const float wq = fast_exp2(mq[j] - M);
+        den += wq * lq[j];
+        num += wq * oq[j];
+      }
     }
     store_out<Tag>(p, row * D + d, num / den);
   }
