@@ -20,6 +20,9 @@ Pins (checked by ``tests/test_oracle_*.py`` without a GPU):
     §2.3); every other byte unchanged.
   * ``copy_blocks``: destination equals the pre-call source, all else
     unchanged, and decode after a copy-on-write remap equals decode before.
+  * ``multi_query`` (q_len new tokens per sequence): row j equals ``decode``
+    of the sequence truncated to the positions it sees; one new token is
+    decode; changing position p changes exactly the rows that see it.
   * closed forms: the printed KV-size, block-size and pool-sizing numbers.
 No function here is "parity unpinned".
 """
@@ -31,5 +34,7 @@ from .paged_attention import (  # noqa: F401
     decode,
     decode_one,
     kv_cache_bytes,
+    multi_query,
+    multi_query_one,
     reshape_and_cache,
 )

@@ -132,6 +132,77 @@ def decode(query, key_cache, value_cache, block_table, seq_lens, scale: float,
 
 
 # ----------------------------------------------------------------------------
+# several new tokens per sequence (speculative verification, chunked prefill)
+# ----------------------------------------------------------------------------
+
+def multi_query_one(q_s, key_cache, value_cache, table_row, seq_len: int,
+                    scale: float) -> np.ndarray:
+    """Attention outputs of the q_len newest tokens of one sequence, float64
+    ``[q_len, num_heads, head_dim]``.
+
+    The target model checks all of a draft model's candidate tokens in one
+    forward pass over the cached prefix ([IO] §4.1-§4.2; [VC] §4.4.1;
+    [EI] §5.2: the candidates' K/V live in the same blocks); a prefill cut
+    into chunks does the same per chunk ([IO] §5.3). Reading taken: the
+    q_len new tokens are the last q_len positions L-q_len .. L-1 of the
+    sequence (their K/V already written to their slots), and new token j
+    attends causally to positions 0 .. L-q_len+j. Each (token, head) is
+    otherwise the decode of [PP] §2.2: gather through the block table,
+    score = q . k * scale, softmax over the attended positions, weighted sum
+    of V. A token with no attended position (L < q_len) gives a zero row.
+    """
+    q = _to_f64(q_s)                      # [q_len, H, D]
+    Q, H, D = q.shape
+    nb, bs, hkv, d = _pool_shape(key_cache)
+    if d != D:
+        raise ValueError("head_dim mismatch")
+    if H % hkv != 0:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    G = H // hkv
+    L = int(seq_len)
+    out = np.zeros((Q, H, D), dtype=np.float64)
+    if L <= 0:
+        return out
+    row = _to_np_int(table_row)
+    t = np.arange(L)
+    phys = row[t // bs]
+    off = t % bs
+    if np.any(phys < 0) or np.any(phys >= nb):
+        raise IndexError("block table entry outside the pool")
+    kc = _to_f64(key_cache[torch.as_tensor(phys), torch.as_tensor(off)]
+                 if isinstance(key_cache, torch.Tensor) else
+                 np.asarray(key_cache)[phys, off])          # [L, Hkv, D]
+    vc = _to_f64(value_cache[torch.as_tensor(phys), torch.as_tensor(off)]
+                 if isinstance(value_cache, torch.Tensor) else
+                 np.asarray(value_cache)[phys, off])
+    for j in range(Q):
+        last = L - Q + j                  # the newest position token j sees
+        if last < 0:
+            continue
+        for h in range(H):
+            kv = h // G
+            scores = (kc[:last + 1, kv, :] @ q[j, h]) * float(scale)
+            w = np.exp(scores - scores.max())
+            out[j, h] = (w @ vc[:last + 1, kv, :]) / w.sum()
+    return out
+
+
+def multi_query(query, key_cache, value_cache, block_table, seq_lens, scale: float,
+                seqs=None) -> np.ndarray:
+    """multi_query_one for a batch: ``query`` ``[num_seqs, q_len, H, D]`` ->
+    float64 ``[num_seqs, q_len, H, D]``; rows not in ``seqs`` (if given) are NaN."""
+    S, Q, H, D = tuple(query.shape)
+    lens = _to_np_int(seq_lens)
+    bt = _to_np_int(block_table)
+    out = np.full((S, Q, H, D), np.nan, dtype=np.float64)
+    rows = range(S) if seqs is None else seqs
+    for s in rows:
+        out[s] = multi_query_one(query[s], key_cache, value_cache, bt[s],
+                                 int(lens[s]), scale)
+    return out
+
+
+# ----------------------------------------------------------------------------
 # cache operations (bit copies in the storage dtype)
 # ----------------------------------------------------------------------------
 

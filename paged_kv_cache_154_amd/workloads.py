@@ -94,7 +94,7 @@ class Workload:
     scale: float
     seq_lens: np.ndarray            # int32 [S]
     block_table: np.ndarray         # int32 [S, MB] (after any copy-on-write remap)
-    query: torch.Tensor             # [S, H, D]
+    query: torch.Tensor             # [S, H, D]; [S, q_len, H, D] when q_len > 1
     key_cache: torch.Tensor         # [NB, bs, Hkv, D], before this step's cache ops
     value_cache: torch.Tensor
     partition_size: int = 0         # 0: the library chooses
@@ -105,6 +105,7 @@ class Workload:
     block_table_before_cow: np.ndarray | None = None
     unique_blocks: int = 0          # physical blocks holding data or referenced
     info: dict = field(default_factory=dict)
+    q_len: int = 1                  # new tokens per sequence (the last q_len positions)
 
     # -- shape helpers ----------------------------------------------------
     @property
@@ -140,7 +141,7 @@ def _place(rng, num_blocks: int, n_virtual: int):
 def _assemble(*, name, seed, rng, H, Hkv, D, bs, dtype, seq_lens, tables_virtual,
               fill, num_blocks, max_blocks, new_positions=None,
               tables_virtual_before=None, cow_virtual_pairs=None,
-              partition_size=0) -> Workload:
+              partition_size=0, q_len=1) -> Workload:
     """Turn a virtual block layout into concrete pools and tables.
 
     tables_virtual[s] lists the virtual block ids of sequence s in logical
@@ -163,7 +164,7 @@ def _assemble(*, name, seed, rng, H, Hkv, D, bs, dtype, seq_lens, tables_virtual
     block_table = table_of(tables_virtual)
     before = table_of(tables_virtual_before) if tables_virtual_before is not None else None
 
-    query = _values(seed, "q", (S, H, D), dtype)
+    query = _values(seed, "q", (S, H, D) if q_len == 1 else (S, q_len, H, D), dtype)
 
     fill = np.asarray(fill, dtype=np.int64)
     # flat slot of every cached token, virtual-block order, slot order
@@ -183,14 +184,17 @@ def _assemble(*, name, seed, rng, H, Hkv, D, bs, dtype, seq_lens, tables_virtual
                   seq_lens=np.asarray(seq_lens, dtype=np.int32),
                   block_table=block_table, query=query, key_cache=key_cache,
                   value_cache=value_cache, partition_size=partition_size,
-                  block_table_before_cow=before, unique_blocks=n_virtual)
+                  block_table_before_cow=before, unique_blocks=n_virtual, q_len=q_len)
 
     if new_positions is not None:
-        T = len(new_positions)
+        # one position per sequence, or a list of them (q_len > 1), in order
+        flat = [(s, int(pos)) for s, p_s in enumerate(new_positions)
+                for pos in (p_s if isinstance(p_s, (list, tuple)) else [p_s])]
+        T = len(flat)
         slots = np.empty(T, dtype=np.int64)
-        for s, pos in enumerate(new_positions):
-            lb, off = divmod(int(pos), bs)
-            slots[s] = int(phys[tables_virtual[s][lb]]) * bs + off
+        for i, (s, pos) in enumerate(flat):
+            lb, off = divmod(pos, bs)
+            slots[i] = int(phys[tables_virtual[s][lb]]) * bs + off
         wl.slot_mapping = slots
         wl.new_key = _values(seed, "new_k", (T, Hkv, D), dtype)
         wl.new_value = _values(seed, "new_v", (T, Hkv, D), dtype)
@@ -200,13 +204,14 @@ def _assemble(*, name, seed, rng, H, Hkv, D, bs, dtype, seq_lens, tables_virtual
     return wl
 
 
-def _plain_layout(seq_lens, bs, new_token: bool):
+def _plain_layout(seq_lens, bs, new_token: bool, q_len: int = 1):
     """Each sequence owns ceil(L/bs) private blocks, sequence-major. With
-    new_token, position L-1 is left empty for this step's scatter."""
+    new_token, positions L-q_len .. L-1 are left empty for this step's
+    scatter."""
     tables, fill = [], []
     for L in seq_lens:
         L = int(L)
-        stored = L - 1 if (new_token and L > 0) else L
+        stored = max(0, L - q_len) if (new_token and L > 0) else L
         nblk = (L + bs - 1) // bs
         row = []
         for i in range(nblk):
@@ -219,24 +224,29 @@ def _plain_layout(seq_lens, bs, new_token: bool):
 def custom(seed: int, *, seq_lens, num_heads: int, num_kv_heads: int, head_dim: int,
            block_size: int, dtype: torch.dtype, num_blocks: int | None = None,
            max_blocks_per_seq: int | None = None, new_token: bool = False,
-           partition_size: int = 0, name: str = "custom") -> Workload:
-    """A plain (unshared) paged batch with the given lengths."""
+           partition_size: int = 0, name: str = "custom", q_len: int = 1) -> Workload:
+    """A plain (unshared) paged batch with the given lengths. With q_len > 1
+    each sequence has q_len new tokens (its last q_len positions): the query
+    is [S, q_len, H, D], and with new_token their K/V come from the scatter."""
     rng = np.random.default_rng(seed)
     seq_lens = [int(x) for x in seq_lens]
-    tables, fill = _plain_layout(seq_lens, block_size, new_token)
+    tables, fill = _plain_layout(seq_lens, block_size, new_token, q_len)
     need = len(fill)
     if num_blocks is None:
         num_blocks = max(1, math.ceil(1.2 * need)) + 1
     if max_blocks_per_seq is None:
         max_blocks_per_seq = max([len(r) for r in tables] + [1])
-    newpos = [L - 1 for L in seq_lens] if new_token else None
-    if new_token and any(L <= 0 for L in seq_lens):
-        raise ValueError("new_token needs seq_len >= 1")
+    if q_len == 1:
+        newpos = [L - 1 for L in seq_lens] if new_token else None
+    else:
+        newpos = [list(range(L - q_len, L)) for L in seq_lens] if new_token else None
+    if new_token and any(L < q_len for L in seq_lens):
+        raise ValueError("new_token needs seq_len >= q_len")
     return _assemble(name=name, seed=seed, rng=rng, H=num_heads, Hkv=num_kv_heads,
                      D=head_dim, bs=block_size, dtype=dtype, seq_lens=seq_lens,
                      tables_virtual=tables, fill=fill, num_blocks=num_blocks,
                      max_blocks=max_blocks_per_seq, new_positions=newpos,
-                     partition_size=partition_size)
+                     partition_size=partition_size, q_len=q_len)
 
 
 # ----------------------------------------------------------------------------

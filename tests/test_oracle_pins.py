@@ -402,3 +402,110 @@ def test_block_and_pool_sizing_against_printed_examples():
     units = lb["kv_gb"] / 0.125 * 1000
     assert units == lb["units_printed"] and units * 16 == lb["tokens_printed"]
     assert abs(units * 16 / 4096 - lb["requests_printed"]) / lb["requests_printed"] < 0.05
+
+
+# ----------------------------------------------------------------------------
+# several new tokens per sequence: pinned to the (pinned) decode oracle
+# ----------------------------------------------------------------------------
+
+MQ_CASES = [
+    # seed, lens, q_len, H, Hkv, D, bs, dtype
+    (41, [4, 17, 40, 70], 4, 8, 2, 64, 16, torch.float32),
+    (42, [2, 9, 33], 2, 16, 2, 128, 8, torch.bfloat16),
+    (43, [8, 31, 65], 8, 4, 4, 64, 32, torch.float16),
+    (44, [5, 100], 5, 4, 1, 64, 16, torch.float32),
+]
+
+
+def _mq(case):
+    seed, lens, q, H, Hkv, D, bs, dt = case
+    return W.custom(seed, seq_lens=lens, num_heads=H, num_kv_heads=Hkv, head_dim=D,
+                    block_size=bs, dtype=dt, q_len=q)
+
+
+@pytest.mark.parametrize("case", MQ_CASES, ids=lambda c: f"seed{c[0]}")
+def test_multi_query_row_j_is_decode_of_the_prefix_it_sees(case):
+    """New token j of a sequence of length L attends to positions
+    0 .. L-q_len+j: its row equals the decode of the same query over the
+    sequence truncated to L-q_len+j+1 tokens (the decode oracle is pinned to
+    torch SDPA above)."""
+    wl = _mq(case)
+    q = wl.q_len
+    out = oracle.multi_query(wl.query, wl.key_cache, wl.value_cache, wl.block_table,
+                             wl.seq_lens, wl.scale)
+    for s in range(wl.num_seqs):
+        L = int(wl.seq_lens[s])
+        for j in range(q):
+            ref = oracle.decode_one(wl.query[s, j], wl.key_cache, wl.value_cache,
+                                    wl.block_table[s], L - q + j + 1, wl.scale)
+            assert np.allclose(out[s, j], ref, rtol=0, atol=1e-12), (s, j)
+
+
+def test_multi_query_with_one_new_token_is_decode():
+    wl = W.custom(45, seq_lens=[1, 20, 77], num_heads=8, num_kv_heads=2, head_dim=64,
+                  block_size=16, dtype=torch.float32)
+    out = oracle.multi_query(wl.query.unsqueeze(1), wl.key_cache, wl.value_cache,
+                             wl.block_table, wl.seq_lens, wl.scale)
+    ref = oracle.decode(wl.query, wl.key_cache, wl.value_cache, wl.block_table,
+                        wl.seq_lens, wl.scale)
+    assert np.array_equal(out[:, 0], ref)
+
+
+def test_multi_query_is_causal_and_short_sequences_give_zero_rows():
+    """Changing the K/V of position p changes exactly the rows of the new
+    tokens that see it (j >= p - (L - q_len)); a sequence shorter than q_len
+    gives zero rows for the tokens that see no position."""
+    wl = _mq((46, [30], 4, 4, 2, 64, 16, torch.float32))
+    args = (wl.block_table, wl.seq_lens, wl.scale)
+    base = oracle.multi_query(wl.query, wl.key_cache, wl.value_cache, *args)
+    L, q, bs = 30, 4, 16
+    for p in (0, L - q, L - q + 2, L - 1):
+        kc = wl.key_cache.clone()
+        blk, off = int(wl.block_table[0, p // bs]), p % bs
+        kc[blk, off] += 1.0
+        out = oracle.multi_query(wl.query, kc, wl.value_cache, *args)
+        for j in range(q):
+            changed = not np.array_equal(out[0, j], base[0, j])
+            assert changed == (L - q + j >= p), (p, j)
+    short = oracle.multi_query(wl.query, wl.key_cache, wl.value_cache, wl.block_table,
+                               np.array([2], dtype=np.int32), wl.scale)
+    assert np.array_equal(short[0, :2], np.zeros_like(short[0, :2]))
+    assert np.isfinite(short).all() and np.abs(short[0, 2:]).sum() > 0
+
+
+def test_multi_query_pin_detects_planted_mistakes():
+    """Plausible mistakes, planted in copies on the CPU, fail the prefix pin:
+    an off-by-one causal limit, the mask aligned to the front instead of the
+    end of the sequence, no mask at all, and token/head order swapped."""
+    wl = _mq((47, [12, 40], 4, 8, 2, 64, 16, torch.float32))
+    q = wl.q_len
+
+    def prefix_ref():
+        return [[oracle.decode_one(wl.query[s, j], wl.key_cache, wl.value_cache,
+                                   wl.block_table[s], int(wl.seq_lens[s]) - q + j + 1, wl.scale)
+                 for j in range(q)] for s in range(wl.num_seqs)]
+
+    ref = prefix_ref()
+
+    def mq_with(last_of):
+        out = np.zeros((wl.num_seqs, q, wl.num_heads, wl.head_dim))
+        for s in range(wl.num_seqs):
+            L = int(wl.seq_lens[s])
+            for j in range(q):
+                n = last_of(L, j) + 1
+                out[s, j] = oracle.decode_one(wl.query[s, j], wl.key_cache, wl.value_cache,
+                                              wl.block_table[s], n, wl.scale)
+        return out
+
+    def far(out):
+        return not all(np.allclose(out[s, j], ref[s][j], rtol=0, atol=1e-9)
+                       for s in range(wl.num_seqs) for j in range(q))
+
+    assert not far(mq_with(lambda L, j: L - q + j))                 # the reading itself
+    assert far(mq_with(lambda L, j: L - q + j - 1))                 # off by one
+    assert far(mq_with(lambda L, j: j))                             # front-aligned mask
+    assert far(mq_with(lambda L, j: L - 1))                         # no mask
+    swapped = wl.query.transpose(1, 2).reshape(wl.query.shape).contiguous()
+    out = oracle.multi_query(swapped, wl.key_cache, wl.value_cache, wl.block_table,
+                             wl.seq_lens, wl.scale)
+    assert far(out)
