@@ -115,6 +115,47 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache,
                       size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * paged_attn_multi_query - attention of q_len new tokens per sequence over
+ * the paged cache: the verification pass of speculative decoding, where the
+ * target model checks a draft model's q_len candidate tokens in one forward
+ * pass over the cached prefix ("LLM inference optimisation in practice"
+ * sections 4.1-4.2; "vLLM core concepts" section 4.4.1; "LLM inference
+ * engine internals" section 5.2: the candidates' K/V share the blocks), or
+ * one chunk of a chunked prefill (the same page, section 5.3).
+ *
+ * The new tokens are the last q_len positions of each sequence (write their
+ * K and V with reshape_and_cache first); new token j attends causally:
+ *   out[s, j, h, :] = sum_{t <= L - q_len + j} softmax_t(scale * q[s, j, h] . k_t) * v_t
+ * with L = seq_lens[s], k_t, v_t as in paged_attn_decode. A token that sees
+ * no position (L < q_len) gives a zero row. q_len = 1 is paged_attn_decode.
+ *
+ *   out, query   [num_seqs, q_len, num_heads, head_dim]
+ *   q_len        1 .. 16 / (num_heads / num_kv_heads) (the q_len * G query
+ *                rows of a KV head share one 16-column MFMA tile)
+ *   workspace    at least paged_attn_multi_query_workspace_size(...) bytes
+ * All other arguments, the partitioning, the status codes and the
+ * workspace rules are those of paged_attn_decode.
+ */
+int paged_attn_multi_query(void* out, const void* query, const void* key_cache,
+                           const void* value_cache, const int32_t* block_table,
+                           const int32_t* seq_lens, int num_seqs, int q_len,
+                           int num_heads, int num_kv_heads, int head_dim,
+                           int block_size, int num_blocks, int max_blocks_per_seq,
+                           int max_seq_len, float scale, int kv_dtype, int out_dtype,
+                           int partition_size, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_attn_multi_query_workspace_size - paged_attn_workspace_size for
+ * q_len new tokens per sequence (the partials hold q_len * num_heads rows per
+ * sequence). 0 when the arguments are invalid or num_seqs is 0.
+ */
+size_t paged_attn_multi_query_workspace_size(int num_seqs, int q_len, int num_heads,
+                                             int num_kv_heads, int head_dim,
+                                             int block_size, int max_seq_len,
+                                             int partition_size);
+
+/*
  * paged_attn_partition_tokens - the partition length paged_attn_decode uses
  * for these arguments (resolving partition_size = 0), or a negative
  * pkv_status for invalid arguments. A value >= max_seq_len means no split.

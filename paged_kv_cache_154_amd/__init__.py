@@ -8,11 +8,15 @@ kernels of ``libpagedkv.so``; there is no Python or CPU fallback.
     paged_attn_decode(out, query, key_cache, value_cache, block_table,
                       seq_lens, scale, max_seq_len, partition_size=0,
                       workspace=None)
+    paged_attn_multi_query(out, query, key_cache, value_cache, block_table,
+                           seq_lens, scale, max_seq_len, partition_size=0,
+                           workspace=None)
     reshape_and_cache(key, value, key_cache, value_cache, slot_mapping)
     copy_blocks(key_cache, value_cache, block_mapping)
 
 Shapes (all dense, on one GPU): query/out ``[num_seqs, num_heads,
-head_dim]``; pools ``[num_blocks, block_size, num_kv_heads, head_dim]``;
+head_dim]`` for decode, ``[num_seqs, q_len, num_heads, head_dim]`` for
+the multi-query pass; pools ``[num_blocks, block_size, num_kv_heads, head_dim]``;
 block_table int32 ``[num_seqs, max_blocks_per_seq]``; seq_lens int32
 ``[num_seqs]``; slot_mapping int64 ``[num_tokens]``; block_mapping int64
 ``[num_pairs, 2]``.
@@ -71,15 +75,62 @@ def paged_attn_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, 
                                                block_size, max_seq_len, partition_size))
 
 
+def paged_attn_multi_query_workspace_size(num_seqs: int, q_len: int, num_heads: int,
+                                          num_kv_heads: int, head_dim: int, block_size: int,
+                                          max_seq_len: int, partition_size: int = 0) -> int:
+    return int(lib().paged_attn_multi_query_workspace_size(
+        num_seqs, q_len, num_heads, num_kv_heads, head_dim, block_size, max_seq_len,
+        partition_size))
+
+
 def workspace_for(query: torch.Tensor, key_cache: torch.Tensor, max_seq_len: int,
                   partition_size: int = 0) -> torch.Tensor | None:
-    """A device buffer big enough for paged_attn_decode with these shapes."""
-    S, H, D = query.shape
+    """A device buffer big enough for paged_attn_decode (query ``[S, H, D]``)
+    or paged_attn_multi_query (query ``[S, q_len, H, D]``) with these shapes."""
+    if query.dim() == 3:
+        S, H, D = query.shape
+        Q = 1
+    else:
+        S, Q, H, D = query.shape
     NB, bs, Hkv, _ = key_cache.shape
-    n = paged_attn_workspace_size(S, H, Hkv, D, bs, max_seq_len, partition_size)
+    n = paged_attn_multi_query_workspace_size(S, Q, H, Hkv, D, bs, max_seq_len, partition_size)
     if n == 0:
         return None
     return torch.empty(n, dtype=torch.uint8, device=query.device)
+
+
+def _attention(name: str, out, query, key_cache, value_cache, block_table, seq_lens, scale,
+               max_seq_len, partition_size, workspace, stream) -> torch.Tensor:
+    multi = name == "paged_attn_multi_query"
+    want = 4 if multi else 3
+    _require(query.dim() == want and out.shape == query.shape,
+             "query/out must be [S, q_len, H, D]" if multi else "query/out must be [S, H, D]")
+    _require(key_cache.dim() == 4 and value_cache.shape == key_cache.shape,
+             "pools must be [num_blocks, block_size, num_kv_heads, head_dim]")
+    _require(block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32,
+             "block_table and seq_lens must be int32")
+    _require(query.dtype == key_cache.dtype == value_cache.dtype, "query and pools share a dtype")
+    if multi:
+        S, Q, H, D = query.shape
+    else:
+        (S, H, D), Q = query.shape, 1
+    NB, bs, Hkv, D2 = key_cache.shape
+    _require(D2 == D, "head_dim of query and pools differ")
+    _require(block_table.dim() == 2 and block_table.shape[0] == S and seq_lens.shape == (S,),
+             "block_table must be [S, max_blocks] and seq_lens [S]")
+    if workspace is None:
+        workspace = workspace_for(query, key_cache, max_seq_len, partition_size)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    head = [_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_table),
+            _ptr(seq_lens), S]
+    if multi:
+        head.append(Q)
+    st = getattr(lib(), name)(
+        *head, H, Hkv, D, bs, NB, block_table.shape[1], int(max_seq_len), float(scale),
+        dtype_code(query.dtype), dtype_code(out.dtype), int(partition_size), _ptr(workspace),
+        ws_bytes, _stream(query, stream))
+    check(st, name)
+    return out
 
 
 def paged_attn_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
@@ -93,27 +144,23 @@ def paged_attn_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.T
     item counter and split-K partials; no initialisation needed); later calls
     on the same stream can reuse it. With ``workspace=None`` one is allocated
     by torch."""
-    _require(query.dim() == 3 and out.shape == query.shape, "query/out must be [S, H, D]")
-    _require(key_cache.dim() == 4 and value_cache.shape == key_cache.shape,
-             "pools must be [num_blocks, block_size, num_kv_heads, head_dim]")
-    _require(block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32,
-             "block_table and seq_lens must be int32")
-    _require(query.dtype == key_cache.dtype == value_cache.dtype, "query and pools share a dtype")
-    S, H, D = query.shape
-    NB, bs, Hkv, D2 = key_cache.shape
-    _require(D2 == D, "head_dim of query and pools differ")
-    _require(block_table.dim() == 2 and block_table.shape[0] == S and seq_lens.shape == (S,),
-             "block_table must be [S, max_blocks] and seq_lens [S]")
-    if workspace is None:
-        workspace = workspace_for(query, key_cache, max_seq_len, partition_size)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().paged_attn_decode(
-        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_table),
-        _ptr(seq_lens), S, H, Hkv, D, bs, NB, block_table.shape[1], int(max_seq_len),
-        float(scale), dtype_code(query.dtype), dtype_code(out.dtype), int(partition_size),
-        _ptr(workspace), ws_bytes, _stream(query, stream))
-    check(st, "paged_attn_decode")
-    return out
+    return _attention("paged_attn_decode", out, query, key_cache, value_cache, block_table,
+                      seq_lens, scale, max_seq_len, partition_size, workspace, stream)
+
+
+def paged_attn_multi_query(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                           value_cache: torch.Tensor, block_table: torch.Tensor,
+                           seq_lens: torch.Tensor, scale: float, max_seq_len: int,
+                           partition_size: int = 0, workspace: torch.Tensor | None = None,
+                           stream=None) -> torch.Tensor:
+    """Causal attention of the last ``q_len`` tokens of each sequence (query
+    ``[S, q_len, H, D]``; their K/V already written to the pool): new token j
+    sees positions ``0 .. seq_len - q_len + j``. ``q_len * (H / Hkv)`` must be
+    at most 16. Workspace rules as for paged_attn_decode, sized by
+    ``paged_attn_multi_query_workspace_size``."""
+    return _attention("paged_attn_multi_query", out, query, key_cache, value_cache,
+                      block_table, seq_lens, scale, max_seq_len, partition_size, workspace,
+                      stream)
 
 
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,

@@ -21,6 +21,12 @@ SIGNATURES = {
                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                    _c_int, _c_float, _c_int, _c_int, _c_int, _c_ptr, _c_size,
                                    _c_ptr]),
+    "paged_attn_multi_query": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                        _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                        _c_int, _c_int, _c_float, _c_int, _c_int, _c_int, _c_ptr,
+                                        _c_size, _c_ptr]),
+    "paged_attn_multi_query_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int,
+                                                        _c_int, _c_int, _c_int]),
     "paged_attn_partition_tokens": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "paged_attn_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                             _c_int]),

@@ -105,30 +105,25 @@ int paged_attn_partition_tokens(int num_seqs, int num_kv_heads, int block_size, 
   return resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
 }
 
-size_t paged_attn_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-                                 int block_size, int max_seq_len, int partition_size) {
-  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return 0;
-  if (num_heads % num_kv_heads != 0 || num_heads / num_kv_heads > 16) return 0;
-  if (!supported_head_dim(head_dim)) return 0;
-  const int P = resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
-  if (P < 0) return 0;
-  return workspace_bytes_for(num_seqs, num_heads, num_kv_heads, head_dim,
-                             cutting_for(max_seq_len, block_size, P).np);
-}
+}  // extern "C"
 
-int paged_attn_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
-                      const int32_t* block_table, const int32_t* seq_lens, int num_seqs,
-                      int num_heads, int num_kv_heads, int head_dim, int block_size,
-                      int num_blocks, int max_blocks_per_seq, int max_seq_len, float scale,
-                      int kv_dtype, int out_dtype, int partition_size, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
-  if (num_seqs < 0) return PKV_ERR_SHAPE;
+namespace {
+
+// paged_attn_decode and paged_attn_multi_query: q_len new tokens per
+// sequence (1 for decode), query and out [num_seqs, q_len, num_heads, head_dim].
+int attention(void* out, const void* query, const void* key_cache, const void* value_cache,
+              const int32_t* block_table, const int32_t* seq_lens, int num_seqs, int q_len,
+              int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+              int max_blocks_per_seq, int max_seq_len, float scale, int kv_dtype, int out_dtype,
+              int partition_size, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (num_seqs < 0 || q_len < 1) return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !query || !key_cache || !value_cache || !block_table || !seq_lens)
     return PKV_ERR_NULL;
   if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
   const int group = num_heads / num_kv_heads;
-  if (group > 16) return PKV_ERR_UNSUPPORTED;
+  // the q_len * group query rows of a KV head fill at most one 16-column MFMA tile
+  if (group > 16 || q_len > 16 || q_len * group > 16) return PKV_ERR_UNSUPPORTED;
   if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
   if (elem_bytes(kv_dtype) == 0) return PKV_ERR_UNSUPPORTED;
   if (out_dtype != kv_dtype && out_dtype != PKV_F32) return PKV_ERR_UNSUPPORTED;
@@ -144,7 +139,7 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
   // the grid) stay in int32
   const int s_launch = num_seqs < pkv::kMaxSeqsPerLaunch ? num_seqs : pkv::kMaxSeqsPerLaunch;
   if ((int64_t)s_launch * num_kv_heads * np > (int64_t)INT32_MAX - (1 << 24)) return PKV_ERR_SHAPE;
-  const size_t need = workspace_bytes_for(num_seqs, num_heads, num_kv_heads, head_dim, np);
+  const size_t need = workspace_bytes_for(num_seqs, q_len * num_heads, num_kv_heads, head_dim, np);
   if (workspace == nullptr || workspace_bytes < need) return PKV_ERR_WORKSPACE;
 
   pkv::DecodeParams p{};
@@ -159,10 +154,11 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
   if (np > 1) {
     const int s = num_seqs < pkv::kMaxSeqsPerLaunch ? num_seqs : pkv::kMaxSeqsPerLaunch;
     p.ws_o = reinterpret_cast<float*>(ws + kHeaderBytes);
-    p.ws_ml = p.ws_o + (size_t)s * num_heads * np * head_dim;
-    p.arrive = reinterpret_cast<unsigned long long*>(p.ws_ml + (size_t)s * num_heads * np * 2);
+    p.ws_ml = p.ws_o + (size_t)s * q_len * num_heads * np * head_dim;
+    p.arrive = reinterpret_cast<unsigned long long*>(p.ws_ml + (size_t)s * q_len * num_heads * np * 2);
   }
   p.num_seqs = num_seqs;
+  p.q_len = q_len;
   p.num_heads = num_heads;
   p.num_kv_heads = num_kv_heads;
   p.group = group;
@@ -175,6 +171,56 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
   p.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
     const hipError_t e = pkv::launch_decode(p, kv_dtype, head_dim, block_size, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+size_t workspace_size(int num_seqs, int q_len, int num_heads, int num_kv_heads, int head_dim,
+                      int block_size, int max_seq_len, int partition_size) {
+  if (num_seqs <= 0 || q_len < 1 || num_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return 0;
+  if (num_heads % num_kv_heads != 0 || q_len > 16 || q_len * (num_heads / num_kv_heads) > 16) return 0;
+  if (!supported_head_dim(head_dim)) return 0;
+  const int P = resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
+  if (P < 0) return 0;
+  return workspace_bytes_for(num_seqs, q_len * num_heads, num_kv_heads, head_dim,
+                             cutting_for(max_seq_len, block_size, P).np);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t paged_attn_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                 int block_size, int max_seq_len, int partition_size) {
+  return workspace_size(num_seqs, 1, num_heads, num_kv_heads, head_dim, block_size, max_seq_len,
+                        partition_size);
+}
+
+size_t paged_attn_multi_query_workspace_size(int num_seqs, int q_len, int num_heads, int num_kv_heads,
+                                             int head_dim, int block_size, int max_seq_len,
+                                             int partition_size) {
+  return workspace_size(num_seqs, q_len, num_heads, num_kv_heads, head_dim, block_size, max_seq_len,
+                        partition_size);
+}
+
+int paged_attn_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                      const int32_t* block_table, const int32_t* seq_lens, int num_seqs,
+                      int num_heads, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, int max_blocks_per_seq, int max_seq_len, float scale,
+                      int kv_dtype, int out_dtype, int partition_size, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  return attention(out, query, key_cache, value_cache, block_table, seq_lens, num_seqs, 1, num_heads,
+                   num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_seq_len, scale,
+                   kv_dtype, out_dtype, partition_size, workspace, workspace_bytes, stream);
+}
+
+int paged_attn_multi_query(void* out, const void* query, const void* key_cache, const void* value_cache,
+                           const int32_t* block_table, const int32_t* seq_lens, int num_seqs, int q_len,
+                           int num_heads, int num_kv_heads, int head_dim, int block_size,
+                           int num_blocks, int max_blocks_per_seq, int max_seq_len, float scale,
+                           int kv_dtype, int out_dtype, int partition_size, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  return attention(out, query, key_cache, value_cache, block_table, seq_lens, num_seqs, q_len, num_heads,
+                   num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_seq_len, scale,
+                   kv_dtype, out_dtype, partition_size, workspace, workspace_bytes, stream);
 }
 
 int reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,

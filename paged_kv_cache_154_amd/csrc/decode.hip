@@ -5,6 +5,11 @@
 // engine internals" section 2.4): for each sequence s and query head h, over
 // the tokens t < seq_len reached through the block table,
 //   out[s,h] = sum_t softmax_t(scale * q[s,h] . K[t, h/G]) * V[t, h/G].
+// With q_len > 1 new tokens per sequence (the candidates of speculative
+// decoding verified in one pass, or a chunk of a prefill: "LLM inference
+// optimisation in practice" sections 4.1-4.2 and 5.3), new token j attends
+// to the positions t <= seq_len - q_len + j; its q_len * G query rows fill
+// the MFMA columns of a KV head, each column with its own limit.
 //
 // How (an MI355X design, not the pages' kernel):
 //  * The unit of work is a 16-token key tile of one (sequence, KV head). A
@@ -19,7 +24,8 @@
 //      - Q.K^T on v_mfma_f32_16x16x32_{f16,bf16} (fp32 pools:
 //        v_mfma_f32_16x16x4_f32) with the key tile as the A operand (16
 //        tokens x 32 head-dim elements, straight from the pool) and the G
-//        query heads of the KV head as the B operand (columns >= G are 0).
+//        query heads of the KV head (q_len * G query rows with several new
+//        tokens) as the B operand (the other columns are 0).
 //        The result S[token][head] leaves each lane one head's scores for 4
 //        tokens, so a head's softmax state lives in one lane column;
 //      - P.V on v_mfma_f32_16x16x4_f32 with A = V^T (each lane holds head_dim
@@ -170,6 +176,11 @@ struct WavesPerEU {
 };
 // log2 of the largest weight allowed before the running max is moved.
 constexpr float kRescaleSlack = 8.0f;
+// Starting running max: a finite stand-in for -inf, so that a column that
+// sees no position in a tile (or a whole partition: a causal limit) keeps
+// exact zero weights instead of NaN (2^(-inf - -inf)); the first attended
+// score replaces it, and 2^(kNoMax - score) is 0 like 2^-inf.
+constexpr float kNoMax = -1e30f;
 
 // Per-lane state of one wave working through the tiles of one (sequence, KV
 // head): the query operand, the softmax state of head `col` and its O^T
@@ -190,8 +201,9 @@ struct TileEngine {
   static constexpr int KTS = RB + 16;      // LDS row stride of the K tile
   static constexpr int KT_BYTES = kKLds ? 16 * KTS : 0;  // one wave's K tile
 
-  int col;  // MFMA column: head within the group
+  int col;  // MFMA column: query row within the KV head's rows
   int grp;  // lane group 0..3
+  int lim;  // last position column `col` attends to
   uint4 qv[NKL];
   float m;     // running max of head `col` (log2 units)
   float lsum;  // this lane's share of the running sum of weights
@@ -202,18 +214,17 @@ struct TileEngine {
     grp = lane >> 4;
   }
 
-  // q_group: the row of the first query head of this KV head's group.
-  __device__ void load_q(const unsigned char* q_group, int G) {
-    const unsigned char* qrow = q_group + (size_t)(col < G ? col : 0) * RB;
+  // qrow: this lane's query row (column col), read when `valid`.
+  __device__ void load_q(const unsigned char* qrow, bool valid) {
 #pragma unroll
     for (int i = 0; i < NKL; ++i) {
-      qv[i] = col < G ? *reinterpret_cast<const uint4*>(qrow + 16 * (4 * i + grp))
-                      : make_uint4(0u, 0u, 0u, 0u);
+      qv[i] = valid ? *reinterpret_cast<const uint4*>(qrow + 16 * (4 * i + grp))
+                    : make_uint4(0u, 0u, 0u, 0u);
     }
   }
 
   __device__ void reset() {
-    m = -INFINITY;
+    m = kNoMax;
     lsum = 0.0f;
 #pragma unroll
     for (int j = 0; j < VPL; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -273,8 +284,9 @@ struct TileEngine {
 #pragma unroll
     for (int i = 0; i < NKL; ++i) a = Tr::qk(kr[i], qv[i], a);
     float s[4];
+    const int last = min(t_last, lim);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[r] = (cs + 4 * grp + r) <= t_last ? a[r] * scale_log2 : -INFINITY;
+    for (int r = 0; r < 4; ++r) s[r] = (cs + 4 * grp + r) <= last ? a[r] * scale_log2 : -INFINITY;
 
     // Online softmax with a lazy running max: the max (and the rescale of
     // lsum and O) moves only when some lane's tile max exceeds it by more than
@@ -595,13 +607,14 @@ __device__ inline void install_epoch(unsigned long long* word, uint32_t epoch) {
 // waves' K tiles, reused for the waves' O rows (and at the start for the
 // plan's scan); then the waves' (m, l); then the next item; then the plan.
 __host__ __device__ inline int bt_lds_bytes(int span, int BS) { return ((span / BS + 1) * 4 + 15) & ~15; }
-__host__ __device__ inline int lds_main_bytes(int D, int G, int span, int BS, int kt_bytes) {
-  const int o_bytes = kWaves * G * o_stride(D) * 4;
+// R: query rows per KV head (q_len * G).
+__host__ __device__ inline int lds_main_bytes(int D, int R, int span, int BS, int kt_bytes) {
+  const int o_bytes = kWaves * R * o_stride(D) * 4;
   const int tile_bytes = bt_lds_bytes(span, BS) + kWaves * kt_bytes;
   return ((o_bytes > tile_bytes ? o_bytes : tile_bytes) + 15) & ~15;
 }
-__host__ __device__ inline int lds_total_bytes(int D, int G, int span, int BS, int kt_bytes, int S) {
-  return lds_main_bytes(D, G, span, BS, kt_bytes) + 2 * kWaves * 16 * 4 + 16 + plan_bytes(S);
+__host__ __device__ inline int lds_total_bytes(int D, int R, int span, int BS, int kt_bytes, int S) {
+  return lds_main_bytes(D, R, span, BS, kt_bytes) + 2 * kWaves * 16 * 4 + 16 + plan_bytes(S);
 }
 
 // One work item: KV head kvh of partition `part` of sequence `seq`, by the
@@ -620,12 +633,20 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   constexpr int RB = Eng::RB;
   constexpr int VPL = Eng::VPL;
   const int G = p.group;
+  const int R = p.q_len * G;  // query rows of this KV head: (token j, head g) -> j * G + g
   const int head0 = kvh * G;
+  // global row of query row c: [S, q_len, H] flattened
+  auto row_of = [&](int c) -> size_t {
+    const int j = c / G;
+    return ((size_t)seq * p.q_len + j) * p.num_heads + head0 + (c - j * G);
+  };
 
-  if (L == 0) {  // nothing to attend to: a zero row
+  if (L == 0) {  // nothing to attend to: zero rows
     if (draw && tid == 0) ticket = take_ticket(p.work, p.epoch);
-    for (int idx = tid; idx < G * D; idx += kThreads)
-      store_out<Tag>(p, ((size_t)seq * p.num_heads + head0) * D + idx, 0.0f);
+    for (int idx = tid; idx < R * D; idx += kThreads) {
+      const int c = idx / D;
+      store_out<Tag>(p, row_of(c) * D + (idx - c * D), 0.0f);
+    }
     return;
   }
   const Cut c = cut_of(L, p.partition);
@@ -663,7 +684,8 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
 
   Eng eng;
   eng.init(lane);
-  eng.load_q(static_cast<const unsigned char*>(p.q) + ((size_t)seq * p.num_heads + head0) * RB, G);
+  eng.load_q(static_cast<const unsigned char*>(p.q) + row_of(eng.col < R ? eng.col : 0) * RB, eng.col < R);
+  eng.lim = eng.col < R ? L - p.q_len + eng.col / G : L - 1;
   eng.reset();
   __syncthreads();
 
@@ -699,12 +721,12 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   float* s_o = reinterpret_cast<float*>(smem);
   float* s_m = reinterpret_cast<float*>(smem + lds_main);
   float* s_l = s_m + kWaves * 16;
-  if (eng.col < G) {
+  if (eng.col < R) {
     if (eng.grp == 0) {
       s_m[wave * 16 + eng.col] = eng.m;
       s_l[wave * 16 + eng.col] = lsum;
     }
-    float* orow = s_o + (size_t)(wave * G + eng.col) * OST;
+    float* orow = s_o + (size_t)(wave * R + eng.col) * OST;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -712,10 +734,10 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   }
   __syncthreads();
 
-  for (int idx = tid; idx < G * D; idx += kThreads) {
+  for (int idx = tid; idx < R * D; idx += kThreads) {
     const int h = idx / D;
     const int d = idx - h * D;
-    float M = -INFINITY;
+    float M = kNoMax;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w * 16 + h]);
     float den = 0.0f, num = 0.0f;
@@ -723,11 +745,11 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
     for (int w = 0; w < kWaves; ++w) {
       const float sc = fast_exp2(s_m[w * 16 + h] - M);
       den += sc * s_l[w * 16 + h];
-      num += sc * s_o[(w * G + h) * OST + d];
+      num += sc * s_o[(w * R + h) * OST + d];
     }
-    const size_t row = (size_t)seq * p.num_heads + head0 + h;
+    const size_t row = row_of(h);
     if (nparts <= 1) {
-      store_out<Tag>(p, row * D + d, num / den);
+      store_out<Tag>(p, row * D + d, den > 0.0f ? num / den : 0.0f);  // 0: no position seen
     } else {
       // agent-scope stores: written through to where every XCD reads them
       const size_t pi = row * p.num_partitions + part;
@@ -754,22 +776,22 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   if (tid == 0) *s_last = take_ticket(p.arrive + (size_t)seq * p.num_kv_heads + kvh, p.epoch) == nparts - 1;
   __syncthreads();
   if (!*s_last) return;
-  for (int idx = tid; idx < G * D; idx += kThreads) {
+  for (int idx = tid; idx < R * D; idx += kThreads) {
     const int h = idx / D;
     const int d = idx - h * D;
-    const size_t row = (size_t)seq * p.num_heads + head0 + h;
+    const size_t row = row_of(h);
     const unsigned long long* ml =
         reinterpret_cast<const unsigned long long*>(p.ws_ml + 2 * row * p.num_partitions);
     const float* o = p.ws_o + row * p.num_partitions * D + d;
     // kMergeBatch partitions per round trip: every load of a batch is issued
     // before any is used; the running max moves between batches
-    float M = -INFINITY, den = 0.0f, num = 0.0f;
+    float M = kNoMax, den = 0.0f, num = 0.0f;
     for (int q0 = 0; q0 < nparts; q0 += kMergeBatch) {
       float mq[kMergeBatch], lq[kMergeBatch], oq[kMergeBatch];
 #pragma unroll
       for (int j = 0; j < kMergeBatch; ++j) {
         const int q = q0 + j;
-        mq[j] = -INFINITY;
+        mq[j] = kNoMax;
         lq[j] = oq[j] = 0.0f;
         if (q < nparts) {
           const unsigned long long pair = __hip_atomic_load(&ml[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -793,7 +815,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
         num += wq * oq[j];
       }
     }
-    store_out<Tag>(p, row * D + d, num / den);
+    store_out<Tag>(p, row * D + d, den > 0.0f ? num / den : 0.0f);
   }
 }
 
@@ -808,7 +830,7 @@ void decode_partition_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int wave = uniform(threadIdx.x >> 6);
   const int span = p.partition < p.max_seq_len ? p.partition : p.max_seq_len;
-  const int lds_main = lds_main_bytes(D, p.group, span, BS, TileEngine<Tag, D, BS>::KT_BYTES);
+  const int lds_main = lds_main_bytes(D, p.q_len * p.group, span, BS, TileEngine<Tag, D, BS>::KT_BYTES);
   // Two slots for the next item, used alternately: an item may pass no
   // barrier (a zero-length sequence), and a slot is rewritten only after the
   // barrier that follows every wave's read of it. The third int is the
@@ -882,7 +904,7 @@ template <class Tag, int D, int BS>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   const int span = p.partition < p.max_seq_len ? p.partition : p.max_seq_len;
   const void* kfn = reinterpret_cast<const void*>(&decode_partition_kernel<Tag, D, BS>);
-  const size_t q_row = (size_t)p.num_heads * D;
+  const size_t q_row = (size_t)p.q_len * p.num_heads * D;  // elements per sequence
   const size_t out_elem = p.out_f32 ? 4 : (size_t)Tag::kBytes;
   // Launches of at most `chunk` sequences each, in order on the stream; they
   // share the workspace (header, partials, arrival words). The chunk keeps the LDS of a
@@ -890,7 +912,7 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   // so that two workgroups fit per CU, when the rest of it leaves room.
   int chunk = kMaxSeqsPerLaunch;
   {
-    const int fixed = lds_total_bytes(D, p.group, span, BS, TileEngine<Tag, D, BS>::KT_BYTES, 0);
+    const int fixed = lds_total_bytes(D, p.q_len * p.group, span, BS, TileEngine<Tag, D, BS>::KT_BYTES, 0);
     const int room = (kLdsPerWorkgroup - fixed - 32) / 10;
     if (room < chunk) chunk = room > 256 ? room : 256;
   }
@@ -902,7 +924,8 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
     c.out = static_cast<unsigned char*>(p.out) + (size_t)s0 * q_row * out_elem;
     c.block_table = p.block_table + (size_t)s0 * p.max_blocks;
     c.seq_lens = p.seq_lens + s0;
-    const size_t lds = (size_t)lds_total_bytes(D, c.group, span, BS, TileEngine<Tag, D, BS>::KT_BYTES, c.num_seqs);
+    const size_t lds =
+        (size_t)lds_total_bytes(D, c.q_len * c.group, span, BS, TileEngine<Tag, D, BS>::KT_BYTES, c.num_seqs);
     const int64_t max_items = (int64_t)c.num_seqs * c.num_kv_heads * c.num_partitions;
     int64_t grid = resident_workgroups(kfn, lds);
     if (grid > max_items) grid = max_items;

@@ -21,6 +21,8 @@ struct DecodeParams {
   float* ws_ml;   // [S, H, NP, 2] (running max in log2 units, sum of weights)
   unsigned long long* arrive;  // [S, Hkv] (epoch << 32) | partitions done (split only)
   int num_seqs;
+  int q_len;           // new tokens per sequence (1: decode); query and out are
+                       // [S, q_len, H, D]; token j sees positions <= L - q_len + j
   int num_heads;
   int num_kv_heads;
   int group;           // num_heads / num_kv_heads

@@ -76,6 +76,50 @@ def test_decode_host_checks(kw, code):
     assert _decode(**kw) == code
 
 
+def _multi_query(**kw):
+    a = dict(out=FAKE, query=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, S=4, Q=4, H=32, Hkv=8,
+             D=128, bs=16, NB=100, MB=16, maxlen=256, scale=0.088, kvdt=2, outdt=2, P=0,
+             ws=None, wsb=0)
+    a.update(kw)
+    return _lib.lib().paged_attn_multi_query(a["out"], a["query"], a["k"], a["v"], a["bt"],
+                                             a["sl"], a["S"], a["Q"], a["H"], a["Hkv"], a["D"],
+                                             a["bs"], a["NB"], a["MB"], a["maxlen"], a["scale"],
+                                             a["kvdt"], a["outdt"], a["P"], a["ws"], a["wsb"],
+                                             None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S=0, out=None), OK),
+    (dict(Q=0), SHAPE),
+    (dict(Q=-3), SHAPE),
+    (dict(Q=5), UNSUP),                        # 5 tokens x 4 heads > 16 query rows
+    (dict(Q=2, H=8 * 9), UNSUP),               # 2 x 9
+    (dict(Q=2 ** 30, H=8), UNSUP),             # q_len * G would overflow int
+    (dict(Q=16, H=8), WS),                     # 16 x 1 rows: valid, but no workspace given
+    (dict(Q=2, H=8 * 8), WS),                  # 2 x 8 rows
+    (dict(out=None), NULL),
+    (dict(D=96), UNSUP),
+])
+def test_multi_query_host_checks(kw, code):
+    assert _multi_query(**kw) == code
+
+
+def test_multi_query_workspace_sizing():
+    L = _lib.lib()
+    hdr = 256
+    for args in [(64, 32, 8, 128, 16, 4039, 0), (256, 32, 8, 128, 8, 10000, 512),
+                 (4, 4, 4, 64, 16, 50, 16), (0, 32, 8, 128, 16, 4039, 0)]:
+        S, H, Hkv, D, bs, maxlen, P = args
+        assert (L.paged_attn_multi_query_workspace_size(S, 1, H, Hkv, D, bs, maxlen, P)
+                == L.paged_attn_workspace_size(*args))
+    # partials scale with the q_len * num_heads query rows; arrival words do not
+    assert (L.paged_attn_multi_query_workspace_size(256, 4, 32, 8, 128, 8, 10000, 512)
+            == hdr + 256 * 4 * 32 * 20 * (128 + 2) * 4 + 256 * 8 * 8)
+    assert L.paged_attn_multi_query_workspace_size(64, 2, 32, 8, 128, 16, 512, 512) == hdr
+    assert L.paged_attn_multi_query_workspace_size(64, 5, 32, 8, 128, 16, 4039, 0) == 0
+    assert L.paged_attn_multi_query_workspace_size(64, 0, 32, 8, 128, 16, 4039, 0) == 0
+
+
 def test_partition_and_workspace_sizing():
     L = _lib.lib()
     # partition_size 0: the library's choice
@@ -130,6 +174,9 @@ def test_binding_rejects_bad_tensors_before_the_library():
     sl = torch.zeros(2, dtype=torch.int32)
     with pytest.raises(ValueError):
         pkv.paged_attn_decode(torch.empty_like(q), q, kc, kc, bt, sl, 0.125, 10)
+    with pytest.raises(ValueError):                     # decode query given to multi_query
+        pkv.paged_attn_multi_query(torch.empty_like(q), q, kc, kc,
+                                   torch.zeros(2, 4, dtype=torch.int32), sl, 0.125, 10)
     with pytest.raises(ValueError):
         pkv.reshape_and_cache(torch.zeros(3, 4, 64), torch.zeros(3, 4, 64), kc, kc,
                               torch.zeros(3, dtype=torch.int32))

@@ -1,0 +1,192 @@
+"""GPU parity of paged_attn_multi_query (q_len new tokens per sequence,
+causal over the cached prefix) against the fp64 oracle's multi_query, through
+the C ABI. Bars as for decode: max-abs 1e-5 (fp32), 2e-3 (fp16), 8e-3 (bf16);
+rows of tokens that see no position are exactly zero; q_len = 1 is decode,
+bit for bit."""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_154_amd as pkv
+from paged_kv_cache_154_amd import workloads as W
+from gpu_common import DEV, TOL, max_err, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def mq_gpu(wl, d, out_dtype=None, partition_size=None, workspace=None, max_seq_len=None):
+    """The step's scatter of the q_len new tokens' K/V, then the multi-query pass."""
+    if "slots" in d:
+        pkv.reshape_and_cache(d["nk"], d["nv"], d["kc"], d["vc"], d["slots"])
+    out = torch.empty(wl.query.shape, dtype=out_dtype or wl.dtype, device=DEV)
+    P = wl.partition_size if partition_size is None else partition_size
+    pkv.paged_attn_multi_query(out, d["q"], d["kc"], d["vc"], d["bt"], d["sl"], wl.scale,
+                               max_seq_len or wl.max_seq_len, P, workspace=workspace)
+    torch.cuda.synchronize()
+    return out
+
+
+def mq_oracle(wl, seqs=None):
+    kc, vc = wl.key_cache, wl.value_cache
+    if wl.slot_mapping is not None:
+        kc, vc = oracle.reshape_and_cache(wl.new_key, wl.new_value, kc, vc, wl.slot_mapping)
+    return oracle.multi_query(wl.query, kc, vc, wl.block_table, wl.seq_lens, wl.scale, seqs=seqs)
+
+
+def _wl(name, dt, D, bs, H, Hkv, Q, lens, P, new_token=True, **kw):
+    return W.custom(zlib.crc32(name.encode()) % 10000 + 300, seq_lens=lens, num_heads=H,
+                    num_kv_heads=Hkv, head_dim=D, block_size=bs, dtype=dt, partition_size=P,
+                    new_token=new_token, q_len=Q, name=name, **kw)
+
+
+MQ_SMALL = [
+    # id, dtype, D, bs, H, Hkv, q_len, lens, partition
+    ("bf16_d128_bs16_g4_q4", torch.bfloat16, 128, 16, 32, 8, 4, [4, 5, 16, 17, 100, 513, 2000], 0),
+    ("f16_d128_bs32_g8_q2", torch.float16, 128, 32, 64, 8, 2, [2, 33, 64, 300, 1029], 0),
+    ("bf16_d64_bs8_g1_q16", torch.bfloat16, 64, 8, 4, 4, 16, [16, 17, 40, 700], 0),
+    ("f32_d64_bs16_g2_q8", torch.float32, 64, 16, 4, 2, 8, [8, 9, 50, 129], 0),
+    ("f32_d128_bs8_g1_q3", torch.float32, 128, 8, 2, 2, 3, [3, 90, 257], 0),
+    ("f16_d64_bs32_g5_q3", torch.float16, 64, 32, 10, 2, 3, [3, 31, 32, 33, 97], 0),
+    # partitions whose boundary falls among the new tokens: some tokens see
+    # nothing of the last partition, whose partial is then empty
+    ("bf16_d128_bs16_g4_q4_split64", torch.bfloat16, 128, 16, 32, 8, 4,
+     [4, 63, 64, 65, 66, 67, 130, 1500], 64),
+    ("f16_d128_bs8_g2_q8_split16", torch.float16, 128, 8, 16, 8, 8, [8, 15, 16, 17, 23, 24, 200], 16),
+    ("f32_d64_bs16_g1_q16_split16", torch.float32, 64, 16, 2, 2, 16, [16, 17, 31, 32, 33, 300], 16),
+    ("bf16_d64_bs32_g8_q2_split32", torch.bfloat16, 64, 32, 16, 2, 2, [2, 32, 33, 34, 1000], 32),
+]
+
+
+@pytest.mark.parametrize("case", MQ_SMALL, ids=[c[0] for c in MQ_SMALL])
+def test_multi_query_small_cases_match_oracle(case):
+    name, dt, D, bs, H, Hkv, Q, lens, P = case
+    wl = _wl(name, dt, D, bs, H, Hkv, Q, lens, P)
+    ref = mq_oracle(wl)
+    for out_dt in dict.fromkeys([dt, torch.float32]):
+        say(f"multi-query {name} out={out_dt}")
+        out = mq_gpu(wl, to_dev(wl), out_dtype=out_dt)
+        assert torch.isfinite(out).all()
+        err = max_err(out, ref)
+        assert err <= TOL[dt], (name, out_dt, err)
+
+
+@pytest.mark.parametrize("P", [0, 16])
+def test_multi_query_tokens_that_see_nothing_give_zero_rows(P):
+    """Sequences shorter than q_len (the cache already holds all L positions):
+    token j sees positions <= L - q_len + j, none at all when that is < 0."""
+    Q = 4
+    lens = [0, 1, 2, 3, 4, 5, 40]
+    wl = _wl(f"short_q4_P{P}", torch.bfloat16, 128, 16, 16, 4, Q, lens, P, new_token=False)
+    ref = mq_oracle(wl)
+    say(f"multi-query short sequences P={P}")
+    out = mq_gpu(wl, to_dev(wl), out_dtype=torch.float32)
+    for s, L in enumerate(lens):
+        for j in range(Q):
+            if L - Q + j < 0:
+                assert torch.equal(out[s, j].cpu(), torch.zeros_like(out[s, j].cpu())), (s, j)
+    assert torch.isfinite(out).all()
+    assert max_err(out, ref) <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("P", [0, 32])
+def test_multi_query_with_one_token_is_decode_bitwise(dt, P):
+    wl = W.custom(31, seq_lens=[1, 17, 33, 300, 1000], num_heads=16, num_kv_heads=4,
+                  head_dim=128, block_size=16, dtype=dt, new_token=False)
+    d = to_dev(wl)
+    say(f"multi-query q_len=1 vs decode {dt} P={P}")
+    dec = torch.empty(wl.query.shape, dtype=torch.float32, device=DEV)
+    pkv.paged_attn_decode(dec, d["q"], d["kc"], d["vc"], d["bt"], d["sl"], wl.scale,
+                          wl.max_seq_len, P)
+    q4 = d["q"].unsqueeze(1).contiguous()
+    mq = torch.empty(q4.shape, dtype=torch.float32, device=DEV)
+    pkv.paged_attn_multi_query(mq, q4, d["kc"], d["vc"], d["bt"], d["sl"], wl.scale,
+                               wl.max_seq_len, P)
+    torch.cuda.synchronize()
+    assert torch.equal(mq[:, 0].view(torch.int32), dec.view(torch.int32))
+
+
+def test_multi_query_rows_are_decodes_of_their_prefixes():
+    """Token j of a sequence of length L gives what a decode over the first
+    L - q_len + j + 1 positions gives for its query, to fp32 rounding (the
+    other rows of the tile may move the running max at other times): the
+    causal limit is the only difference between the rows. A limit off by one
+    position moves a row by far more than the bar."""
+    Q, lens = 4, [7, 64, 65, 200]
+    wl = _wl("prefix_rows", torch.float16, 128, 16, 32, 8, Q, lens, 0, new_token=False)
+    d = to_dev(wl)
+    out = mq_gpu(wl, d, out_dtype=torch.float32)
+    for j in range(Q):
+        sl_j = (d["sl"] - Q + j + 1).to(torch.int32)
+        dec = torch.empty((len(lens),) + tuple(wl.query.shape[2:]), dtype=torch.float32,
+                          device=DEV)
+        say(f"multi-query row {j} vs decode of its prefix")
+        pkv.paged_attn_decode(dec, d["q"][:, j].contiguous(), d["kc"], d["vc"], d["bt"], sl_j,
+                              wl.scale, wl.max_seq_len, 0)
+        torch.cuda.synchronize()
+        assert (out[:, j] - dec).abs().max().item() <= 1e-5, j
+
+
+def test_multi_query_workspace_garbage_and_reuse():
+    """The workspace needs no initialisation; one buffer, filled with garbage
+    before each call, serves decode and multi-query calls of different q_len
+    and partitions in turn."""
+    a = _wl("ws_a", torch.bfloat16, 128, 16, 32, 8, 4, [4, 300, 1300, 64, 9], 0)
+    b = _wl("ws_b", torch.float16, 64, 8, 8, 8, 16, [16, 40, 700], 0)
+    c = W.custom(33, seq_lens=[5, 700, 1300], num_heads=16, num_kv_heads=4, head_dim=128,
+                 block_size=16, dtype=torch.bfloat16, new_token=False)
+    ws = torch.empty(1 << 23, dtype=torch.uint8, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(6)
+    refs = {"a": mq_oracle(a), "b": mq_oracle(b),
+            "c": oracle.decode(c.query, c.key_cache, c.value_cache, c.block_table, c.seq_lens,
+                               c.scale)}
+    wls = {"a": a, "b": b, "c": c}
+    for i, (k, P) in enumerate([("a", 64), ("b", 32), ("c", 64), ("a", 0), ("b", 16), ("a", 64)]):
+        wl = wls[k]
+        if k == "c":
+            need = pkv.paged_attn_workspace_size(wl.num_seqs, wl.num_heads, wl.num_kv_heads,
+                                                 wl.head_dim, wl.block_size, wl.max_seq_len, P)
+        else:
+            need = pkv.paged_attn_multi_query_workspace_size(
+                wl.num_seqs, wl.q_len, wl.num_heads, wl.num_kv_heads, wl.head_dim,
+                wl.block_size, wl.max_seq_len, P)
+        assert need <= ws.numel()
+        if i % 2:
+            ws.fill_(0xFF)
+        else:
+            ws.copy_(torch.randint(0, 256, ws.shape, generator=g, device=DEV, dtype=torch.uint8))
+        say(f"shared workspace {k} P={P}")
+        d = to_dev(wl)
+        if k == "c":
+            out = torch.empty(wl.query.shape, dtype=torch.float32, device=DEV)
+            pkv.paged_attn_decode(out, d["q"], d["kc"], d["vc"], d["bt"], d["sl"], wl.scale,
+                                  wl.max_seq_len, P, workspace=ws)
+            torch.cuda.synchronize()
+        else:
+            out = mq_gpu(wl, d, out_dtype=torch.float32, partition_size=P, workspace=ws)
+        assert max_err(out, refs[k]) <= TOL[wl.dtype], (k, P)
+
+
+@pytest.mark.parametrize("P", [0, 512])
+def test_multi_query_llama3_8b_shaped_verification(P):
+    """Speculative verification at the Llama-3-8B shape: 64 sequences of
+    512-4096 tokens, 32 query heads on 8 KV heads, head_dim 128, bf16,
+    16-token blocks, 4 new tokens per sequence (4 x 4 = 16 query rows per KV
+    head: one full MFMA tile). Sampled sequences against the oracle."""
+    rng = np.random.default_rng(4401)
+    lens = rng.integers(512, 4097, size=64).tolist()
+    wl = _wl("llama3_8b_q4", torch.bfloat16, 128, 16, 32, 8, 4, lens, P)
+    order = np.argsort(lens)
+    seqs = sorted(set(order[:4].tolist() + order[-4:].tolist() + [5, 17, 33, 50]))
+    ref = mq_oracle(wl, seqs=seqs)
+    say(f"multi-query Llama-3-8B shape q_len=4 P={P}")
+    for out_dt in (torch.float32, torch.bfloat16):
+        out = mq_gpu(wl, to_dev(wl), out_dtype=out_dt)
+        assert torch.isfinite(out).all()
+        err = max_err(out, ref, seqs)
+        say(f"  out={out_dt} max_abs_err={err:.3g} on {len(seqs)} seqs")
+        assert err <= TOL[torch.bfloat16], (out_dt, err)
