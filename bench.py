@@ -23,9 +23,13 @@ placement of the same blocks. ``--per-config`` adds every page-shaped
 workload (the Llama-3-8B and Llama-2-70B layers, the prefix-sharing batch
 and the mixed batch with split sequences): decode calls timed cold, with
 p10/p50/p90, and the scatter and block copy of each step.
+``--multi-query`` adds the verification pass of speculative decoding (q_len
+2, 4 and 8 new tokens per sequence, causal) on the same lengths, beside decode;
+``--q-len Q`` makes that pass, with its scatter of 64 x Q tokens, the timed
+step itself (the profile of it then covers that pass alone).
 
     python bench.py [--steps K] [--warmup W] [--layers N] [--no-cpu-baseline] [--secondary]
-                    [--per-config]
+                    [--per-config] [--multi-query] [--q-len Q]
 """
 
 import argparse
@@ -53,10 +57,11 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per decode call from the committed rocprofv3 counter runs,
-    or None when the kernel sources changed after those runs."""
-    path = os.path.join(ROOT, "profiles", "decode_llama3_8b_bf16_traffic.json")
+def measured_traffic(name="decode_llama3_8b_bf16"):
+    """HBM bytes per attention call from the committed rocprofv3 counter runs
+    of this workload, or None when there are none or the kernel sources
+    changed after them."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     try:
         with open(path) as fh:
             doc = json.load(fh)
@@ -102,8 +107,10 @@ def stream_read_peak(dev, gib=4, reps=8):
 
 def time_decode(pkv, wl, dev, layers=2, calls=20, P=0):
     """Median decode-call time (us) of a workload: calls queued back to back
-    (as in the timed steps), rotating over layer copies of the pools."""
+    (as in the timed steps), rotating over layer copies of the pools. A
+    workload with several new tokens per sequence runs the multi-query pass."""
     import torch
+    attn = pkv.paged_attn_decode if wl.q_len == 1 else pkv.paged_attn_multi_query
     q = wl.query.to(dev)
     bt = torch.from_numpy(wl.block_table).to(dev)
     sl = torch.from_numpy(wl.seq_lens).to(dev)
@@ -116,14 +123,14 @@ def time_decode(pkv, wl, dev, layers=2, calls=20, P=0):
     ws = pkv.workspace_for(q, kc0, wl.max_seq_len, P)
     for i in range(4):
         kc, vc = pools[i % layers]
-        pkv.paged_attn_decode(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
+        attn(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(calls)]
     torch.cuda.synchronize()
     for i in range(calls):
         kc, vc = pools[i % layers]
         ev[i][0].record()
-        pkv.paged_attn_decode(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
+        attn(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
         ev[i][1].record()
     torch.cuda.synchronize()
     del pools
@@ -170,6 +177,30 @@ def secondary(pkv, W, base, dev):
                         "paged_over_contiguous": round(t_paged / t_contig, 4)}
     log(f"placement: paged {t_paged:.1f} us, contiguous {t_contig:.1f} us")
     return out
+
+
+def multi_query_rows(pkv, W, base, dev, q_lens=(2, 4, 8)):
+    """The verification pass of speculative decoding on the Llama-3-8B-shaped
+    lengths and placement of the decode step:
+    q_len new tokens per sequence (their K/V scattered first), each KV head's
+    blocks read once for all q_len x G query rows. Back-to-back medians beside
+    decode of the same batch; KV GB/s over the same pool bytes."""
+    import torch
+    G = base.num_heads // base.num_kv_heads
+    t_dec = time_decode(pkv, base, dev, calls=40)
+    rows = {"decode_us": round(t_dec, 1)}
+    for Q in q_lens:
+        if Q * G > 128:
+            continue
+        wl = W.llama3_8b(q_len=Q)
+        t = time_decode(pkv, wl, dev, calls=40)
+        rows[f"q_len={Q}"] = {"us": round(t, 1), "kv_GBps": round(wl.kv_bytes() / t / 1e3, 1),
+                              "over_decode": round(t / t_dec, 3),
+                              "tokens_per_s": round(Q * wl.num_seqs / (t * 1e-6), 1)}
+        log(f"multi-query q_len={Q}: {t:.1f} us (decode {t_dec:.1f} us)")
+        del wl
+        torch.cuda.empty_cache()
+    return rows
 
 
 def _events(n):
@@ -290,7 +321,7 @@ def per_config(pkv, W, dev, calls=200, warm=20):
 
 
 def cpu_baseline(wl, budget_s=20.0):
-    """The CPU oracle on the same step (scatter + decode of every sequence),
+    """The CPU oracle on the same step (scatter + attention of every sequence),
     wall clock, median over repeats within about budget_s seconds."""
     import torch
 
@@ -300,7 +331,10 @@ def cpu_baseline(wl, budget_s=20.0):
         t0 = time.perf_counter()
         kc, vc = oracle.reshape_and_cache(wl.new_key, wl.new_value, wl.key_cache,
                                           wl.value_cache, wl.slot_mapping)
-        oracle.decode(wl.query, kc, vc, wl.block_table, wl.seq_lens, wl.scale)
+        if wl.q_len == 1:
+            oracle.decode(wl.query, kc, vc, wl.block_table, wl.seq_lens, wl.scale)
+        else:
+            oracle.multi_query(wl.query, kc, vc, wl.block_table, wl.seq_lens, wl.scale)
         times.append(time.perf_counter() - t0)
         log(f"cpu oracle step {len(times)}: {times[-1]:.2f} s")
     t = statistics.median(times)
@@ -308,7 +342,7 @@ def cpu_baseline(wl, budget_s=20.0):
             "cores": torch.get_num_threads(), "kind": "oracle",
             "sample": (f"the whole step of the same workload ({wl.num_seqs} sequences, "
                        f"{wl.num_tokens} tokens: oracle scatter of the new tokens + fp64 "
-                       f"decode), median of {len(times)} run(s), {t:.2f} s per step"),
+                       f"{'decode' if wl.q_len == 1 else f'multi-query, q_len {wl.q_len}'}), median of {len(times)} run(s), {t:.2f} s per step"),
             "seconds_per_step": round(t, 3),
             "seqs_per_s": round(wl.num_seqs / t, 3)}
 
@@ -325,6 +359,12 @@ def main():
                     help="skip measuring the streaming-read rate")
     ap.add_argument("--secondary", action="store_true",
                     help="add the block-size sweep and the placement comparison")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="new tokens per sequence in the timed step: >1 times the "
+                         "multi-query (speculative verification) pass instead of decode")
+    ap.add_argument("--multi-query", action="store_true",
+                    help="also time the multi-query (speculative verification) pass, "
+                         "q_len 2, 4 and 8, on the same lengths")
     ap.add_argument("--per-config", action="store_true",
                     help="add cold-cache timings of every page-shaped workload")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -352,9 +392,12 @@ def main():
         log("copied 1 GiB x 10")
         return
     log("generating workload (Llama-3-8B-shaped layer)")
-    wl = W.llama3_8b()
+    Q = args.q_len
+    wl = W.llama3_8b(q_len=Q)
     P = wl.partition_size if args.partition_size is None else args.partition_size
-    S, H, D = wl.query.shape
+    S, H, D = wl.num_seqs, wl.num_heads, wl.head_dim
+    attn = pkv.paged_attn_decode if Q == 1 else pkv.paged_attn_multi_query
+    attn_name = "paged_attn_decode" if Q == 1 else f"paged_attn_multi_query (q_len {Q})"
     NB, bs, Hkv, _ = wl.key_cache.shape
 
     q = wl.query.to(dev)
@@ -364,7 +407,7 @@ def main():
     slots = torch.from_numpy(wl.slot_mapping).to(dev)
     kc0, vc0 = wl.key_cache.to(dev), wl.value_cache.to(dev)
     layers = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(args.layers - 1)]
-    out = torch.empty(S, H, D, dtype=wl.dtype, device=dev)
+    out = torch.empty(wl.query.shape, dtype=wl.dtype, device=dev)
     ws = pkv.workspace_for(q, kc0, wl.max_seq_len, P)
     part_tokens = pkv.paged_attn_partition_tokens(S, Hkv, bs, wl.max_seq_len, P)
     stream = torch.cuda.current_stream(dev)
@@ -372,7 +415,7 @@ def main():
     def step(i):
         kc, vc = layers[i % len(layers)]
         pkv.reshape_and_cache(nk, nv, kc, vc, slots)
-        pkv.paged_attn_decode(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
+        attn(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
@@ -391,7 +434,7 @@ def main():
         kc, vc = layers[i % len(layers)]
         pkv.reshape_and_cache(nk, nv, kc, vc, slots)
         ev[i][0].record(stream)
-        pkv.paged_attn_decode(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
+        attn(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
         ev[i][1].record(stream)
     t_stop.record(stream)
     torch.cuda.synchronize()
@@ -408,14 +451,14 @@ def main():
     # and dispatch latency to each call; this is closer to the kernel time.
     for i in range(args.warmup):
         kc, vc = layers[i % len(layers)]
-        pkv.paged_attn_decode(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
+        attn(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
     b0 = torch.cuda.Event(enable_timing=True)
     b1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     b0.record(stream)
     for i in range(args.steps):
         kc, vc = layers[i % len(layers)]
-        pkv.paged_attn_decode(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
+        attn(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
     b1.record(stream)
     torch.cuda.synchronize()
     dec_bb = b0.elapsed_time(b1) / args.steps
@@ -438,12 +481,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "llama3_8b_bf16: Llama-3-8B-shaped single-layer decode",
+            "workload": ("llama3_8b_bf16: Llama-3-8B-shaped single-layer decode" if Q == 1 else
+                         f"llama3_8b_bf16_q{Q}: Llama-3-8B-shaped single-layer verification "
+                         f"of {Q} new tokens per sequence"),
             "num_seqs": S, "num_heads": H, "num_kv_heads": Hkv, "head_dim": D,
             "block_size": bs, "num_blocks": NB, "seq_lens": "uniform [512, 4096], seed 1542",
             "tokens": wl.num_tokens, "kv_bytes_per_step": kv,
             "partition_tokens": part_tokens, "layers_rotated": len(layers),
-            "step": "reshape_and_cache(64 new tokens) + paged_attn_decode",
+            "step": f"reshape_and_cache({S * Q} new tokens) + {attn_name}",
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seqs_per_s_per_layer": round(S / (ms_step * 1e-3), 1),
@@ -458,8 +503,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(),
-            "kernel": "paged_attn_decode (decode_partition_kernel)",
+            "traffic": measured_traffic("decode_llama3_8b_bf16" if Q == 1 else
+                                        f"multi_query_q{Q}_llama3_8b_bf16"),
+            "kernel": f"{attn_name} (decode_partition_kernel)",
         },
         "cpu_baseline": None,
     }
@@ -468,10 +514,13 @@ def main():
         peak = stream_read_peak(dev)
         res["measured_stream_read_GBps"] = round(peak, 1)
         res["roofline"]["frac_of_measured_stream_read"] = round(achieved / peak, 4)
-    if args.secondary:
+    if args.secondary or args.multi_query:
         del layers
         torch.cuda.empty_cache()
+    if args.secondary:
         res["secondary"] = secondary(pkv, W, wl, dev)
+    if args.multi_query:
+        res["multi_query"] = multi_query_rows(pkv, W, wl, dev)
     if args.per_config:
         res["per_config"] = per_config(pkv, W, dev)
     if not args.no_cpu_baseline:

@@ -13,6 +13,9 @@
  *     dense and row-major; no strides. The caller allocates and owns all of
  *     it, including the split-K workspace. The library allocates nothing and
  *     keeps no state between calls; calls are reentrant.
+ *   - Query, output, key/value rows, pools and the workspace move in 16-byte
+ *     vector accesses: those pointers must be 16-byte aligned (every torch
+ *     or hipMalloc allocation is), else the call returns PKV_ERR_SHAPE.
  *   - Work is enqueued on `stream` (NULL = the default stream) and the call
  *     returns without waiting for it.
  *   - Return value: PKV_OK (0) or a negative pkv_status. Arguments are
@@ -49,7 +52,7 @@ enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 };
 enum pkv_status {
   PKV_OK = 0,
   PKV_ERR_NULL = -1,        /* a required pointer is NULL */
-  PKV_ERR_SHAPE = -2,       /* inconsistent or negative sizes */
+  PKV_ERR_SHAPE = -2,       /* inconsistent or negative sizes, or a misaligned pointer */
   PKV_ERR_UNSUPPORTED = -3, /* valid but not built: dtype, head_dim, block_size, group size */
   PKV_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
   PKV_ERR_HIP = -5          /* the HIP runtime reported an error at launch */
@@ -130,8 +133,9 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache,
  * no position (L < q_len) gives a zero row. q_len = 1 is paged_attn_decode.
  *
  *   out, query   [num_seqs, q_len, num_heads, head_dim]
- *   q_len        1 .. 16 / (num_heads / num_kv_heads) (the q_len * G query
- *                rows of a KV head share one 16-column MFMA tile)
+ *   q_len        1 .. 128 / (num_heads / num_kv_heads): the q_len * G query
+ *                rows of a KV head fill 16-column MFMA tiles, one per group
+ *                of waves (up to 8 groups); beyond that PKV_ERR_UNSUPPORTED
  *   workspace    at least paged_attn_multi_query_workspace_size(...) bytes
  * All other arguments, the partitioning, the status codes and the
  * workspace rules are those of paged_attn_decode.

@@ -27,6 +27,13 @@ bool supported_block_size(int bs) { return bs == 8 || bs == 16 || bs == 32; }
 
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 
+// Rows and quads of rows move in 16-byte vector accesses.
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+// Query rows (q_len x group) one KV head's workgroup takes: a tile of 16 MFMA
+// columns per wave.
+constexpr int kMaxQueryRows = 16 * pkv::kWaves;
+
 // Partition length chosen when partition_size is 0. A workgroup (8 waves)
 // handles one (sequence, KV head, partition); 512 fit on the GPU at once (256
 // CUs, 2 each). Measured on MI355X: with >= 2048 (sequence, KV head) pairs and
@@ -79,7 +86,8 @@ Cutting cutting_for(int max_seq_len, int block_size, int P) {
 
 // Workspace layout: a 256-byte header (the partition kernel's item counter,
 // tagged with the launch's epoch), then, when sequences are split, fp32 O partials
-// [S', H, NP, D], (m, l) pairs [S', H, NP, 2] and one 64-bit arrival word per
+// [S', q_len, H, NP, D] (the D values of one partial in the kernel's own
+// order), (m, l) pairs [S', q_len, H, NP, 2] and one 64-bit arrival word per
 // (sequence, KV head) [S', Hkv] (also epoch-tagged), for S' = min(S, the
 // sequences of one launch); launches run in order and reuse them.
 constexpr size_t kHeaderBytes = 256;
@@ -122,8 +130,9 @@ int attention(void* out, const void* query, const void* key_cache, const void* v
     return PKV_ERR_NULL;
   if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
   const int group = num_heads / num_kv_heads;
-  // the q_len * group query rows of a KV head fill at most one 16-column MFMA tile
-  if (group > 16 || q_len > 16 || q_len * group > 16) return PKV_ERR_UNSUPPORTED;
+  // the q_len * group query rows of a KV head: at most one 16-column MFMA tile
+  // per wave of a workgroup
+  if (group > 16 || q_len > kMaxQueryRows || q_len * group > kMaxQueryRows) return PKV_ERR_UNSUPPORTED;
   if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
   if (elem_bytes(kv_dtype) == 0) return PKV_ERR_UNSUPPORTED;
   if (out_dtype != kv_dtype && out_dtype != PKV_F32) return PKV_ERR_UNSUPPORTED;
@@ -141,6 +150,9 @@ int attention(void* out, const void* query, const void* key_cache, const void* v
   if ((int64_t)s_launch * num_kv_heads * np > (int64_t)INT32_MAX - (1 << 24)) return PKV_ERR_SHAPE;
   const size_t need = workspace_bytes_for(num_seqs, q_len * num_heads, num_kv_heads, head_dim, np);
   if (workspace == nullptr || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+  if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
+      !aligned16(workspace))
+    return PKV_ERR_SHAPE;
 
   pkv::DecodeParams p{};
   p.out = out;
@@ -176,7 +188,9 @@ int attention(void* out, const void* query, const void* key_cache, const void* v
 size_t workspace_size(int num_seqs, int q_len, int num_heads, int num_kv_heads, int head_dim,
                       int block_size, int max_seq_len, int partition_size) {
   if (num_seqs <= 0 || q_len < 1 || num_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return 0;
-  if (num_heads % num_kv_heads != 0 || q_len > 16 || q_len * (num_heads / num_kv_heads) > 16) return 0;
+  if (num_heads % num_kv_heads != 0 || q_len > kMaxQueryRows ||
+      q_len * (num_heads / num_kv_heads) > kMaxQueryRows)
+    return 0;
   if (!supported_head_dim(head_dim)) return 0;
   const int P = resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
   if (P < 0) return 0;
@@ -229,6 +243,8 @@ int reshape_and_cache(const void* key, const void* value, void* key_cache, void*
   if (num_tokens < 0) return PKV_ERR_SHAPE;
   if (num_tokens == 0) return PKV_OK;
   if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PKV_ERR_NULL;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+    return PKV_ERR_SHAPE;
   if (num_kv_heads <= 0 || num_blocks <= 0) return PKV_ERR_SHAPE;
   if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
   const int eb = elem_bytes(dtype);
@@ -247,6 +263,7 @@ int copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping
   if (num_pairs < 0) return PKV_ERR_SHAPE;
   if (num_pairs == 0) return PKV_OK;
   if (!key_cache || !value_cache || !block_mapping) return PKV_ERR_NULL;
+  if (!aligned16(key_cache) || !aligned16(value_cache)) return PKV_ERR_SHAPE;
   if (num_kv_heads <= 0 || num_blocks <= 0) return PKV_ERR_SHAPE;
   if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
   const int eb = elem_bytes(dtype);
@@ -276,7 +293,7 @@ int pagedkv_stream_read(const void* src, size_t bytes, uint32_t* sink, int grid,
   if (grid < 0) return PKV_ERR_SHAPE;
   if (bytes == 0) return PKV_OK;
   if (!src || !sink) return PKV_ERR_NULL;
-  if (bytes % 16 != 0 || grid == 0) return PKV_ERR_SHAPE;
+  if (bytes % 16 != 0 || grid == 0 || !aligned16(src)) return PKV_ERR_SHAPE;
   const hipError_t e = pkv::launch_stream_read(src, bytes, sink, grid, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
@@ -285,7 +302,7 @@ const char* pagedkv_status_string(int status) {
   switch (status) {
     case PKV_OK: return "PKV_OK";
     case PKV_ERR_NULL: return "PKV_ERR_NULL: a required pointer is NULL";
-    case PKV_ERR_SHAPE: return "PKV_ERR_SHAPE: inconsistent or negative sizes";
+    case PKV_ERR_SHAPE: return "PKV_ERR_SHAPE: inconsistent or negative sizes, or a misaligned pointer";
     case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED: dtype, head_dim, block_size or group size not built";
     case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE: split-K workspace missing or too small";
     case PKV_ERR_HIP: return "PKV_ERR_HIP: the HIP runtime reported a launch error";

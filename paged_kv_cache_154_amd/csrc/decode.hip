@@ -57,6 +57,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 namespace pkv {
@@ -89,6 +90,9 @@ struct KV<F32Tag> {
   __device__ static inline void store(void* out, size_t i, float x) {
     static_cast<float*>(out)[i] = x;
   }
+  __device__ static inline void store4(void* out, size_t i, float4 x) {
+    *reinterpret_cast<float4*>(static_cast<float*>(out) + i) = x;
+  }
 };
 
 template <>
@@ -105,6 +109,13 @@ struct KV<F16Tag> {
   __device__ static inline void store(void* out, size_t i, float x) {
     static_cast<_Float16*>(out)[i] = static_cast<_Float16>(x);
   }
+  __device__ static inline void store4(void* out, size_t i, float4 x) {
+    const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(x.x)) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(x.y)) << 16);
+    const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<_Float16>(x.z)) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(x.w)) << 16);
+    *reinterpret_cast<uint2*>(static_cast<_Float16*>(out) + i) = make_uint2(lo, hi);
+  }
 };
 
 template <>
@@ -120,6 +131,13 @@ struct KV<BF16Tag> {
   }
   __device__ static inline void store(void* out, size_t i, float x) {
     static_cast<__bf16*>(out)[i] = static_cast<__bf16>(x);
+  }
+  __device__ static inline void store4(void* out, size_t i, float4 x) {
+    const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x.x)) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x.y)) << 16);
+    const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x.z)) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x.w)) << 16);
+    *reinterpret_cast<uint2*>(static_cast<__bf16*>(out) + i) = make_uint2(lo, hi);
   }
 };
 
@@ -157,6 +175,27 @@ __device__ inline void store_out(const DecodeParams& p, size_t i, float x) {
     KV<Tag>::store(p.out, i, x);
   }
 }
+
+// Elements i .. i+3 of out (i a multiple of 4).
+template <class Tag>
+__device__ inline void store_out4(const DecodeParams& p, size_t i, float4 x) {
+  if (p.out_f32) {
+    KV<F32Tag>::store4(p.out, i, x);
+  } else {
+    KV<Tag>::store4(p.out, i, x);
+  }
+}
+
+// (a, b) as one 8-byte word, a in the low half, and back.
+__device__ inline unsigned long long pack2(float a, float b) {
+  return (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
+}
+__device__ inline float lo_of(unsigned long long w) { return __uint_as_float((uint32_t)w); }
+__device__ inline float hi_of(unsigned long long w) { return __uint_as_float((uint32_t)(w >> 32)); }
+
+// MFMA column tiles of 16 query rows for R rows per KV head, one per group of
+// waves: 1, 2, 4 or 8 (R <= 16 * kWaves).
+__host__ __device__ inline int col_tiles(int R) { return R <= 16 ? 1 : R <= 32 ? 2 : R <= 64 ? 4 : 8; }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -232,8 +271,9 @@ struct TileEngine {
 
   // One tile of tokens cs .. cs+15 (cs a multiple of 16, cs <= t_last).
   // row_off(t) is the byte offset of token t's row for this KV head (t <= t_last);
-  // kt is the wave's LDS tile (KT_BYTES); nt selects non-temporal loads.
-  template <bool nt, class RowOff>
+  // kt is the wave's LDS tile (KT_BYTES); nt selects non-temporal loads;
+  // causal applies the column's own limit `lim` as well (several new tokens).
+  template <bool nt, bool causal, class RowOff>
   __device__ void step(const unsigned char* kbase, const unsigned char* vbase, int cs, int t_last,
                        uint32_t slot_bytes, float scale_log2, RowOff row_off, unsigned char* kt) {
     uint4 kr[NKL];
@@ -284,7 +324,7 @@ struct TileEngine {
 #pragma unroll
     for (int i = 0; i < NKL; ++i) a = Tr::qk(kr[i], qv[i], a);
     float s[4];
-    const int last = min(t_last, lim);
+    const int last = causal ? min(t_last, lim) : t_last;
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[r] = (cs + 4 * grp + r) <= last ? a[r] * scale_log2 : -INFINITY;
 
@@ -607,9 +647,9 @@ __device__ inline void install_epoch(unsigned long long* word, uint32_t epoch) {
 // waves' K tiles, reused for the waves' O rows (and at the start for the
 // plan's scan); then the waves' (m, l); then the next item; then the plan.
 __host__ __device__ inline int bt_lds_bytes(int span, int BS) { return ((span / BS + 1) * 4 + 15) & ~15; }
-// R: query rows per KV head (q_len * G).
+// R: query rows per KV head (q_len * G); a wave keeps at most 16 of them.
 __host__ __device__ inline int lds_main_bytes(int D, int R, int span, int BS, int kt_bytes) {
-  const int o_bytes = kWaves * R * o_stride(D) * 4;
+  const int o_bytes = kWaves * (R < 16 ? R : 16) * o_stride(D) * 4;
   const int tile_bytes = bt_lds_bytes(span, BS) + kWaves * kt_bytes;
   return ((o_bytes > tile_bytes ? o_bytes : tile_bytes) + 15) & ~15;
 }
@@ -632,20 +672,25 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   using Eng = TileEngine<Tag, D, BS>;
   constexpr int RB = Eng::RB;
   constexpr int VPL = Eng::VPL;
+  constexpr int DQ = D / 4;  // quads (4 consecutive head-dim elements) per row
   const int G = p.group;
   const int R = p.q_len * G;  // query rows of this KV head: (token j, head g) -> j * G + g
   const int head0 = kvh * G;
+  // new token of query row c, c / G, as a multiply and a shift (exact for
+  // every c < 128 and G <= 16): no division before the query load of an item
+  const int g_inv = (2048 + G - 1) / G;
+  auto token_of = [&](int c) { return (c * g_inv) >> 11; };
   // global row of query row c: [S, q_len, H] flattened
   auto row_of = [&](int c) -> size_t {
-    const int j = c / G;
+    const int j = token_of(c);
     return ((size_t)seq * p.q_len + j) * p.num_heads + head0 + (c - j * G);
   };
 
   if (L == 0) {  // nothing to attend to: zero rows
     if (draw && tid == 0) ticket = take_ticket(p.work, p.epoch);
-    for (int idx = tid; idx < R * D; idx += kThreads) {
-      const int c = idx / D;
-      store_out<Tag>(p, row_of(c) * D + (idx - c * D), 0.0f);
+    for (int qi = tid; qi < R * DQ; qi += kThreads) {
+      const int r = qi / DQ;
+      store_out4<Tag>(p, row_of(r) * D + 4 * (qi - r * DQ), make_float4(0.f, 0.f, 0.f, 0.f));
     }
     return;
   }
@@ -682,10 +727,22 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
     if (seq + 1 < p.num_seqs) shared |= mine[p.max_blocks] == b0;
   }
 
+  // Column groups: with more than 16 query rows the rows are cut into tiles
+  // of 16 MFMA columns and the waves into as many groups; the waves of group
+  // g keep rows 16 g .. 16 g + 15 and share out the key tiles among
+  // themselves, so every group reads every key tile (once from HBM, then
+  // from L2: those loads are cached).
+  const int nct = col_tiles(R);
+  const int wpg = kWaves / nct;  // waves per group
+  const int cgroup = wave / wpg;
+  const int wi = wave - cgroup * wpg;
+  const int RW = R < 16 ? R : 16;  // rows per wave
   Eng eng;
   eng.init(lane);
-  eng.load_q(static_cast<const unsigned char*>(p.q) + row_of(eng.col < R ? eng.col : 0) * RB, eng.col < R);
-  eng.lim = eng.col < R ? L - p.q_len + eng.col / G : L - 1;
+  const int myrow = 16 * cgroup + eng.col;
+  const bool valid = myrow < R;
+  eng.load_q(static_cast<const unsigned char*>(p.q) + row_of(valid ? myrow : 0) * RB, valid);
+  eng.lim = valid ? L - p.q_len + token_of(myrow) : L - 1;
   eng.reset();
   __syncthreads();
 
@@ -701,12 +758,19 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
     const uint32_t phys = (uint32_t)s_bt[u / BS - (uint32_t)lb0];
     return (uint64_t)(phys * BS + (u % BS)) * slot_bytes;
   };
-  if (shared) {
-    for (int cs = t_begin + wave * kTile; cs < t_end; cs += kWaves * kTile)
-      eng.template step<false>(kbase, vbase, cs, t_end - 1, slot_bytes, p.scale_log2, row_off, kt);
+  // the loop is compiled four ways (load kind x causal limit), chosen per item
+  auto tiles = [&](auto nt, auto causal) {
+    for (int cs = t_begin + wi * kTile; cs < t_end; cs += wpg * kTile)
+      eng.template step<decltype(nt)::value, decltype(causal)::value>(kbase, vbase, cs, t_end - 1, slot_bytes,
+                                                                      p.scale_log2, row_off, kt);
+  };
+  using Yes = std::true_type;
+  using No = std::false_type;
+  const bool cached = shared || nct > 1;
+  if (p.q_len == 1) {
+    if (cached) tiles(No{}, No{}); else tiles(Yes{}, No{});
   } else {
-    for (int cs = t_begin + wave * kTile; cs < t_end; cs += kWaves * kTile)
-      eng.template step<true>(kbase, vbase, cs, t_end - 1, slot_bytes, p.scale_log2, row_off, kt);
+    if (cached) tiles(No{}, Yes{}); else tiles(Yes{}, Yes{});
   }
 
   // ---- merge the waves ---------------------------------------------------
@@ -721,12 +785,12 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   float* s_o = reinterpret_cast<float*>(smem);
   float* s_m = reinterpret_cast<float*>(smem + lds_main);
   float* s_l = s_m + kWaves * 16;
-  if (eng.col < R) {
+  if (valid) {
     if (eng.grp == 0) {
       s_m[wave * 16 + eng.col] = eng.m;
       s_l[wave * 16 + eng.col] = lsum;
     }
-    float* orow = s_o + (size_t)(wave * R + eng.col) * OST;
+    float* orow = s_o + (size_t)(wave * RW + eng.col) * OST;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -734,30 +798,57 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   }
   __syncthreads();
 
-  for (int idx = tid; idx < R * D; idx += kThreads) {
-    const int h = idx / D;
-    const int d = idx - h * D;
+  // One quad of one row per thread and pass: the group's waves combined with
+  // one scale factor per wave. Straight-line code (a wave past the group's
+  // end is read at the group's first and weighted 0), so that every LDS read
+  // of the pass is issued at once.
+  for (int qi = tid; qi < R * DQ; qi += kThreads) {
+    const int r = qi / DQ;
+    const int qd = qi - r * DQ;  // quad within the row
+    const int d = 4 * qd;
+    const int col = r & 15;
+    const int w0 = (r >> 4) * wpg;
+    float mw[kWaves], lw[kWaves];
+    float4 ow[kWaves];
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      const int w = w0 + (i < wpg ? i : 0);
+      mw[i] = s_m[w * 16 + col];
+      lw[i] = s_l[w * 16 + col];
+      ow[i] = *reinterpret_cast<const float4*>(s_o + (size_t)(w * RW + col) * OST + d);
+    }
     float M = kNoMax;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w * 16 + h]);
-    float den = 0.0f, num = 0.0f;
+    for (int i = 0; i < kWaves; ++i) M = fmaxf(M, mw[i]);  // repeats change nothing
+    float den = 0.0f;
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float sc = fast_exp2(s_m[w * 16 + h] - M);
-      den += sc * s_l[w * 16 + h];
-      num += sc * s_o[(w * R + h) * OST + d];
+    for (int i = 0; i < kWaves; ++i) {
+      const float sc = i < wpg ? fast_exp2(mw[i] - M) : 0.0f;
+      den += sc * lw[i];
+      num.x += sc * ow[i].x;
+      num.y += sc * ow[i].y;
+      num.z += sc * ow[i].z;
+      num.w += sc * ow[i].w;
     }
-    const size_t row = row_of(h);
+    const size_t row = row_of(r);
     if (nparts <= 1) {
-      store_out<Tag>(p, row * D + d, den > 0.0f ? num / den : 0.0f);  // 0: no position seen
+      // 0: a row that saw no position
+      store_out4<Tag>(p, row * D + d,
+                      den > 0.0f ? make_float4(num.x / den, num.y / den, num.z / den, num.w / den)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f));
     } else {
-      // agent-scope stores: written through to where every XCD reads them
+      // agent-scope stores: written through to where every XCD reads them.
+      // A partial's D values are kept as its quads' (0, 1) pairs, then their
+      // (2, 3) pairs, so that each store (and each load of the merge) of the
+      // wave covers contiguous memory.
       const size_t pi = row * p.num_partitions + part;
-      __hip_atomic_store(&p.ws_o[pi * D + d], num, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (d == 0) {
-        __hip_atomic_store(&p.ws_ml[2 * pi], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&p.ws_ml[2 * pi + 1], den, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      unsigned long long* o2 = reinterpret_cast<unsigned long long*>(p.ws_o + pi * D + 2 * qd);
+      __hip_atomic_store(o2, pack2(num.x, num.y), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(o2 + DQ, pack2(num.z, num.w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (d == 0)
+        __hip_atomic_store(reinterpret_cast<unsigned long long*>(p.ws_ml + 2 * pi), pack2(M, den),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if (nparts <= 1) return;
@@ -776,46 +867,59 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   if (tid == 0) *s_last = take_ticket(p.arrive + (size_t)seq * p.num_kv_heads + kvh, p.epoch) == nparts - 1;
   __syncthreads();
   if (!*s_last) return;
-  for (int idx = tid; idx < R * D; idx += kThreads) {
-    const int h = idx / D;
-    const int d = idx - h * D;
-    const size_t row = row_of(h);
+  for (int qi = tid; qi < R * DQ; qi += kThreads) {
+    const int r = qi / DQ;
+    const int qd = qi - r * DQ;
+    const int d = 4 * qd;
+    const size_t row = row_of(r);
     const unsigned long long* ml =
         reinterpret_cast<const unsigned long long*>(p.ws_ml + 2 * row * p.num_partitions);
-    const float* o = p.ws_o + row * p.num_partitions * D + d;
-    // kMergeBatch partitions per round trip: every load of a batch is issued
-    // before any is used; the running max moves between batches
-    float M = kNoMax, den = 0.0f, num = 0.0f;
+    const unsigned long long* o =
+        reinterpret_cast<const unsigned long long*>(p.ws_o + row * p.num_partitions * D + 2 * qd);
+    // kMergeBatch partitions per round trip: every load of a batch (the
+    // (m, l) pair and the quad of each partition) is issued before any is
+    // used; the running max moves between batches
+    float M = kNoMax, den = 0.0f;
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int q0 = 0; q0 < nparts; q0 += kMergeBatch) {
-      float mq[kMergeBatch], lq[kMergeBatch], oq[kMergeBatch];
+      unsigned long long mlq[kMergeBatch], oa[kMergeBatch], ob[kMergeBatch];
+      // one base per batch: the loads below take constant offsets from it
+      const unsigned long long* mlb = ml + q0;
+      const unsigned long long* ob0 = o + (size_t)q0 * (D / 2);
 #pragma unroll
       for (int j = 0; j < kMergeBatch; ++j) {
-        const int q = q0 + j;
-        mq[j] = kNoMax;
-        lq[j] = oq[j] = 0.0f;
-        if (q < nparts) {
-          const unsigned long long pair = __hip_atomic_load(&ml[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          mq[j] = __uint_as_float((uint32_t)pair);
-          lq[j] = __uint_as_float((uint32_t)(pair >> 32));
-          oq[j] = __hip_atomic_load(&o[(size_t)q * D], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        mlq[j] = pack2(kNoMax, 0.0f);
+        oa[j] = ob[j] = 0ull;
+        if (q0 + j < nparts) {
+          mlq[j] = __hip_atomic_load(&mlb[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          oa[j] = __hip_atomic_load(&ob0[j * (D / 2)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ob[j] = __hip_atomic_load(&ob0[j * (D / 2) + DQ], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
-      float cm = mq[0];
+      float cm = lo_of(mlq[0]);
 #pragma unroll
-      for (int j = 1; j < kMergeBatch; ++j) cm = fmaxf(cm, mq[j]);
+      for (int j = 1; j < kMergeBatch; ++j) cm = fmaxf(cm, lo_of(mlq[j]));
       const float M_new = fmaxf(M, cm);
       const float alpha = fast_exp2(M - M_new);  // 0 for the first batch
       den *= alpha;
-      num *= alpha;
+      num.x *= alpha;
+      num.y *= alpha;
+      num.z *= alpha;
+      num.w *= alpha;
       M = M_new;
 #pragma unroll
       for (int j = 0; j < kMergeBatch; ++j) {
-        const float wq = fast_exp2(mq[j] - M);
-        den += wq * lq[j];
-        num += wq * oq[j];
+        const float wq = fast_exp2(lo_of(mlq[j]) - M);
+        den += wq * hi_of(mlq[j]);
+        num.x += wq * lo_of(oa[j]);
+        num.y += wq * hi_of(oa[j]);
+        num.z += wq * lo_of(ob[j]);
+        num.w += wq * hi_of(ob[j]);
       }
     }
-    store_out<Tag>(p, row * D + d, den > 0.0f ? num / den : 0.0f);
+    store_out4<Tag>(p, row * D + d,
+                    den > 0.0f ? make_float4(num.x / den, num.y / den, num.z / den, num.w / den)
+                               : make_float4(0.f, 0.f, 0.f, 0.f));
   }
 }
 

@@ -17,8 +17,9 @@ struct DecodeParams {
   const int32_t* seq_lens;
   unsigned long long* work;  // item counter: (epoch << 32) | items taken
   uint32_t epoch;            // set per launch: nonzero, distinct within the process
-  float* ws_o;    // [S, H, NP, D] weighted-V partial sums (split only)
-  float* ws_ml;   // [S, H, NP, 2] (running max in log2 units, sum of weights)
+  float* ws_o;    // [S, q_len, H, NP, D] weighted-V partial sums (split only); the D
+                  // values of one partial: the (0, 1) pairs of its quads, then the (2, 3) pairs
+  float* ws_ml;   // [S, q_len, H, NP, 2] (running max in log2 units, sum of weights)
   unsigned long long* arrive;  // [S, Hkv] (epoch << 32) | partitions done (split only)
   int num_seqs;
   int q_len;           // new tokens per sequence (1: decode); query and out are

@@ -269,18 +269,22 @@ def tiny() -> Workload:
                      new_positions=[L - 1 for L in lens])
 
 
-def llama3_8b() -> Workload:
+def llama3_8b(q_len: int = 1) -> Workload:
     """Llama-3-8B-shaped layer: 64 sequences, 32 q / 8 KV heads, head_dim 128,
     bf16, block_size 16, lengths uniform in [512, 4096], 20000-block pool,
-    plus reshape_and_cache of each sequence's new token."""
+    plus reshape_and_cache of each sequence's new token. With q_len > 1 the
+    same lengths hold q_len new tokens each (the last q_len positions: a
+    speculative verification step), written by the step's scatter."""
     seed = SEED_BASE + 2
     rng = np.random.default_rng(seed)
     lens = rng.integers(512, 4097, size=64).tolist()
-    tables, fill = _plain_layout(lens, 16, new_token=True)
-    return _assemble(name="llama3_8b_bf16", seed=seed, rng=rng, H=32, Hkv=8, D=128,
-                     bs=16, dtype=torch.bfloat16, seq_lens=lens, tables_virtual=tables,
-                     fill=fill, num_blocks=20000, max_blocks=256,
-                     new_positions=[L - 1 for L in lens])
+    tables, fill = _plain_layout(lens, 16, new_token=True, q_len=q_len)
+    newpos = ([L - 1 for L in lens] if q_len == 1 else
+              [list(range(L - q_len, L)) for L in lens])
+    return _assemble(name="llama3_8b_bf16" if q_len == 1 else f"llama3_8b_bf16_q{q_len}",
+                     seed=seed, rng=rng, H=32, Hkv=8, D=128, bs=16, dtype=torch.bfloat16,
+                     seq_lens=lens, tables_virtual=tables, fill=fill, num_blocks=20000,
+                     max_blocks=256, new_positions=newpos, q_len=q_len)
 
 
 def llama2_70b() -> Workload:

@@ -71,6 +71,9 @@ def _decode(**kw):
     (dict(maxlen=4096, MB=256, P=64), WS),     # a workspace is always needed
     (dict(maxlen=256, P=256), WS),
     (dict(maxlen=20000, MB=2000, P=20000), UNSUP),  # one partition too long for LDS
+    (dict(out=ctypes.c_void_p(0x1008), ws=FAKE, wsb=1 << 20), SHAPE),   # misaligned output
+    (dict(k=ctypes.c_void_p(0x1004), ws=FAKE, wsb=1 << 20), SHAPE),     # misaligned pool
+    (dict(ws=ctypes.c_void_p(0x1008), wsb=1 << 20), SHAPE),             # misaligned workspace
 ])
 def test_decode_host_checks(kw, code):
     assert _decode(**kw) == code
@@ -92,10 +95,13 @@ def _multi_query(**kw):
     (dict(S=0, out=None), OK),
     (dict(Q=0), SHAPE),
     (dict(Q=-3), SHAPE),
-    (dict(Q=5), UNSUP),                        # 5 tokens x 4 heads > 16 query rows
-    (dict(Q=2, H=8 * 9), UNSUP),               # 2 x 9
+    (dict(Q=33), UNSUP),                       # 33 tokens x 4 heads > 128 query rows
+    (dict(Q=15, H=8 * 9), UNSUP),              # 15 x 9 = 135
+    (dict(Q=129, H=8), UNSUP),                 # 129 x 1
     (dict(Q=2 ** 30, H=8), UNSUP),             # q_len * G would overflow int
-    (dict(Q=16, H=8), WS),                     # 16 x 1 rows: valid, but no workspace given
+    (dict(Q=32), WS),                          # 32 x 4 = 128 rows: valid, but no workspace given
+    (dict(Q=5), WS),                           # 20 rows: two column tiles
+    (dict(Q=128, H=8), WS),                    # 128 x 1 rows
     (dict(Q=2, H=8 * 8), WS),                  # 2 x 8 rows
     (dict(out=None), NULL),
     (dict(D=96), UNSUP),
@@ -116,7 +122,9 @@ def test_multi_query_workspace_sizing():
     assert (L.paged_attn_multi_query_workspace_size(256, 4, 32, 8, 128, 8, 10000, 512)
             == hdr + 256 * 4 * 32 * 20 * (128 + 2) * 4 + 256 * 8 * 8)
     assert L.paged_attn_multi_query_workspace_size(64, 2, 32, 8, 128, 16, 512, 512) == hdr
-    assert L.paged_attn_multi_query_workspace_size(64, 5, 32, 8, 128, 16, 4039, 0) == 0
+    assert L.paged_attn_multi_query_workspace_size(64, 33, 32, 8, 128, 16, 4039, 0) == 0
+    assert (L.paged_attn_multi_query_workspace_size(64, 8, 32, 8, 128, 16, 4039, 0)
+            == hdr + 64 * 8 * 32 * 4 * 130 * 4 + 64 * 8 * 8)
     assert L.paged_attn_multi_query_workspace_size(64, 0, 32, 8, 128, 16, 4039, 0) == 0
 
 
@@ -150,10 +158,13 @@ def test_partition_and_workspace_sizing():
     (lambda L: L.reshape_and_cache(FAKE, FAKE, FAKE, FAKE, FAKE, -4, 8, 128, 16, 10, 2, None), SHAPE),
     (lambda L: L.reshape_and_cache(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 80, 16, 10, 2, None), UNSUP),
     (lambda L: L.reshape_and_cache(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 7, None), UNSUP),
+    (lambda L: L.reshape_and_cache(FAKE, ctypes.c_void_p(0x1002), FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 2,
+                                   None), SHAPE),                                  # misaligned
     (lambda L: L.copy_blocks(FAKE, FAKE, FAKE, 0, 10, 16, 8, 128, 2, None), OK),
     (lambda L: L.copy_blocks(FAKE, None, FAKE, 3, 10, 16, 8, 128, 2, None), NULL),
     (lambda L: L.copy_blocks(FAKE, FAKE, FAKE, 3, 0, 16, 8, 128, 2, None), SHAPE),
     (lambda L: L.copy_blocks(FAKE, FAKE, FAKE, 3, 10, 12, 8, 128, 2, None), UNSUP),
+    (lambda L: L.copy_blocks(ctypes.c_void_p(0x1008), FAKE, FAKE, 3, 10, 16, 8, 128, 2, None), SHAPE),
     (lambda L: L.pagedkv_check_decode_inputs(FAKE, FAKE, 4, 16, 10, 8, 128, None, None), NULL),
     (lambda L: L.pagedkv_check_decode_inputs(FAKE, FAKE, 4, 16, 10, 8, -1, FAKE, None), SHAPE),
     (lambda L: L.pagedkv_stream_read(FAKE, 0, FAKE, 16, None), OK),          # nothing to read
@@ -161,6 +172,7 @@ def test_partition_and_workspace_sizing():
     (lambda L: L.pagedkv_stream_read(FAKE, 1000, FAKE, 16, None), SHAPE),   # not a multiple of 16
     (lambda L: L.pagedkv_stream_read(FAKE, 1024, FAKE, 0, None), SHAPE),
     (lambda L: L.pagedkv_stream_read(FAKE, 1024, FAKE, -2, None), SHAPE),
+    (lambda L: L.pagedkv_stream_read(ctypes.c_void_p(0x1004), 1024, FAKE, 16, None), SHAPE),
 ])
 def test_cache_op_host_checks(call, code):
     assert call(_lib.lib()) == code

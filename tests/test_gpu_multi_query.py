@@ -58,6 +58,15 @@ MQ_SMALL = [
     ("f16_d128_bs8_g2_q8_split16", torch.float16, 128, 8, 16, 8, 8, [8, 15, 16, 17, 23, 24, 200], 16),
     ("f32_d64_bs16_g1_q16_split16", torch.float32, 64, 16, 2, 2, 16, [16, 17, 31, 32, 33, 300], 16),
     ("bf16_d64_bs32_g8_q2_split32", torch.bfloat16, 64, 32, 16, 2, 2, [2, 32, 33, 34, 1000], 32),
+    # more than 16 query rows per KV head: column groups of waves (R = q_len x G)
+    ("bf16_d128_bs16_g4_q8", torch.bfloat16, 128, 16, 32, 8, 8, [8, 9, 16, 17, 100, 777], 0),  # R 32
+    ("f16_d128_bs32_g8_q8", torch.float16, 128, 32, 64, 8, 8, [8, 40, 64, 65, 1030], 0),  # R 64
+    ("bf16_d64_bs16_g16_q8", torch.bfloat16, 64, 16, 16, 1, 8, [8, 23, 300], 0),  # R 128
+    ("f32_d128_bs8_g2_q10", torch.float32, 128, 8, 4, 2, 10, [10, 11, 31, 200], 0),  # R 20
+    ("bf16_d128_bs16_g4_q6_split64", torch.bfloat16, 128, 16, 32, 8, 6,
+     [6, 63, 64, 65, 69, 70, 71, 1500], 64),  # R 24
+    ("f16_d64_bs8_g8_q5_split16", torch.float16, 64, 8, 16, 2, 5, [5, 15, 16, 17, 20, 21, 333], 16),
+    ("f32_d64_bs16_g1_q40_split32", torch.float32, 64, 16, 2, 2, 40, [40, 41, 63, 64, 65, 71, 250], 32),
 ]
 
 
@@ -171,19 +180,20 @@ def test_multi_query_workspace_garbage_and_reuse():
         assert max_err(out, refs[k]) <= TOL[wl.dtype], (k, P)
 
 
-@pytest.mark.parametrize("P", [0, 512])
-def test_multi_query_llama3_8b_shaped_verification(P):
+@pytest.mark.parametrize("Q,P", [(4, 0), (4, 512), (8, 0)])
+def test_multi_query_llama3_8b_shaped_verification(Q, P):
     """Speculative verification at the Llama-3-8B shape: 64 sequences of
     512-4096 tokens, 32 query heads on 8 KV heads, head_dim 128, bf16,
-    16-token blocks, 4 new tokens per sequence (4 x 4 = 16 query rows per KV
-    head: one full MFMA tile). Sampled sequences against the oracle."""
+    16-token blocks, 4 or 8 new tokens per sequence (16 or 32 query rows per
+    KV head: one or two MFMA column tiles). Sampled sequences against the
+    oracle."""
     rng = np.random.default_rng(4401)
     lens = rng.integers(512, 4097, size=64).tolist()
-    wl = _wl("llama3_8b_q4", torch.bfloat16, 128, 16, 32, 8, 4, lens, P)
+    wl = _wl(f"llama3_8b_q{Q}", torch.bfloat16, 128, 16, 32, 8, Q, lens, P)
     order = np.argsort(lens)
     seqs = sorted(set(order[:4].tolist() + order[-4:].tolist() + [5, 17, 33, 50]))
     ref = mq_oracle(wl, seqs=seqs)
-    say(f"multi-query Llama-3-8B shape q_len=4 P={P}")
+    say(f"multi-query Llama-3-8B shape q_len={Q} P={P}")
     for out_dt in (torch.float32, torch.bfloat16):
         out = mq_gpu(wl, to_dev(wl), out_dtype=out_dt)
         assert torch.isfinite(out).all()

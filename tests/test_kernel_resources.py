@@ -1,0 +1,29 @@
+"""The decode kernels compile for gfx950 without register spills or scratch
+memory (a spill puts per-lane scratch traffic into every work item). Host
+only: hipcc cross-compiles, nothing runs on a GPU."""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from paged_kv_cache_154_amd import build as B
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                    reason="hipcc not installed")
+def test_decode_kernels_do_not_spill(tmp_path):
+    src = os.path.join(B.CSRC, "decode.hip")
+    out = tmp_path / "decode.s"
+    cmd = [B.hipcc(), *B.HIP_FLAGS, "-I", B.INCLUDE, "-I", B.CSRC, "--cuda-device-only",
+           "-S", src, "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True, timeout=600)
+    text = out.read_text()
+    metas = re.findall(r"\.name:\s+(\S*decode_partition_kernel\S*)(.*?)(?=\n\s+- \.|\Z)", text, flags=re.S)
+    assert len(metas) == 18, "3 dtypes x 2 head dims x 3 block sizes"
+    for name, meta in metas:
+        vspill = int(re.search(r"\.vgpr_spill_count:\s+(\d+)", meta).group(1))
+        scratch = int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", meta).group(1))
+        assert vspill == 0 and scratch == 0, (name, vspill, scratch)
