@@ -24,6 +24,17 @@ Pins (checked by ``tests/test_oracle_*.py`` without a GPU):
     of the sequence truncated to the positions it sees; one new token is
     decode; changing position p changes exactly the rows that see it.
   * closed forms: the printed KV-size, block-size and pool-sizing numbers.
+  * ``fp8_kv`` (an e4m3 KV cache, LLM inference optimisation in practice,
+    §6.2): the value table against its landmarks (smallest subnormal and
+    normal, 1, 448, NaN) and torch's float8_e4m3fn for all 256 codes; the
+    encoder against torch's rounding inside the range, every midpoint to the
+    even code, saturation at 448, NaN and signed zero, a round trip of every
+    finite code, the quotient formed in fp32; the scatter's placement and
+    negative slots; attention over pools of small integers (exact in e4m3)
+    equal to ``decode``, k_scale and v_scale acting as scalings; multi-query
+    rows equal to decodes of their prefixes; planted mistakes (scales
+    swapped or dividing, exponent bias 8, no subnormals, ties away from
+    even, no saturation) each fail a pin.
 No function here is "parity unpinned".
 """
 
@@ -38,3 +49,4 @@ from .paged_attention import (  # noqa: F401
     multi_query_one,
     reshape_and_cache,
 )
+from . import fp8_kv  # noqa: F401,E402
