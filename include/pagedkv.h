@@ -29,7 +29,11 @@
  *     then the result for that sequence or token is unspecified.
  *     pagedkv_check_decode_inputs() reports such entries.
  *   - dtype codes: PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 (IEEE binary32,
- *     binary16, bfloat16).
+ *     binary16, bfloat16), PKV_E4M3 = 3 (OCP FP8 E4M3: one byte, bias 7,
+ *     3 mantissa bits, largest finite 448, 0x7F/0xFF NaN, no infinity; a
+ *     KV-cache format that stands for code * scale with a scale per KV head,
+ *     see the *_fp8 entry points; reshape_and_cache and copy_blocks move its
+ *     codes as bytes like any other type).
  */
 #ifndef PAGEDKV_H_
 #define PAGEDKV_H_
@@ -47,7 +51,7 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 #endif
 
-enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 };
+enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_E4M3 = 3 };
 
 enum pkv_status {
   PKV_OK = 0,
@@ -160,6 +164,43 @@ size_t paged_attn_multi_query_workspace_size(int num_seqs, int q_len, int num_he
                                              int partition_size);
 
 /*
+ * paged_attn_decode_fp8, paged_attn_multi_query_fp8 - paged_attn_decode and
+ * paged_attn_multi_query over an e4m3 KV cache ("LLM inference optimisation
+ * in practice" section 6.2: attention computed on a low-precision KV cache,
+ * halving the bytes each step reads from a 16-bit cache). Element d of the
+ * K row of a cached token, KV head j, stands for
+ *   e4m3_value(key_cache[...][j][d]) * k_scale[j],
+ * and likewise for V with v_scale: the attention is that of the two entry
+ * points above on those values. In the kernels the keys are widened to the
+ * query's type (exactly) for the 16-bit MFMA, the values to fp32, k_scale
+ * multiplies the scores and v_scale the output.
+ *
+ *   key_cache, value_cache  uint8 e4m3 codes [num_blocks, block_size, num_kv_heads, head_dim]
+ *   k_scale, v_scale        fp32 [num_kv_heads], device memory
+ *   query                   [num_seqs, (q_len,) num_heads, head_dim] of query_dtype
+ *   query_dtype             PKV_F16 or PKV_BF16
+ *   out_dtype               query_dtype or PKV_F32
+ * Everything else (shapes, partitions, the workspace and its size, status
+ * codes) is that of the 16-bit entry points; a NULL scale is PKV_ERR_NULL.
+ */
+int paged_attn_decode_fp8(void* out, const void* query, const void* key_cache,
+                          const void* value_cache, const float* k_scale, const float* v_scale,
+                          const int32_t* block_table, const int32_t* seq_lens, int num_seqs,
+                          int num_heads, int num_kv_heads, int head_dim, int block_size,
+                          int num_blocks, int max_blocks_per_seq, int max_seq_len, float scale,
+                          int query_dtype, int out_dtype, int partition_size, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+int paged_attn_multi_query_fp8(void* out, const void* query, const void* key_cache,
+                               const void* value_cache, const float* k_scale,
+                               const float* v_scale, const int32_t* block_table,
+                               const int32_t* seq_lens, int num_seqs, int q_len, int num_heads,
+                               int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                               int max_blocks_per_seq, int max_seq_len, float scale,
+                               int query_dtype, int out_dtype, int partition_size,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * paged_attn_partition_tokens - the partition length paged_attn_decode uses
  * for these arguments (resolving partition_size = 0), or a negative
  * pkv_status for invalid arguments. A value >= max_seq_len means no split.
@@ -202,6 +243,25 @@ int reshape_and_cache(const void* key, const void* value, void* key_cache,
                       int num_tokens, int num_kv_heads, int head_dim,
                       int block_size, int num_blocks, int dtype,
                       hipStream_t stream);
+
+/*
+ * reshape_and_cache_fp8 - reshape_and_cache into e4m3 pools, quantising:
+ * element d of KV head j of token i is stored as the e4m3 code of
+ * key[i][j][d] / k_scale[j] (the quotient formed in fp32, then rounded to
+ * the nearest e4m3 value, ties to the even code; magnitudes of 448 and more
+ * saturate to 448; NaN stays NaN), and likewise for value with v_scale.
+ * Slots as for reshape_and_cache. The scales are the caller's (for example
+ * calibrated per layer and KV head) and the same ones go to the attention.
+ *
+ *   key, value              [num_tokens, num_kv_heads, head_dim] of src_dtype
+ *                           (PKV_F32, PKV_F16 or PKV_BF16)
+ *   key_cache, value_cache  uint8 [num_blocks, block_size, num_kv_heads, head_dim]
+ *   k_scale, v_scale        fp32 [num_kv_heads], device memory
+ */
+int reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                          void* value_cache, const int64_t* slot_mapping, const float* k_scale,
+                          const float* v_scale, int num_tokens, int num_kv_heads, int head_dim,
+                          int block_size, int num_blocks, int src_dtype, hipStream_t stream);
 
 /*
  * copy_blocks - copy-on-write block copies: for each pair (src, dst) of

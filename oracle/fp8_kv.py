@@ -62,7 +62,18 @@ def e4m3_decode(codes) -> np.ndarray:
 
 def e4m3_encode(x32) -> np.ndarray:
     """fp32 values -> e4m3 codes (uint8): nearest value, ties to the even
-    code, |x| > 448 saturating to 448, NaN to 0x7F with the sign bit of x."""
+    code, |x| > 448 saturating to 448, NaN to 0x7F with the sign bit of x.
+    Element by element (large arrays in pieces, which changes nothing)."""
+    x = np.asarray(x32, dtype=np.float32)
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    step = 1 << 20
+    for i in range(0, flat.size, step):
+        out[i:i + step] = _encode_piece(flat[i:i + step])
+    return out.reshape(x.shape)
+
+
+def _encode_piece(x32) -> np.ndarray:
     x = np.asarray(x32, dtype=np.float32).astype(np.float64)
     sign = np.where(np.signbit(x), 0x80, 0x00).astype(np.uint8)
     a = np.abs(x)

@@ -14,6 +14,15 @@ kernels of ``libpagedkv.so``; there is no Python or CPU fallback.
     reshape_and_cache(key, value, key_cache, value_cache, slot_mapping)
     copy_blocks(key_cache, value_cache, block_mapping)
 
+e4m3 KV cache (pools of uint8 codes, or torch.float8_e4m3fn; fp32 scales
+``[num_kv_heads]`` for K and for V; the query bf16 or fp16):
+
+    reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping,
+                          k_scale, v_scale)
+    paged_attn_decode_fp8(out, query, key_cache, value_cache, k_scale, v_scale,
+                          block_table, seq_lens, scale, max_seq_len, ...)
+    paged_attn_multi_query_fp8(...)   # query [num_seqs, q_len, num_heads, head_dim]
+
 Shapes (all dense, on one GPU): query/out ``[num_seqs, num_heads,
 head_dim]`` for decode, ``[num_seqs, q_len, num_heads, head_dim]`` for
 the multi-query pass; pools ``[num_blocks, block_size, num_kv_heads, head_dim]``;
@@ -26,10 +35,11 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import (PKV_BF16, PKV_F16, PKV_F32, LIB_PATH, PagedKVError,  # noqa: F401
+from ._lib import (PKV_BF16, PKV_E4M3, PKV_F16, PKV_F32, LIB_PATH, PagedKVError,  # noqa: F401
                    check, lib, status_string)
 
-_DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+_DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16,
+               torch.uint8: PKV_E4M3, torch.float8_e4m3fn: PKV_E4M3}
 
 
 def dtype_code(dtype: torch.dtype) -> int:
@@ -100,8 +110,10 @@ def workspace_for(query: torch.Tensor, key_cache: torch.Tensor, max_seq_len: int
 
 
 def _attention(name: str, out, query, key_cache, value_cache, block_table, seq_lens, scale,
-               max_seq_len, partition_size, workspace, stream) -> torch.Tensor:
-    multi = name == "paged_attn_multi_query"
+               max_seq_len, partition_size, workspace, stream, k_scale=None,
+               v_scale=None) -> torch.Tensor:
+    multi = "multi_query" in name
+    f8 = name.endswith("_fp8")
     want = 4 if multi else 3
     _require(query.dim() == want and out.shape == query.shape,
              "query/out must be [S, q_len, H, D]" if multi else "query/out must be [S, H, D]")
@@ -109,7 +121,17 @@ def _attention(name: str, out, query, key_cache, value_cache, block_table, seq_l
              "pools must be [num_blocks, block_size, num_kv_heads, head_dim]")
     _require(block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32,
              "block_table and seq_lens must be int32")
-    _require(query.dtype == key_cache.dtype == value_cache.dtype, "query and pools share a dtype")
+    if f8:
+        _require(dtype_code(key_cache.dtype) == PKV_E4M3 and key_cache.dtype == value_cache.dtype,
+                 "e4m3 pools must be uint8 or float8_e4m3fn")
+        _require(query.dtype in (torch.float16, torch.bfloat16), "the query must be fp16 or bf16")
+        _require(k_scale is not None and v_scale is not None and k_scale.dtype == torch.float32
+                 and v_scale.dtype == torch.float32
+                 and k_scale.shape == v_scale.shape == (key_cache.shape[2],),
+                 "k_scale and v_scale must be fp32 [num_kv_heads]")
+    else:
+        _require(query.dtype == key_cache.dtype == value_cache.dtype,
+                 "query and pools share a dtype")
     if multi:
         S, Q, H, D = query.shape
     else:
@@ -121,14 +143,17 @@ def _attention(name: str, out, query, key_cache, value_cache, block_table, seq_l
     if workspace is None:
         workspace = workspace_for(query, key_cache, max_seq_len, partition_size)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    head = [_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_table),
-            _ptr(seq_lens), S]
+    head = [_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache)]
+    if f8:
+        head += [_ptr(k_scale), _ptr(v_scale)]
+    head += [_ptr(block_table), _ptr(seq_lens), S]
     if multi:
         head.append(Q)
+    # the 16-bit entry points take the KV dtype (= the query's), the e4m3 ones the query's
     st = getattr(lib(), name)(
         *head, H, Hkv, D, bs, NB, block_table.shape[1], int(max_seq_len), float(scale),
-        dtype_code(query.dtype), dtype_code(out.dtype), int(partition_size), _ptr(workspace),
-        ws_bytes, _stream(query, stream))
+        dtype_code(query.dtype), dtype_code(out.dtype), int(partition_size), _ptr(workspace), ws_bytes,
+        _stream(query, stream))
     check(st, name)
     return out
 
@@ -161,6 +186,54 @@ def paged_attn_multi_query(out: torch.Tensor, query: torch.Tensor, key_cache: to
     return _attention("paged_attn_multi_query", out, query, key_cache, value_cache,
                       block_table, seq_lens, scale, max_seq_len, partition_size, workspace,
                       stream)
+
+
+def paged_attn_decode_fp8(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                          value_cache: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor,
+                          block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                          max_seq_len: int, partition_size: int = 0,
+                          workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode over e4m3 pools: code * k_scale[kv head] and code * v_scale[kv head]
+    stand for K and V. query bf16/fp16 [S, H, D]; out of the query's type or fp32."""
+    return _attention("paged_attn_decode_fp8", out, query, key_cache, value_cache, block_table,
+                      seq_lens, scale, max_seq_len, partition_size, workspace, stream,
+                      k_scale, v_scale)
+
+
+def paged_attn_multi_query_fp8(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                               value_cache: torch.Tensor, k_scale: torch.Tensor,
+                               v_scale: torch.Tensor, block_table: torch.Tensor,
+                               seq_lens: torch.Tensor, scale: float, max_seq_len: int,
+                               partition_size: int = 0, workspace: torch.Tensor | None = None,
+                               stream=None) -> torch.Tensor:
+    """paged_attn_multi_query over e4m3 pools (query [S, q_len, H, D])."""
+    return _attention("paged_attn_multi_query_fp8", out, query, key_cache, value_cache,
+                      block_table, seq_lens, scale, max_seq_len, partition_size, workspace,
+                      stream, k_scale, v_scale)
+
+
+def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                          value_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                          k_scale: torch.Tensor, v_scale: torch.Tensor, stream=None) -> None:
+    """Quantise each new token's K and V (fp32/fp16/bf16) into e4m3 codes of
+    x / scale[kv head] at slot_mapping[i] of the uint8 pools."""
+    _require(key.dim() == 3 and value.shape == key.shape, "key/value must be [T, Hkv, D]")
+    _require(key_cache.dim() == 4 and value_cache.shape == key_cache.shape, "pool shape")
+    _require(dtype_code(key_cache.dtype) == PKV_E4M3 and key_cache.dtype == value_cache.dtype,
+             "e4m3 pools must be uint8 or float8_e4m3fn")
+    _require(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (key.shape[0],),
+             "slot_mapping must be int64 [T]")
+    _require(key.dtype == value.dtype and key.dtype in (torch.float32, torch.float16,
+                                                        torch.bfloat16), "key/value dtype")
+    NB, bs, Hkv, D = key_cache.shape
+    _require(tuple(key.shape[1:]) == (Hkv, D), "key rows must be [num_kv_heads, head_dim]")
+    _require(k_scale.dtype == torch.float32 and v_scale.dtype == torch.float32
+             and k_scale.shape == v_scale.shape == (Hkv,), "scales must be fp32 [num_kv_heads]")
+    st = lib().reshape_and_cache_fp8(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                                     _ptr(slot_mapping), _ptr(k_scale), _ptr(v_scale),
+                                     key.shape[0], Hkv, D, bs, NB, dtype_code(key.dtype),
+                                     _stream(key_cache, stream))
+    check(st, "reshape_and_cache_fp8")
 
 
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,

@@ -7,7 +7,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
 
-PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PKV_F32, PKV_F16, PKV_BF16, PKV_E4M3 = 0, 1, 2, 3
 PKV_OK = 0
 
 _c_int = ctypes.c_int
@@ -27,6 +27,16 @@ SIGNATURES = {
                                         _c_size, _c_ptr]),
     "paged_attn_multi_query_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int,
                                                         _c_int, _c_int, _c_int]),
+    "paged_attn_decode_fp8": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                       _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                       _c_int, _c_int, _c_float, _c_int, _c_int, _c_int, _c_ptr,
+                                       _c_size, _c_ptr]),
+    "paged_attn_multi_query_fp8": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                            _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int,
+                                            _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
+                                            _c_int, _c_int, _c_int, _c_ptr, _c_size, _c_ptr]),
+    "reshape_and_cache_fp8": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                       _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
     "paged_attn_partition_tokens": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "paged_attn_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                             _c_int]),

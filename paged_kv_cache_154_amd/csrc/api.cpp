@@ -19,6 +19,7 @@ int elem_bytes(int dtype) {
     case PKV_F32: return 4;
     case PKV_F16:
     case PKV_BF16: return 2;
+    case PKV_E4M3: return 1;
     default: return 0;
   }
 }
@@ -117,17 +118,22 @@ int paged_attn_partition_tokens(int num_seqs, int num_kv_heads, int block_size, 
 
 namespace {
 
-// paged_attn_decode and paged_attn_multi_query: q_len new tokens per
-// sequence (1 for decode), query and out [num_seqs, q_len, num_heads, head_dim].
+// Every attention entry point: q_len new tokens per sequence (1 for decode),
+// query and out [num_seqs, q_len, num_heads, head_dim]. The query has
+// query_dtype: the KV dtype, or fp16/bf16 over an e4m3 pool (which takes a
+// K and a V scale per KV head).
 int attention(void* out, const void* query, const void* key_cache, const void* value_cache,
-              const int32_t* block_table, const int32_t* seq_lens, int num_seqs, int q_len,
-              int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
-              int max_blocks_per_seq, int max_seq_len, float scale, int kv_dtype, int out_dtype,
+              const float* k_scale, const float* v_scale, const int32_t* block_table,
+              const int32_t* seq_lens, int num_seqs, int q_len, int num_heads, int num_kv_heads,
+              int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+              int max_seq_len, float scale, int kv_dtype, int query_dtype, int out_dtype,
               int partition_size, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (num_seqs < 0 || q_len < 1) return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !query || !key_cache || !value_cache || !block_table || !seq_lens)
     return PKV_ERR_NULL;
+  const bool f8 = kv_dtype == PKV_E4M3;
+  if (f8 && (!k_scale || !v_scale)) return PKV_ERR_NULL;
   if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
   const int group = num_heads / num_kv_heads;
   // the q_len * group query rows of a KV head: at most one 16-column MFMA tile
@@ -135,7 +141,9 @@ int attention(void* out, const void* query, const void* key_cache, const void* v
   if (group > 16 || q_len > kMaxQueryRows || q_len * group > kMaxQueryRows) return PKV_ERR_UNSUPPORTED;
   if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
   if (elem_bytes(kv_dtype) == 0) return PKV_ERR_UNSUPPORTED;
-  if (out_dtype != kv_dtype && out_dtype != PKV_F32) return PKV_ERR_UNSUPPORTED;
+  if (f8 ? (query_dtype != PKV_F16 && query_dtype != PKV_BF16) : query_dtype != kv_dtype)
+    return PKV_ERR_UNSUPPORTED;
+  if (out_dtype != query_dtype && out_dtype != PKV_F32) return PKV_ERR_UNSUPPORTED;
   if (num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0) return PKV_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size < max_seq_len) return PKV_ERR_SHAPE;
   if ((int64_t)num_blocks * block_size > (int64_t)INT32_MAX) return PKV_ERR_UNSUPPORTED;
@@ -161,6 +169,8 @@ int attention(void* out, const void* query, const void* key_cache, const void* v
   p.v = value_cache;
   p.block_table = block_table;
   p.seq_lens = seq_lens;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   p.work = reinterpret_cast<unsigned long long*>(ws);
   if (np > 1) {
@@ -181,7 +191,7 @@ int attention(void* out, const void* query, const void* key_cache, const void* v
   p.num_partitions = np;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
-    const hipError_t e = pkv::launch_decode(p, kv_dtype, head_dim, block_size, stream);
+  const hipError_t e = pkv::launch_decode(p, kv_dtype, query_dtype, head_dim, block_size, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -221,9 +231,11 @@ int paged_attn_decode(void* out, const void* query, const void* key_cache, const
                       int num_blocks, int max_blocks_per_seq, int max_seq_len, float scale,
                       int kv_dtype, int out_dtype, int partition_size, void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
-  return attention(out, query, key_cache, value_cache, block_table, seq_lens, num_seqs, 1, num_heads,
-                   num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_seq_len, scale,
-                   kv_dtype, out_dtype, partition_size, workspace, workspace_bytes, stream);
+  if (kv_dtype == PKV_E4M3) return PKV_ERR_UNSUPPORTED;  // needs the scales: paged_attn_decode_fp8
+  return attention(out, query, key_cache, value_cache, nullptr, nullptr, block_table, seq_lens, num_seqs,
+                   1, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                   max_seq_len, scale, kv_dtype, kv_dtype, out_dtype, partition_size, workspace,
+                   workspace_bytes, stream);
 }
 
 int paged_attn_multi_query(void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -232,9 +244,37 @@ int paged_attn_multi_query(void* out, const void* query, const void* key_cache, 
                            int num_blocks, int max_blocks_per_seq, int max_seq_len, float scale,
                            int kv_dtype, int out_dtype, int partition_size, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
-  return attention(out, query, key_cache, value_cache, block_table, seq_lens, num_seqs, q_len, num_heads,
-                   num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_seq_len, scale,
-                   kv_dtype, out_dtype, partition_size, workspace, workspace_bytes, stream);
+  if (kv_dtype == PKV_E4M3) return PKV_ERR_UNSUPPORTED;  // needs the scales: paged_attn_multi_query_fp8
+  return attention(out, query, key_cache, value_cache, nullptr, nullptr, block_table, seq_lens, num_seqs,
+                   q_len, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                   max_seq_len, scale, kv_dtype, kv_dtype, out_dtype, partition_size, workspace,
+                   workspace_bytes, stream);
+}
+
+int paged_attn_decode_fp8(void* out, const void* query, const void* key_cache, const void* value_cache,
+                          const float* k_scale, const float* v_scale, const int32_t* block_table,
+                          const int32_t* seq_lens, int num_seqs, int num_heads, int num_kv_heads,
+                          int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                          int max_seq_len, float scale, int query_dtype, int out_dtype,
+                          int partition_size, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  return attention(out, query, key_cache, value_cache, k_scale, v_scale, block_table, seq_lens, num_seqs,
+                   1, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                   max_seq_len, scale, PKV_E4M3, query_dtype, out_dtype, partition_size, workspace,
+                   workspace_bytes, stream);
+}
+
+int paged_attn_multi_query_fp8(void* out, const void* query, const void* key_cache,
+                               const void* value_cache, const float* k_scale, const float* v_scale,
+                               const int32_t* block_table, const int32_t* seq_lens, int num_seqs,
+                               int q_len, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                               int num_blocks, int max_blocks_per_seq, int max_seq_len, float scale,
+                               int query_dtype, int out_dtype, int partition_size, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  return attention(out, query, key_cache, value_cache, k_scale, v_scale, block_table, seq_lens, num_seqs,
+                   q_len, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                   max_seq_len, scale, PKV_E4M3, query_dtype, out_dtype, partition_size, workspace,
+                   workspace_bytes, stream);
 }
 
 int reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
@@ -254,6 +294,26 @@ int reshape_and_cache(const void* key, const void* value, void* key_cache, void*
   const hipError_t e = pkv::launch_reshape_and_cache(
       key, value, key_cache, value_cache, slot_mapping, num_tokens, (int)row_bytes,
       (int64_t)num_blocks * block_size, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int reshape_and_cache_fp8(const void* key, const void* value, void* key_cache, void* value_cache,
+                          const int64_t* slot_mapping, const float* k_scale, const float* v_scale,
+                          int num_tokens, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                          int src_dtype, hipStream_t stream) {
+  if (num_tokens < 0) return PKV_ERR_SHAPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping || !k_scale || !v_scale)
+    return PKV_ERR_NULL;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+    return PKV_ERR_SHAPE;
+  if (num_kv_heads <= 0 || num_blocks <= 0) return PKV_ERR_SHAPE;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
+  if (src_dtype != PKV_F32 && src_dtype != PKV_F16 && src_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)num_kv_heads * head_dim > INT32_MAX / 8) return PKV_ERR_SHAPE;
+  const hipError_t e = pkv::launch_reshape_and_cache_fp8(
+      key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale, num_tokens, num_kv_heads,
+      head_dim, src_dtype, (int64_t)num_blocks * block_size, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

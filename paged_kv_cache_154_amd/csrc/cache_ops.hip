@@ -30,6 +30,62 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   value_cache[dst] = value[src];
 }
 
+// The e4m3 code of x (OCP FP8 E4M3: bias 7, 3 mantissa bits, subnormals
+// m * 2^-9, no infinity, 0x7F the NaN): the nearest e4m3 value with ties to
+// the even code, magnitudes of 448 and more (infinity too) saturating to 448,
+// NaN kept. Exact in fp32: the subnormal step is a power of two, and the
+// normal range rounds the fp32 mantissa to 3 bits by integer arithmetic.
+__device__ inline uint32_t e4m3_code(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (!(a == a)) return sign | 0x7Fu;
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) {
+    // below 2^-6: multiples of 2^-9, rounded half to even (8 is code 0x08 = 2^-6)
+    return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+  }
+  // 2^-6 <= a < 448: drop 20 of the 23 mantissa bits, half to even; a carry
+  // out of the mantissa moves the exponent up, as it should
+  const uint32_t au = u & 0x7FFFFFFFu;
+  const uint32_t r = au + 0x7FFFFu + ((au >> 20) & 1u);
+  const uint32_t e = (r >> 23) - 120u;  // fp32 exponent bias 127 -> e4m3 bias 7
+  return sign | (e << 3) | ((r >> 20) & 7u);
+}
+
+// The quantising scatter of an e4m3 cache: one lane per 16 elements of a
+// token's row (within one KV head), each divided by its KV head's scale in
+// fp32 and stored as 16 one-byte codes. T is the type of key and value.
+template <class T>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    const T* __restrict__ key, const T* __restrict__ value, uint4* __restrict__ key_cache,
+    uint4* __restrict__ value_cache, const int64_t* __restrict__ slot_mapping,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale, int num_tokens,
+    int chunks_per_row, int chunks_per_head, int64_t num_slots) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)num_tokens * chunks_per_row;
+  if (gid >= total) return;
+  const int64_t i = gid / chunks_per_row;
+  const int c = (int)(gid - i * chunks_per_row);
+  const int64_t slot = slot_mapping[i];
+  if (slot < 0 || slot >= num_slots) return;  // no slot (padding) or outside the pool
+  const int head = c / chunks_per_head;
+  constexpr int NQ = (int)sizeof(T);          // 16-byte loads per 16 elements
+  auto quantise = [&](const T* src, float scale) -> uint4 {
+    union { uint4 v[NQ]; T e[16]; } in;
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) in.v[k] = reinterpret_cast<const uint4*>(src)[k];
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) w[e >> 2] |= e4m3_code(static_cast<float>(in.e[e]) / scale) << (8 * (e & 3));
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  };
+  const int64_t src = (i * chunks_per_row + c) * 16;
+  const int64_t dst = slot * chunks_per_row + c;
+  key_cache[dst] = quantise(key + src, k_scale[head]);
+  value_cache[dst] = quantise(value + src, v_scale[head]);
+}
+
 // Whole-block copies src -> dst for K and V ("vLLM core concepts" section
 // 4.2.2: a shared block is copied before it is written).
 __global__ __launch_bounds__(256) void copy_blocks_kernel(
@@ -98,6 +154,38 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* ke
       static_cast<const uint4*>(key), static_cast<const uint4*>(value),
       static_cast<uint4*>(key_cache), static_cast<uint4*>(value_cache), slot_mapping, num_tokens,
       chunks, num_slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                                        void* value_cache, const int64_t* slot_mapping,
+                                        const float* k_scale, const float* v_scale, int num_tokens,
+                                        int num_kv_heads, int head_dim, int src_dtype,
+                                        int64_t num_slots, hipStream_t stream) {
+  const int per_head = head_dim / 16;
+  const int chunks = num_kv_heads * per_head;
+  const int64_t total = (int64_t)num_tokens * chunks;
+  const unsigned grid = (unsigned)((total + 255) / 256);
+  uint4* kc = static_cast<uint4*>(key_cache);
+  uint4* vc = static_cast<uint4*>(value_cache);
+  switch (src_dtype) {
+    case 0:
+      reshape_and_cache_fp8_kernel<float><<<dim3(grid), dim3(256), 0, stream>>>(
+          static_cast<const float*>(key), static_cast<const float*>(value), kc, vc, slot_mapping,
+          k_scale, v_scale, num_tokens, chunks, per_head, num_slots);
+      break;
+    case 1:
+      reshape_and_cache_fp8_kernel<_Float16><<<dim3(grid), dim3(256), 0, stream>>>(
+          static_cast<const _Float16*>(key), static_cast<const _Float16*>(value), kc, vc,
+          slot_mapping, k_scale, v_scale, num_tokens, chunks, per_head, num_slots);
+      break;
+    case 2:
+      reshape_and_cache_fp8_kernel<__bf16><<<dim3(grid), dim3(256), 0, stream>>>(
+          static_cast<const __bf16*>(key), static_cast<const __bf16*>(value), kc, vc,
+          slot_mapping, k_scale, v_scale, num_tokens, chunks, per_head, num_slots);
+      break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

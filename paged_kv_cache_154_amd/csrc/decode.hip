@@ -70,6 +70,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 struct F32Tag { static constexpr int kBytes = 4; };
 struct F16Tag { static constexpr int kBytes = 2; };
 struct BF16Tag { static constexpr int kBytes = 2; };
+// e4m3 K/V (one byte per element, a scale per KV head) with a bf16 or fp16
+// query and output ("LLM inference optimisation in practice" section 6.2:
+// attention over a low-precision KV cache).
+struct E4M3BF16Tag { static constexpr int kBytes = 1; };
+struct E4M3F16Tag { static constexpr int kBytes = 1; };
 
 template <class Tag>
 struct KV;
@@ -77,6 +82,8 @@ struct KV;
 template <>
 struct KV<F32Tag> {
   static constexpr int kBytes = 4;
+  static constexpr int kQBytes = 4;   // query element
+  static constexpr bool kF8 = false;
   // One 16-byte key chunk (4 head-dim elements) against the matching query
   // chunk: four K=4 steps of the fp32 MFMA.
   __device__ static inline f32x4 qk(const uint4& k, const uint4& q, f32x4 acc) {
@@ -98,6 +105,8 @@ struct KV<F32Tag> {
 template <>
 struct KV<F16Tag> {
   static constexpr int kBytes = 2;
+  static constexpr int kQBytes = 2;
+  static constexpr bool kF8 = false;
   __device__ static inline f32x4 qk(const uint4& k, const uint4& q, f32x4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, k),
                                                   __builtin_bit_cast(f16x8, q), acc, 0, 0, 0);
@@ -121,6 +130,8 @@ struct KV<F16Tag> {
 template <>
 struct KV<BF16Tag> {
   static constexpr int kBytes = 2;
+  static constexpr int kQBytes = 2;
+  static constexpr bool kF8 = false;
   __device__ static inline f32x4 qk(const uint4& k, const uint4& q, f32x4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
                                                    __builtin_bit_cast(bf16x8, q), acc, 0, 0, 0);
@@ -141,6 +152,55 @@ struct KV<BF16Tag> {
   }
 };
 
+// e4m3 code `b` (0..3) of the word w, as fp32 (every e4m3 value is exact).
+__device__ inline float f8_at(uint32_t w, int b) {
+  switch (b) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8(w, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8(w, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8(w, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8(w, 3);
+  }
+}
+
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+// The e4m3 K/V traits over a 16-bit query type Q16 (KV<BF16Tag> or
+// KV<F16Tag>): the key codes are widened to Q16 in registers (exactly: e4m3
+// has 3 mantissa bits and a range inside both) for the 16-bit MFMA, values
+// to fp32 for the fp32 MFMA.
+template <class Q16, bool kBF>
+struct KVe4m3 {
+  static constexpr int kBytes = 1;
+  static constexpr int kQBytes = 2;
+  static constexpr bool kF8 = true;
+  __device__ static inline f32x4 qk(const uint4& k, const uint4& q, f32x4 acc) { return Q16::qk(k, q, acc); }
+  // four codes -> two words of 16-bit values (element order kept)
+  __device__ static inline void widen4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    const f32x2v a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    const f32x2v b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    if constexpr (kBF) {
+      // bf16 is the upper half of the fp32 (exact here)
+      lo = __builtin_amdgcn_perm(__float_as_uint(a.y), __float_as_uint(a.x), 0x07060302u);
+      hi = __builtin_amdgcn_perm(__float_as_uint(b.y), __float_as_uint(b.x), 0x07060302u);
+    } else {
+      lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a.x, a.y));
+      hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(b.x, b.y));
+    }
+  }
+  // 16 codes -> the two 8-element key chunks of the 16-bit MFMA
+  __device__ static inline void widen(const uint4& raw, uint4& c0, uint4& c1) {
+    widen4(raw.x, c0.x, c0.y);
+    widen4(raw.y, c0.z, c0.w);
+    widen4(raw.z, c1.x, c1.y);
+    widen4(raw.w, c1.z, c1.w);
+  }
+  __device__ static inline float elem(const uint32_t* w, int j) { return f8_at(w[j >> 2], j & 3); }
+  __device__ static inline void store(void* out, size_t i, float x) { Q16::store(out, i, x); }
+  __device__ static inline void store4(void* out, size_t i, float4 x) { Q16::store4(out, i, x); }
+};
+template <> struct KV<E4M3BF16Tag> : KVe4m3<KV<BF16Tag>, true> {};
+template <> struct KV<E4M3F16Tag> : KVe4m3<KV<F16Tag>, false> {};
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Loads that stream past the caches (true) or are cached as usual (false).
@@ -153,7 +213,9 @@ template <> struct NTL<false> {
 };
 template <bool nt, int NW>
 __device__ inline void load_words(uint32_t (&w)[NW], const unsigned char* ptr) {
-  if constexpr (NW == 2) {
+  if constexpr (NW == 1) {
+    w[0] = NTL<nt>::ld(reinterpret_cast<const uint32_t*>(ptr));
+  } else if constexpr (NW == 2) {
     const u32x2* a2 = reinterpret_cast<const u32x2*>(ptr);
     const u32x2 a = NTL<nt>::ld(a2);
     w[0] = a.x; w[1] = a.y;
@@ -228,13 +290,17 @@ template <class Tag, int D, int BS>
 struct TileEngine {
   using Tr = KV<Tag>;
   static constexpr int E = Tr::kBytes;
+  static constexpr bool kF8 = Tr::kF8;
   static constexpr int RB = D * E;        // bytes of one token row of one KV head
-  static constexpr int NKL = RB / 64;     // 16-byte key chunks per lane per tile
+  static constexpr int QB = D * Tr::kQBytes;  // bytes of one query row
+  static constexpr int NKR = RB / 64;     // 16-byte key chunks per lane per tile, as loaded
+  // key operands per lane per tile (e4m3: each loaded chunk widens to two)
+  static constexpr int NKL = kF8 ? 2 * NKR : NKR;
   static constexpr int VPL = D / 16;      // V elements per lane per token
   static constexpr int VW = VPL * E / 4;  // 32-bit words per lane per token of V
   static_assert(RB % 64 == 0, "row must split into 4 lane groups of 16-byte chunks");
   // Rows of >= 256 bytes load K like V (whole rows) and reorder it through
-  // LDS; 128-byte rows (head_dim 64, 16-bit) load it in the operand layout.
+  // LDS; shorter rows load it in the operand layout.
   static constexpr bool kKLds = RB >= 256;
   static constexpr int KCL = RB / 256;     // 16-byte chunks per lane per token (K rows whole)
   static constexpr int KTS = RB + 16;      // LDS row stride of the K tile
@@ -253,12 +319,16 @@ struct TileEngine {
     grp = lane >> 4;
   }
 
-  // qrow: this lane's query row (column col), read when `valid`.
+  // qrow: this lane's query row (column col), read when `valid`. Chunk i
+  // holds the head-dim elements that key operand i of this lane holds:
+  // 32 i + 8 grp .. +7 when keys are loaded in 16-byte chunks of 8 elements;
+  // for e4m3 keys (16 elements per loaded chunk, widened to operands 2u and
+  // 2u + 1) 64 u + 16 grp + 8 h .. +7 for i = 2u + h.
   __device__ void load_q(const unsigned char* qrow, bool valid) {
 #pragma unroll
     for (int i = 0; i < NKL; ++i) {
-      qv[i] = valid ? *reinterpret_cast<const uint4*>(qrow + 16 * (4 * i + grp))
-                    : make_uint4(0u, 0u, 0u, 0u);
+      const int off = kF8 ? 128 * (i >> 1) + 32 * grp + 16 * (i & 1) : 16 * (4 * i + grp);
+      qv[i] = valid ? *reinterpret_cast<const uint4*>(qrow + off) : make_uint4(0u, 0u, 0u, 0u);
     }
   }
 
@@ -297,14 +367,30 @@ struct TileEngine {
       }
     } else {
       const unsigned char* kp = kbase + row_off(min(cs + col, t_last)) + 16 * grp;
+      if constexpr (kF8) {
+        // raw codes in the first NKR slots, widened after the loads are issued
 #pragma unroll
-      for (int i = 0; i < NKL; ++i) kr[i] = *reinterpret_cast<const uint4*>(kp + 64 * i);
+        for (int u = 0; u < NKR; ++u) {
+          const u32x4 a = NTL<nt>::ld(reinterpret_cast<const u32x4*>(kp + 64 * u));
+          kr[u] = make_uint4(a.x, a.y, a.z, a.w);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NKL; ++i) kr[i] = *reinterpret_cast<const uint4*>(kp + 64 * i);
+      }
     }
     const unsigned char* vp = vbase + off4 + col * (VPL * E);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       load_words<nt, VW>(vr[r], vp + (uint32_t)((uint32_t)r < room ? r : room) * slot_bytes);
     __builtin_amdgcn_sched_barrier(0);  // every load of the tile in flight first
+    if constexpr (kF8) {
+#pragma unroll
+      for (int u = NKR - 1; u >= 0; --u) {  // from the top: slot u is read before it is written
+        const uint4 raw = kr[u];
+        Tr::widen(raw, kr[2 * u], kr[2 * u + 1]);
+      }
+    }
     if constexpr (kKLds) {
       // through the wave's LDS tile (rows padded by 16 bytes: both the row
       // writes and the column reads below hit every bank once) into the
@@ -741,7 +827,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   eng.init(lane);
   const int myrow = 16 * cgroup + eng.col;
   const bool valid = myrow < R;
-  eng.load_q(static_cast<const unsigned char*>(p.q) + row_of(valid ? myrow : 0) * RB, valid);
+  eng.load_q(static_cast<const unsigned char*>(p.q) + row_of(valid ? myrow : 0) * Eng::QB, valid);
   eng.lim = valid ? L - p.q_len + token_of(myrow) : L - 1;
   eng.reset();
   __syncthreads();
@@ -758,11 +844,19 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
     const uint32_t phys = (uint32_t)s_bt[u / BS - (uint32_t)lb0];
     return (uint64_t)(phys * BS + (u % BS)) * slot_bytes;
   };
+  // e4m3 pools: the KV head's K scale multiplies every score, its V scale
+  // the output (applied once, after the weighted sums)
+  float scale_log2 = p.scale_log2;
+  float v_scale = 1.0f;
+  if constexpr (Eng::kF8) {
+    scale_log2 *= p.k_scale[kvh];
+    v_scale = p.v_scale[kvh];
+  }
   // the loop is compiled four ways (load kind x causal limit), chosen per item
   auto tiles = [&](auto nt, auto causal) {
     for (int cs = t_begin + wi * kTile; cs < t_end; cs += wpg * kTile)
       eng.template step<decltype(nt)::value, decltype(causal)::value>(kbase, vbase, cs, t_end - 1, slot_bytes,
-                                                                      p.scale_log2, row_off, kt);
+                                                                      scale_log2, row_off, kt);
   };
   using Yes = std::true_type;
   using No = std::false_type;
@@ -781,6 +875,19 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   // items taken one after the other (the KV heads of the same tokens) start
   // close together in time.
   if (draw && tid == 0) ticket = take_ticket(p.work, p.epoch);
+  // num / den per element (times the V scale of an e4m3 pool); 0 for a row
+  // that saw no position
+  auto finish = [&](float4 num, float den) -> float4 {
+    if (!(den > 0.0f)) return make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 o = make_float4(num.x / den, num.y / den, num.z / den, num.w / den);
+    if constexpr (Eng::kF8) {
+      o.x *= v_scale;
+      o.y *= v_scale;
+      o.z *= v_scale;
+      o.w *= v_scale;
+    }
+    return o;
+  };
   const int OST = o_stride(D);
   float* s_o = reinterpret_cast<float*>(smem);
   float* s_m = reinterpret_cast<float*>(smem + lds_main);
@@ -833,10 +940,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
     }
     const size_t row = row_of(r);
     if (nparts <= 1) {
-      // 0: a row that saw no position
-      store_out4<Tag>(p, row * D + d,
-                      den > 0.0f ? make_float4(num.x / den, num.y / den, num.z / den, num.w / den)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f));
+      store_out4<Tag>(p, row * D + d, finish(num, den));
     } else {
       // agent-scope stores: written through to where every XCD reads them.
       // A partial's D values are kept as its quads' (0, 1) pairs, then their
@@ -917,9 +1021,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
         num.w += wq * hi_of(ob[j]);
       }
     }
-    store_out4<Tag>(p, row * D + d,
-                    den > 0.0f ? make_float4(num.x / den, num.y / den, num.z / den, num.w / den)
-                               : make_float4(0.f, 0.f, 0.f, 0.f));
+    store_out4<Tag>(p, row * D + d, finish(num, den));
   }
 }
 
@@ -1009,7 +1111,8 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   const int span = p.partition < p.max_seq_len ? p.partition : p.max_seq_len;
   const void* kfn = reinterpret_cast<const void*>(&decode_partition_kernel<Tag, D, BS>);
   const size_t q_row = (size_t)p.q_len * p.num_heads * D;  // elements per sequence
-  const size_t out_elem = p.out_f32 ? 4 : (size_t)Tag::kBytes;
+  const size_t q_elem = (size_t)KV<Tag>::kQBytes;  // the output, unless fp32, has the query's type
+  const size_t out_elem = p.out_f32 ? 4 : q_elem;
   // Launches of at most `chunk` sequences each, in order on the stream; they
   // share the workspace (header, partials, arrival words). The chunk keeps the LDS of a
   // workgroup (its plan grows with the sequences) within half a CU's 160 KiB,
@@ -1024,7 +1127,7 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
     DecodeParams c = p;
     c.epoch = next_launch_epoch();  // each launch tags its own item counter
     c.num_seqs = p.num_seqs - s0 < chunk ? p.num_seqs - s0 : chunk;
-    c.q = static_cast<const unsigned char*>(p.q) + (size_t)s0 * q_row * Tag::kBytes;
+    c.q = static_cast<const unsigned char*>(p.q) + (size_t)s0 * q_row * q_elem;
     c.out = static_cast<unsigned char*>(p.out) + (size_t)s0 * q_row * out_elem;
     c.block_table = p.block_table + (size_t)s0 * p.max_blocks;
     c.seq_lens = p.seq_lens + s0;
@@ -1062,12 +1165,16 @@ hipError_t launch_d(const DecodeParams& p, int d, int bs, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, int block_size,
-                         hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int query_dtype, int head_dim,
+                         int block_size, hipStream_t stream) {
   switch (kv_dtype) {
     case 0: return launch_d<F32Tag>(p, head_dim, block_size, stream);
     case 1: return launch_d<F16Tag>(p, head_dim, block_size, stream);
     case 2: return launch_d<BF16Tag>(p, head_dim, block_size, stream);
+    case 3:
+      if (query_dtype == 1) return launch_d<E4M3F16Tag>(p, head_dim, block_size, stream);
+      if (query_dtype == 2) return launch_d<E4M3BF16Tag>(p, head_dim, block_size, stream);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

@@ -21,6 +21,8 @@ struct DecodeParams {
                   // values of one partial: the (0, 1) pairs of its quads, then the (2, 3) pairs
   float* ws_ml;   // [S, q_len, H, NP, 2] (running max in log2 units, sum of weights)
   unsigned long long* arrive;  // [S, Hkv] (epoch << 32) | partitions done (split only)
+  const float* k_scale;  // [Hkv] e4m3 pools: value = code * scale (else unused)
+  const float* v_scale;  // [Hkv]
   int num_seqs;
   int q_len;           // new tokens per sequence (1: decode); query and out are
                        // [S, q_len, H, D]; token j sees positions <= L - q_len + j
@@ -52,8 +54,17 @@ constexpr int kMaxSeqsPerLaunch = 2048;
 // A fresh epoch for one launch of the decode kernel (see DecodeParams::work).
 uint32_t next_launch_epoch();
 
-hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim,
+// kv_dtype: 0 fp32, 1 fp16, 2 bf16 (the query's type too), 3 e4m3 with a
+// query of type query_dtype (1 fp16 or 2 bf16).
+hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int query_dtype, int head_dim,
                          int block_size, hipStream_t stream);
+
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value,
+                                        void* key_cache, void* value_cache,
+                                        const int64_t* slot_mapping, const float* k_scale,
+                                        const float* v_scale, int num_tokens,
+                                        int num_kv_heads, int head_dim, int src_dtype,
+                                        int64_t num_slots, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value,
                                     void* key_cache, void* value_cache,

@@ -110,6 +110,38 @@ def test_multi_query_host_checks(kw, code):
     assert _multi_query(**kw) == code
 
 
+def _decode_fp8(**kw):
+    a = dict(out=FAKE, query=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, sl=FAKE, S=4, H=32,
+             Hkv=8, D=128, bs=16, NB=100, MB=16, maxlen=256, scale=0.088, qdt=2, outdt=2, P=0,
+             ws=None, wsb=0)
+    a.update(kw)
+    return _lib.lib().paged_attn_decode_fp8(a["out"], a["query"], a["k"], a["v"], a["ks"], a["vs"],
+                                            a["bt"], a["sl"], a["S"], a["H"], a["Hkv"], a["D"],
+                                            a["bs"], a["NB"], a["MB"], a["maxlen"], a["scale"],
+                                            a["qdt"], a["outdt"], a["P"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S=0, out=None), OK),
+    (dict(ks=None), NULL),
+    (dict(vs=None), NULL),
+    (dict(qdt=0), UNSUP),                      # fp32 query over an e4m3 pool
+    (dict(qdt=3), UNSUP),
+    (dict(qdt=2, outdt=1), UNSUP),             # bf16 query, fp16 output
+    (dict(D=96), UNSUP),
+    (dict(qdt=1, outdt=0), WS),                # fp16 query, fp32 output: valid, no workspace
+    (dict(qdt=2, outdt=2), WS),
+])
+def test_decode_fp8_host_checks(kw, code):
+    assert _decode_fp8(**kw) == code
+
+
+def test_sixteen_bit_entry_points_refuse_e4m3_pools():
+    assert _decode(kvdt=3, outdt=3) == UNSUP
+    assert _decode(kvdt=3, outdt=0) == UNSUP
+    assert _multi_query(kvdt=3, outdt=0) == UNSUP
+
+
 def test_multi_query_workspace_sizing():
     L = _lib.lib()
     hdr = 256
@@ -161,6 +193,18 @@ def test_partition_and_workspace_sizing():
     (lambda L: L.reshape_and_cache(FAKE, ctypes.c_void_p(0x1002), FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 2,
                                    None), SHAPE),                                  # misaligned
     (lambda L: L.copy_blocks(FAKE, FAKE, FAKE, 0, 10, 16, 8, 128, 2, None), OK),
+    (lambda L: L.copy_blocks(FAKE, FAKE, FAKE, 0, 10, 16, 8, 128, 3, None), OK),   # e4m3 bytes
+    (lambda L: L.copy_blocks(FAKE, FAKE, FAKE, 3, 10, 16, 8, 128, 4, None), UNSUP),
+    (lambda L: L.reshape_and_cache_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 16, 10, 2,
+                                       None), OK),
+    (lambda L: L.reshape_and_cache_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 8, 128, 16, 10, 2,
+                                       None), NULL),
+    (lambda L: L.reshape_and_cache_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 3,
+                                       None), UNSUP),                       # source must be 16/32-bit
+    (lambda L: L.reshape_and_cache_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 96, 16, 10, 2,
+                                       None), UNSUP),
+    (lambda L: L.reshape_and_cache_fp8(FAKE, FAKE, ctypes.c_void_p(0x1001), FAKE, FAKE, FAKE, FAKE, 4,
+                                       8, 128, 16, 10, 2, None), SHAPE),
     (lambda L: L.copy_blocks(FAKE, None, FAKE, 3, 10, 16, 8, 128, 2, None), NULL),
     (lambda L: L.copy_blocks(FAKE, FAKE, FAKE, 3, 0, 16, 8, 128, 2, None), SHAPE),
     (lambda L: L.copy_blocks(FAKE, FAKE, FAKE, 3, 10, 12, 8, 128, 2, None), UNSUP),

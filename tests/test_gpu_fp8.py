@@ -1,0 +1,231 @@
+"""GPU parity of the e4m3 KV cache, through the C ABI: the quantising scatter
+bit-exact against the oracle (over whole pools and on rounding ties,
+saturation and special values), every finite code decoded exactly, and
+decode / multi-query over e4m3 pools against the oracle's attention over the
+same codes (bars of the query's type: 2e-3 fp16, 8e-3 bf16)."""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import fp8_kv as F
+import paged_kv_cache_154_amd as pkv
+from paged_kv_cache_154_amd import workloads as W
+from gpu_common import DEV, TOL, max_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def scales_for(pool: torch.Tensor) -> torch.Tensor:
+    """A scale per KV head: the largest finite magnitude over 448 (a caller's
+    calibration; an input here, not part of the method)."""
+    a = torch.nan_to_num(pool.float().abs(), nan=0.0, posinf=0.0, neginf=0.0)
+    return (a.amax(dim=(0, 1, 3)) / 448.0).clamp_min(1e-6).contiguous()
+
+
+def quantise_pools(wl):
+    """The workload's 16-bit pools as e4m3 pools, on the GPU (one scatter
+    over every slot) and in the oracle; the two must agree bit for bit.
+    Then the step's new tokens, if any, by both. Returns device pools,
+    oracle pools and the scales."""
+    NB, bs, Hkv, D = wl.key_cache.shape
+    ks, vs = scales_for(wl.key_cache), scales_for(wl.value_cache)
+    all_slots = torch.arange(NB * bs, dtype=torch.int64)
+    flat_k = wl.key_cache.reshape(NB * bs, Hkv, D).contiguous()
+    flat_v = wl.value_cache.reshape(NB * bs, Hkv, D).contiguous()
+    gk = torch.empty((NB, bs, Hkv, D), dtype=torch.uint8, device=DEV)
+    gv = torch.empty_like(gk)
+    ks_d, vs_d = ks.to(DEV), vs.to(DEV)
+    pkv.reshape_and_cache_fp8(flat_k.to(DEV), flat_v.to(DEV), gk, gv, all_slots.to(DEV), ks_d, vs_d)
+    ok, ov = F.reshape_and_cache_fp8(flat_k, flat_v, np.zeros((NB, bs, Hkv, D), np.uint8),
+                                     np.zeros((NB, bs, Hkv, D), np.uint8), all_slots.numpy(),
+                                     ks.numpy(), vs.numpy())
+    if wl.slot_mapping is not None:
+        sm = torch.from_numpy(wl.slot_mapping)
+        pkv.reshape_and_cache_fp8(wl.new_key.to(DEV), wl.new_value.to(DEV), gk, gv, sm.to(DEV),
+                                  ks_d, vs_d)
+        ok, ov = F.reshape_and_cache_fp8(wl.new_key, wl.new_value, ok, ov, sm.numpy(),
+                                         ks.numpy(), vs.numpy())
+    torch.cuda.synchronize()
+    assert np.array_equal(gk.cpu().numpy(), ok), "K pool differs from the oracle's quantisation"
+    assert np.array_equal(gv.cpu().numpy(), ov), "V pool differs from the oracle's quantisation"
+    return gk, gv, ok, ov, ks, vs
+
+
+@pytest.mark.parametrize("src", [torch.float32, torch.float16, torch.bfloat16])
+def test_quantising_scatter_bit_exact_on_ties_saturation_and_specials(src):
+    """Rows built from e4m3 midpoints (exact ties: scale a power of two),
+    values past 448 x scale, subnormal-range values, NaN, infinities, signed
+    zeros and random values, scattered to random slots; untouched bytes keep
+    their fill."""
+    rng = np.random.default_rng(5)
+    Hkv, D, bs, NB = 2, 128, 16, 12
+    t = F.e4m3_value_table()[:0x7F]
+    mids = (t[:-1] + t[1:]) / 2                                   # 126 ties
+    specials = [np.nan, np.inf, -np.inf, 0.0, -0.0, 1e4, -1e4, 2.0 ** -12, -(2.0 ** -11), 447.9]
+    T = 6
+    x = rng.standard_normal((T, Hkv, D)) * 3.0
+    x[0, 0, :126] = mids[:126] if D >= 126 else mids[:D]
+    x[1, 1, :126] = -mids[:126]
+    x[2, 0, :len(specials)] = specials
+    x[3] *= 1e-3
+    key = torch.from_numpy(x.astype(np.float32)).to(src)
+    value = torch.from_numpy((x[::-1] * 0.5).copy().astype(np.float32)).to(src)
+    ks = torch.tensor([1.0, 0.25], dtype=torch.float32)          # powers of two: ties stay exact
+    vs = torch.tensor([2.0 ** -3, 4.0], dtype=torch.float32)
+    slots = torch.tensor([5, 40, -1, 191, 77, 16], dtype=torch.int64)
+    fill = rng.integers(0, 256, size=(NB, bs, Hkv, D), dtype=np.uint8)
+    gk = torch.from_numpy(fill.copy()).to(DEV)
+    gv = torch.from_numpy(fill[::-1].copy()).to(DEV)
+    say(f"fp8 scatter specials, source {src}")
+    pkv.reshape_and_cache_fp8(key.to(DEV), value.to(DEV), gk, gv, slots.to(DEV), ks.to(DEV),
+                              vs.to(DEV))
+    torch.cuda.synchronize()
+    ok, ov = F.reshape_and_cache_fp8(key, value, fill.copy(), fill[::-1].copy(), slots.numpy(),
+                                     ks.numpy(), vs.numpy())
+    assert np.array_equal(gk.cpu().numpy(), ok)
+    assert np.array_equal(gv.cpu().numpy(), ov)
+
+
+def test_every_finite_code_decodes_exactly():
+    """seq_len 1: the output is the single V row, code x v_scale, in fp32 bit
+    for bit; the V rows hold every finite code."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)  # 254
+    Hkv, D, bs = 2, 128, 16
+    S = 2                                      # 2 sequences x 2 KV heads x 128 = 512 >= 254
+    NB = 4
+    vpool = np.zeros((NB, bs, Hkv, D), np.uint8)
+    flat = np.resize(codes, S * Hkv * D).reshape(S, Hkv, D)
+    vpool[1, 0] = flat[0]
+    vpool[3, 0] = flat[1]
+    kpool = np.random.default_rng(6).integers(0, 0x7F, size=(NB, bs, Hkv, D), dtype=np.uint8)
+    vs = torch.tensor([0.5, 3.0], dtype=torch.float32)
+    ks = torch.tensor([1.0, 1.0], dtype=torch.float32)
+    bt = torch.tensor([[1], [3]], dtype=torch.int32)
+    sl = torch.tensor([1, 1], dtype=torch.int32)
+    H = 4
+    q = torch.randn(S, H, D).to(torch.bfloat16)
+    for qdt in (torch.bfloat16, torch.float16):
+        say(f"fp8 every code, query {qdt}")
+        out = torch.empty(S, H, D, dtype=torch.float32, device=DEV)
+        pkv.paged_attn_decode_fp8(out, q.to(qdt).to(DEV), torch.from_numpy(kpool).to(DEV),
+                                  torch.from_numpy(vpool).to(DEV), ks.to(DEV), vs.to(DEV),
+                                  bt.to(DEV), sl.to(DEV), 0.1, 16)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        for s in range(S):
+            for h in range(H):
+                j = h // (H // Hkv)
+                expect = F.e4m3_decode(flat[s, j]) * float(vs[j])
+                assert np.array_equal(got[s, h], expect), (s, h)
+
+
+FP8_SMALL = [
+    # id, query dtype, D, bs, H, Hkv, lens, partition
+    ("bf16q_d128_bs16_g4", torch.bfloat16, 128, 16, 32, 8, [1, 15, 16, 17, 33, 200, 1000], 0),
+    ("f16q_d128_bs32_g8", torch.float16, 128, 32, 64, 8, [2, 31, 32, 33, 513], 0),
+    ("bf16q_d64_bs8_g1", torch.bfloat16, 64, 8, 4, 4, [7, 8, 9, 77, 640], 0),
+    ("f16q_d64_bs16_g16", torch.float16, 64, 16, 16, 1, [1, 40, 300], 0),
+    ("bf16q_d128_bs8_g4_split128", torch.bfloat16, 128, 8, 32, 8, [8, 127, 128, 129, 1500], 128),
+    ("f16q_d128_bs16_g2_split16", torch.float16, 128, 16, 8, 4, [1, 16, 17, 80, 333], 16),
+]
+
+
+@pytest.mark.parametrize("case", FP8_SMALL, ids=[c[0] for c in FP8_SMALL])
+def test_fp8_decode_matches_oracle(case):
+    name, qdt, D, bs, H, Hkv, lens, P = case
+    wl = W.custom(zlib.crc32(name.encode()) % 10000 + 500, seq_lens=lens, num_heads=H,
+                  num_kv_heads=Hkv, head_dim=D, block_size=bs, dtype=qdt, partition_size=P,
+                  new_token=True)
+    gk, gv, ok, ov, ks, vs = quantise_pools(wl)
+    ref = F.decode_fp8(wl.query, ok, ov, ks.numpy(), vs.numpy(), wl.block_table, wl.seq_lens,
+                       wl.scale)
+    q = wl.query.to(DEV)
+    bt = torch.from_numpy(wl.block_table).to(DEV)
+    sl = torch.from_numpy(wl.seq_lens).to(DEV)
+    for out_dt in (qdt, torch.float32):
+        say(f"fp8 decode {name} out={out_dt}")
+        out = torch.empty(wl.query.shape, dtype=out_dt, device=DEV)
+        pkv.paged_attn_decode_fp8(out, q, gk, gv, ks.to(DEV), vs.to(DEV), bt, sl, wl.scale,
+                                  wl.max_seq_len, P)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all()
+        err = max_err(out, ref)
+        assert err <= TOL[qdt], (name, out_dt, err)
+
+
+@pytest.mark.parametrize("Q,P", [(4, 0), (8, 64), (3, 16)])
+def test_fp8_multi_query_matches_oracle(Q, P):
+    lens = [Q, Q + 1, 63, 64, 65, 300, 1100]
+    wl = W.custom(600 + Q, seq_lens=lens, num_heads=32, num_kv_heads=8, head_dim=128,
+                  block_size=16, dtype=torch.bfloat16, partition_size=P, new_token=True, q_len=Q)
+    gk, gv, ok, ov, ks, vs = quantise_pools(wl)
+    ref = F.multi_query_fp8(wl.query, ok, ov, ks.numpy(), vs.numpy(), wl.block_table,
+                            wl.seq_lens, wl.scale)
+    say(f"fp8 multi-query q_len={Q} P={P}")
+    out = torch.empty(wl.query.shape, dtype=torch.float32, device=DEV)
+    pkv.paged_attn_multi_query_fp8(out, wl.query.to(DEV), gk, gv, ks.to(DEV), vs.to(DEV),
+                                   torch.from_numpy(wl.block_table).to(DEV),
+                                   torch.from_numpy(wl.seq_lens).to(DEV), wl.scale,
+                                   wl.max_seq_len, P)
+    torch.cuda.synchronize()
+    assert max_err(out, ref) <= TOL[torch.bfloat16]
+
+
+def test_fp8_llama3_8b_shaped_step():
+    """The Llama-3-8B-shaped layer with an e4m3 cache: the whole 20 000-block
+    pool quantised on the GPU (one scatter over every slot) and the step's
+    64 new tokens scattered, then decode in the launch bench.py times. The
+    oracle quantises the blocks of sampled sequences itself (compared bit
+    for bit with the GPU's bytes of those blocks) and decodes them."""
+    wl = W.llama3_8b()
+    NB, bs, Hkv, D = wl.key_cache.shape
+    ks, vs = scales_for(wl.key_cache), scales_for(wl.value_cache)
+    say("fp8 Llama-3-8B shape: quantising the pools on the GPU")
+    gk = torch.empty((NB, bs, Hkv, D), dtype=torch.uint8, device=DEV)
+    gv = torch.empty_like(gk)
+    all_slots = torch.arange(NB * bs, dtype=torch.int64, device=DEV)
+    pkv.reshape_and_cache_fp8(wl.key_cache.reshape(-1, Hkv, D).to(DEV),
+                              wl.value_cache.reshape(-1, Hkv, D).to(DEV), gk, gv, all_slots,
+                              ks.to(DEV), vs.to(DEV))
+    sm = torch.from_numpy(wl.slot_mapping)
+    pkv.reshape_and_cache_fp8(wl.new_key.to(DEV), wl.new_value.to(DEV), gk, gv, sm.to(DEV),
+                              ks.to(DEV), vs.to(DEV))
+    out32 = torch.empty(wl.query.shape, dtype=torch.float32, device=DEV)
+    out16 = torch.empty(wl.query.shape, dtype=torch.bfloat16, device=DEV)
+    for out in (out32, out16):
+        pkv.paged_attn_decode_fp8(out, wl.query.to(DEV), gk, gv, ks.to(DEV), vs.to(DEV),
+                                  torch.from_numpy(wl.block_table).to(DEV),
+                                  torch.from_numpy(wl.seq_lens).to(DEV), wl.scale,
+                                  wl.max_seq_len, wl.partition_size)
+    torch.cuda.synchronize()
+
+    order = np.argsort(wl.seq_lens)
+    seqs = sorted(set(order[:3].tolist() + order[-3:].tolist() + [17, 41]))
+    # the oracle's own pool of the sampled sequences' blocks (compact, remapped)
+    blocks = sorted({int(b) for s_ in seqs
+                     for b in wl.block_table[s_, :(int(wl.seq_lens[s_]) + bs - 1) // bs]})
+    remap = {b: i for i, b in enumerate(blocks)}
+    idx = torch.tensor(blocks, dtype=torch.int64)
+    ok = F.quantize(wl.key_cache[idx], ks.numpy().reshape(1, 1, Hkv, 1))
+    ov = F.quantize(wl.value_cache[idx], vs.numpy().reshape(1, 1, Hkv, 1))
+    new_slots = []
+    for i_, slot in enumerate(wl.slot_mapping.tolist()):
+        b, o = divmod(slot, bs)
+        new_slots.append(remap[b] * bs + o if b in remap else -1)
+    ok, ov = F.reshape_and_cache_fp8(wl.new_key, wl.new_value, ok, ov, np.array(new_slots),
+                                     ks.numpy(), vs.numpy())
+    assert np.array_equal(gk[idx.to(DEV)].cpu().numpy(), ok), "K blocks differ from the oracle's"
+    assert np.array_equal(gv[idx.to(DEV)].cpu().numpy(), ov), "V blocks differ from the oracle's"
+    table = np.zeros_like(wl.block_table)
+    for s_ in seqs:
+        nb_ = (int(wl.seq_lens[s_]) + bs - 1) // bs
+        table[s_, :nb_] = [remap[int(b)] for b in wl.block_table[s_, :nb_]]
+    ref = F.decode_fp8(wl.query, ok, ov, ks.numpy(), vs.numpy(), table, wl.seq_lens, wl.scale,
+                       seqs=seqs)
+    for out in (out32, out16):
+        err = max_err(out, ref, seqs)
+        say(f"  out={out.dtype} max_abs_err={err:.3g} on {len(seqs)} seqs")
+        assert err <= TOL[torch.bfloat16]

@@ -22,7 +22,7 @@ def test_decode_kernels_do_not_spill(tmp_path):
     subprocess.run(cmd, check=True, capture_output=True, timeout=600)
     text = out.read_text()
     metas = re.findall(r"\.name:\s+(\S*decode_partition_kernel\S*)(.*?)(?=\n\s+- \.|\Z)", text, flags=re.S)
-    assert len(metas) == 18, "3 dtypes x 2 head dims x 3 block sizes"
+    assert len(metas) == 30, "5 K/V-query types x 2 head dims x 3 block sizes"
     for name, meta in metas:
         vspill = int(re.search(r"\.vgpr_spill_count:\s+(\d+)", meta).group(1))
         scratch = int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", meta).group(1))
