@@ -320,6 +320,58 @@ def per_config(pkv, W, dev, calls=200, warm=20):
     return res
 
 
+def fp8_scales(pool):
+    """A scale per KV head for an e4m3 cache: the largest finite magnitude of
+    the 16-bit pool over 448 (a caller's calibration, outside the method)."""
+    import torch
+    a = torch.nan_to_num(pool.float().abs(), nan=0.0, posinf=0.0, neginf=0.0)
+    return (a.amax(dim=(0, 1, 3)) / 448.0).clamp_min(1e-6).contiguous()
+
+
+def cpu_baseline_fp8(wl, ks, vs, n_seqs=8, budget_s=20.0):
+    """The CPU oracle on the e4m3 step for a sample of the batch: the first
+    n_seqs sequences' blocks quantised beforehand (not timed), then the timed
+    oracle step: the quantising scatter of their new tokens and fp8 decode."""
+    import numpy as np
+    import torch
+
+    from oracle import fp8_kv as F
+    bs = wl.block_size
+    Hkv = wl.num_kv_heads
+    seqs = list(range(min(n_seqs, wl.num_seqs)))
+    blocks = sorted({int(b) for s_ in seqs
+                     for b in wl.block_table[s_, :(int(wl.seq_lens[s_]) + bs - 1) // bs]})
+    remap = {b: i for i, b in enumerate(blocks)}
+    idx = torch.tensor(blocks, dtype=torch.int64)
+    k_s, v_s = ks.cpu().numpy(), vs.cpu().numpy()
+    kq = F.quantize(wl.key_cache[idx], k_s.reshape(1, 1, Hkv, 1))
+    vq = F.quantize(wl.value_cache[idx], v_s.reshape(1, 1, Hkv, 1))
+    table = np.zeros_like(wl.block_table[:len(seqs)])
+    for s_ in seqs:
+        nb_ = (int(wl.seq_lens[s_]) + bs - 1) // bs
+        table[s_, :nb_] = [remap[int(b)] for b in wl.block_table[s_, :nb_]]
+    tok = [i for i, sl_ in enumerate(wl.slot_mapping.tolist()) if sl_ // bs in remap]
+    slots = np.array([remap[wl.slot_mapping[i] // bs] * bs + wl.slot_mapping[i] % bs for i in tok])
+    lens = wl.seq_lens[:len(seqs)]
+    times = []
+    while len(times) < 3 and sum(times) < budget_s:
+        t0 = time.perf_counter()
+        k2, v2 = F.reshape_and_cache_fp8(wl.new_key[tok], wl.new_value[tok], kq, vq, slots, k_s, v_s)
+        attn = F.decode_fp8 if wl.q_len == 1 else F.multi_query_fp8
+        attn(wl.query[:len(seqs)], k2, v2, k_s, v_s, table, lens, wl.scale)
+        times.append(time.perf_counter() - t0)
+        log(f"cpu oracle fp8 step {len(times)}: {times[-1]:.2f} s")
+    t = statistics.median(times)
+    nbytes = int(lens.astype(np.int64).sum()) * 2 * Hkv * wl.head_dim
+    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s",
+            "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": (f"the e4m3 step for the first {len(seqs)} of the {wl.num_seqs} sequences "
+                       f"({int(lens.sum())} tokens: oracle quantising scatter of their new tokens + "
+                       f"fp64 decode over the dequantised codes), median of {len(times)} run(s), "
+                       f"{t:.2f} s"),
+            "seconds_per_step": round(t, 3)}
+
+
 def cpu_baseline(wl, budget_s=20.0):
     """The CPU oracle on the same step (scatter + attention of every sequence),
     wall clock, median over repeats within about budget_s seconds."""
@@ -362,6 +414,9 @@ def main():
     ap.add_argument("--q-len", type=int, default=1,
                     help="new tokens per sequence in the timed step: >1 times the "
                          "multi-query (speculative verification) pass instead of decode")
+    ap.add_argument("--kv-fp8", action="store_true",
+                    help="an e4m3 KV cache (scales per KV head from the 16-bit pools): the "
+                         "step is reshape_and_cache_fp8 + paged_attn_decode_fp8")
     ap.add_argument("--multi-query", action="store_true",
                     help="also time the multi-query (speculative verification) pass, "
                          "q_len 2, 4 and 8, on the same lengths")
@@ -406,6 +461,33 @@ def main():
     nk, nv = wl.new_key.to(dev), wl.new_value.to(dev)
     slots = torch.from_numpy(wl.slot_mapping).to(dev)
     kc0, vc0 = wl.key_cache.to(dev), wl.value_cache.to(dev)
+    fp8 = args.kv_fp8
+    if fp8:
+        # setup, not timed: a scale per KV head (largest magnitude / 448, the
+        # caller's calibration) and every slot of the pools quantised
+        ks, vs = fp8_scales(kc0), fp8_scales(vc0)
+        k8 = torch.empty(kc0.shape, dtype=torch.uint8, device=dev)
+        v8 = torch.empty_like(k8)
+        D_ = wl.head_dim
+        pkv.reshape_and_cache_fp8(kc0.view(-1, Hkv, D_), vc0.view(-1, Hkv, D_), k8, v8,
+                                  torch.arange(NB * bs, dtype=torch.int64, device=dev), ks, vs)
+        del kc0, vc0
+        kc0, vc0 = k8, v8
+        attn_f8 = pkv.paged_attn_decode_fp8 if Q == 1 else pkv.paged_attn_multi_query_fp8
+        attn_name = attn_name.replace("paged_attn_decode", "paged_attn_decode_fp8").replace(
+            "paged_attn_multi_query", "paged_attn_multi_query_fp8")
+
+        def scatter(kc, vc):
+            pkv.reshape_and_cache_fp8(nk, nv, kc, vc, slots, ks, vs)
+
+        def attend(kc, vc):
+            attn_f8(out, q, kc, vc, ks, vs, bt, sl, wl.scale, wl.max_seq_len, P, ws)
+    else:
+        def scatter(kc, vc):
+            pkv.reshape_and_cache(nk, nv, kc, vc, slots)
+
+        def attend(kc, vc):
+            attn(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
     layers = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(args.layers - 1)]
     out = torch.empty(wl.query.shape, dtype=wl.dtype, device=dev)
     ws = pkv.workspace_for(q, kc0, wl.max_seq_len, P)
@@ -414,8 +496,8 @@ def main():
 
     def step(i):
         kc, vc = layers[i % len(layers)]
-        pkv.reshape_and_cache(nk, nv, kc, vc, slots)
-        attn(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
+        scatter(kc, vc)
+        attend(kc, vc)
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
@@ -432,9 +514,9 @@ def main():
     t_start.record(stream)
     for i in range(args.steps):
         kc, vc = layers[i % len(layers)]
-        pkv.reshape_and_cache(nk, nv, kc, vc, slots)
+        scatter(kc, vc)
         ev[i][0].record(stream)
-        attn(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
+        attend(kc, vc)
         ev[i][1].record(stream)
     t_stop.record(stream)
     torch.cuda.synchronize()
@@ -451,20 +533,20 @@ def main():
     # and dispatch latency to each call; this is closer to the kernel time.
     for i in range(args.warmup):
         kc, vc = layers[i % len(layers)]
-        attn(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
+        attend(kc, vc)
     b0 = torch.cuda.Event(enable_timing=True)
     b1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     b0.record(stream)
     for i in range(args.steps):
         kc, vc = layers[i % len(layers)]
-        attn(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
+        attend(kc, vc)
     b1.record(stream)
     torch.cuda.synchronize()
     dec_bb = b0.elapsed_time(b1) / args.steps
     log(f"decode back to back: {dec_bb * 1e3:.1f} us per call")
 
-    kv = wl.kv_bytes()
+    kv = wl.kv_bytes() // (2 if fp8 else 1)      # e4m3: one byte per element
     value = kv / (ms_step * 1e-3) / 1e9
     achieved = kv / (dec_avg * 1e-3) / 1e9
     res = {
@@ -478,12 +560,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "e4m3 KV, bf16 query" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": ("llama3_8b_bf16: Llama-3-8B-shaped single-layer decode" if Q == 1 else
-                         f"llama3_8b_bf16_q{Q}: Llama-3-8B-shaped single-layer verification "
-                         f"of {Q} new tokens per sequence"),
+            "workload": (("llama3_8b_e4m3" if fp8 else "llama3_8b_bf16")
+                         + ("" if Q == 1 else f"_q{Q}") + ": Llama-3-8B-shaped single-layer "
+                         + ("decode" if Q == 1 else f"verification of {Q} new tokens per sequence")
+                         + (", e4m3 KV cache (a scale per KV head)" if fp8 else "")),
             "num_seqs": S, "num_heads": H, "num_kv_heads": Hkv, "head_dim": D,
             "block_size": bs, "num_blocks": NB, "seq_lens": "uniform [512, 4096], seed 1542",
             "tokens": wl.num_tokens, "kv_bytes_per_step": kv,
@@ -503,8 +586,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic("decode_llama3_8b_bf16" if Q == 1 else
-                                        f"multi_query_q{Q}_llama3_8b_bf16"),
+            "traffic": measured_traffic(("decode" if Q == 1 else f"multi_query_q{Q}")
+                                        + ("_llama3_8b_e4m3" if fp8 else "_llama3_8b_bf16")),
             "kernel": f"{attn_name} (decode_partition_kernel)",
         },
         "cpu_baseline": None,
@@ -525,7 +608,7 @@ def main():
         res["per_config"] = per_config(pkv, W, dev)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the same step")
-        res["cpu_baseline"] = cpu_baseline(wl)
+        res["cpu_baseline"] = cpu_baseline_fp8(wl, ks, vs) if fp8 else cpu_baseline(wl)
     print(json.dumps(res), flush=True)
 
 
