@@ -20,6 +20,10 @@ Pins (checked by ``tests/test_oracle_*.py`` without a GPU):
     §2.3); every other byte unchanged.
   * ``copy_blocks``: destination equals the pre-call source, all else
     unchanged, and decode after a copy-on-write remap equals decode before.
+  * ``swap_blocks``: destination blocks equal the source blocks, all else
+    unchanged, the source untouched; swapping out and back in to other
+    blocks, with the block table remapped, leaves decode unchanged; within
+    one pool it is ``copy_blocks``.
   * ``multi_query`` (q_len new tokens per sequence): row j equals ``decode``
     of the sequence truncated to the positions it sees; one new token is
     decode; changing position p changes exactly the rows that see it.
@@ -48,5 +52,6 @@ from .paged_attention import (  # noqa: F401
     multi_query,
     multi_query_one,
     reshape_and_cache,
+    swap_blocks,
 )
 from . import fp8_kv  # noqa: F401,E402

@@ -260,6 +260,28 @@ def copy_blocks(key_cache, value_cache, block_mapping):
     return kc, vc
 
 
+def swap_blocks(src_key, src_value, dst_key, dst_value, block_mapping):
+    """Move whole blocks (K and V) from one pool to another; returns the new
+    destination pools.
+
+    Preemption by swapping: a sequence's blocks are copied from GPU memory to
+    a CPU swap space and freed, and copied back (to any free GPU blocks) when
+    it resumes ([EI] §3.2; the scheduler's blocks_to_swap_out and
+    blocks_to_swap_in outputs in [EI] §3.1; the swap space of [VC] §4.2.4).
+    Read here as a list of (source block, destination block) pairs between
+    two pools of the same block layout; the source is not changed.
+    """
+    dk = dst_key.clone()
+    dv = dst_value.clone()
+    kb, vb = _bits(dk), _bits(dv)
+    sk, sv = _bits(src_key), _bits(src_value)
+    pairs = _to_np_int(block_mapping).reshape(-1, 2)
+    for src, dst in pairs:
+        kb[int(dst)] = sk[int(src)]
+        vb[int(dst)] = sv[int(src)]
+    return dk, dv
+
+
 # ----------------------------------------------------------------------------
 # closed forms
 # ----------------------------------------------------------------------------

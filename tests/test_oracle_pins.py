@@ -358,6 +358,57 @@ def test_cow_fork_example_decode_unchanged_by_private_copy():
 
 
 # ----------------------------------------------------------------------------
+# swap_blocks: preemption by swapping to a CPU swap space and back
+# ----------------------------------------------------------------------------
+
+def test_swap_blocks_moves_blocks_between_pools_only():
+    nb, ncpu, bs, Hkv, D = 10, 6, 16, 2, 64
+    gk = torch.randn(nb, bs, Hkv, D).to(torch.bfloat16)
+    gv = torch.randn(nb, bs, Hkv, D).to(torch.bfloat16)
+    ck = torch.full((ncpu, bs, Hkv, D), float("nan")).to(torch.bfloat16)
+    cv = ck.clone()
+    pairs = np.array([[7, 0], [2, 5], [9, 3]])
+    ck2, cv2 = oracle.swap_blocks(gk, gv, ck, cv, pairs)
+    for src, dst in pairs:
+        assert torch.equal(ck2[dst].view(torch.int16), gk[src].view(torch.int16))
+        assert torch.equal(cv2[dst].view(torch.int16), gv[src].view(torch.int16))
+    untouched = [b for b in range(ncpu) if b not in (0, 5, 3)]
+    assert torch.equal(ck2[untouched].view(torch.int16), ck[untouched].view(torch.int16))
+    # within one pool (sources and destinations disjoint) it is copy_blocks
+    inner = np.array([[1, 8], [4, 6]])
+    a = oracle.swap_blocks(gk, gv, gk, gv, inner)
+    b = oracle.copy_blocks(gk, gv, inner)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1].view(torch.int16), b[1].view(torch.int16))
+
+
+def test_swap_out_and_back_in_elsewhere_leaves_decode_unchanged():
+    """A preempted sequence's blocks go to the swap space, the GPU blocks are
+    reused (here: overwritten with NaN), and the blocks come back to other
+    free GPU blocks with the block table remapped: decode is unchanged."""
+    nb, ncpu, bs, Hkv, D = 16, 8, 8, 2, 32
+    torch.manual_seed(1)
+    gk = torch.randn(nb, bs, Hkv, D)
+    gv = torch.randn(nb, bs, Hkv, D)
+    bt = np.array([[3, 5, 1, 0], [2, 7, 4, 6]])
+    lens = np.array([27, 30])
+    q = torch.randn(2, 4, D)
+    before = oracle.decode(q, gk, gv, bt, lens, 0.2)
+    out_pairs = np.array([[b, i] for i, b in enumerate(bt[1])])          # seq 1 -> CPU 0..3
+    ck, cv = oracle.swap_blocks(gk, gv, torch.zeros(ncpu, bs, Hkv, D),
+                                torch.zeros(ncpu, bs, Hkv, D), out_pairs)
+    gk2, gv2 = gk.clone(), gv.clone()
+    gk2[bt[1]] = float("nan")
+    gv2[bt[1]] = float("nan")
+    new_blocks = [9, 15, 12, 10]
+    gk3, gv3 = oracle.swap_blocks(ck, cv, gk2, gv2, np.array([[i, b] for i, b in enumerate(new_blocks)]))
+    bt2 = bt.copy()
+    bt2[1] = new_blocks
+    after = oracle.decode(q, gk3, gv3, bt2, lens, 0.2)
+    assert np.array_equal(before, after)
+
+
+# ----------------------------------------------------------------------------
 # closed forms against the printed numbers
 # ----------------------------------------------------------------------------
 
