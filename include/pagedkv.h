@@ -264,6 +264,30 @@ int reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
                           int block_size, int num_blocks, int src_dtype, hipStream_t stream);
 
 /*
+ * swap_blocks - preemption by swapping ("LLM inference engine internals"
+ * sections 3.1-3.2: the scheduler's blocks_to_swap_out and
+ * blocks_to_swap_in; the CPU swap space of "vLLM core concepts" section
+ * 4.2.4): for each pair (src, dst) of block_mapping, block src of the source
+ * pools (K and V) is copied to block dst of the destination pools. Swapping
+ * out goes from the GPU pools to pools in pinned host memory, swapping in
+ * back to any free GPU blocks (the caller then points the block table at
+ * them). One kernel launch moves every pair, reading or writing host memory
+ * across the host link.
+ *
+ *   src_*, dst_*     [src_num_blocks | dst_num_blocks, block_size, num_kv_heads,
+ *                    head_dim] of dtype; each either device memory or pinned
+ *                    host memory (hipHostMalloc, a torch pin_memory tensor);
+ *                    pageable host memory is refused with PKV_ERR_UNSUPPORTED
+ *   block_mapping    int64 [num_pairs, 2] (src, dst), device or pinned memory
+ * Pairs outside either pool are skipped; destination blocks must be distinct
+ * and, when both pools are the same memory, disjoint from the sources.
+ */
+int swap_blocks(const void* src_key_cache, const void* src_value_cache, void* dst_key_cache,
+                void* dst_value_cache, const int64_t* block_mapping, int num_pairs,
+                int src_num_blocks, int dst_num_blocks, int block_size, int num_kv_heads,
+                int head_dim, int dtype, hipStream_t stream);
+
+/*
  * copy_blocks - copy-on-write block copies: for each pair (src, dst) of
  * block_mapping, the whole physical block src of both pools (every slot, every
  * KV head) is copied to block dst. A block shared by several sequences is

@@ -13,6 +13,8 @@ kernels of ``libpagedkv.so``; there is no Python or CPU fallback.
                            workspace=None)
     reshape_and_cache(key, value, key_cache, value_cache, slot_mapping)
     copy_blocks(key_cache, value_cache, block_mapping)
+    swap_blocks(src_key_cache, src_value_cache, dst_key_cache, dst_value_cache,
+                block_mapping)      # GPU <-> pinned host pools
 
 e4m3 KV cache (pools of uint8 codes, or torch.float8_e4m3fn; fp32 scales
 ``[num_kv_heads]`` for K and for V; the query bf16 or fp16):
@@ -265,6 +267,35 @@ def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor,
                            block_mapping.shape[0], NB, bs, Hkv, D, dtype_code(key_cache.dtype),
                            _stream(key_cache, stream))
     check(st, "copy_blocks")
+
+
+def swap_blocks(src_key_cache: torch.Tensor, src_value_cache: torch.Tensor,
+                dst_key_cache: torch.Tensor, dst_value_cache: torch.Tensor,
+                block_mapping: torch.Tensor, stream=None) -> None:
+    """Copy whole blocks src -> dst (K and V) between two pools, for each row
+    (src, dst) of block_mapping: swapping out to pinned host pools
+    (``pin_memory=True``) and back in. Pools on the GPU or in pinned host
+    memory; the work runs on the stream of the GPU side."""
+    _require(src_key_cache.dim() == 4 and src_value_cache.shape == src_key_cache.shape,
+             "source pool shape")
+    _require(dst_key_cache.dim() == 4 and dst_value_cache.shape == dst_key_cache.shape,
+             "destination pool shape")
+    _require(tuple(src_key_cache.shape[1:]) == tuple(dst_key_cache.shape[1:]),
+             "pools differ in block layout")
+    _require(src_key_cache.dtype == dst_key_cache.dtype == src_value_cache.dtype
+             == dst_value_cache.dtype, "dtypes differ")
+    _require(block_mapping.dtype == torch.int64 and block_mapping.dim() == 2
+             and block_mapping.shape[1] == 2, "block_mapping must be int64 [P, 2]")
+    for t in (src_key_cache, src_value_cache, dst_key_cache, dst_value_cache, block_mapping):
+        _require(t.is_cuda or t.is_pinned(), "pools and mapping must be on the GPU or pinned")
+    NBs, bs, Hkv, D = src_key_cache.shape
+    gpu = next((t for t in (src_key_cache, dst_key_cache, block_mapping) if t.is_cuda), None)
+    _require(gpu is not None or stream is not None, "give a stream when no pool is on the GPU")
+    st = lib().swap_blocks(_ptr(src_key_cache), _ptr(src_value_cache), _ptr(dst_key_cache),
+                           _ptr(dst_value_cache), _ptr(block_mapping), block_mapping.shape[0], NBs,
+                           dst_key_cache.shape[0], bs, Hkv, D, dtype_code(src_key_cache.dtype),
+                           _stream(gpu if gpu is not None else src_key_cache, stream))
+    check(st, "swap_blocks")
 
 
 def check_decode_inputs(block_table: torch.Tensor, seq_lens: torch.Tensor, block_size: int,

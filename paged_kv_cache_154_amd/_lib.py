@@ -44,6 +44,8 @@ SIGNATURES = {
                                    _c_int, _c_int, _c_int, _c_int, _c_ptr]),
     "copy_blocks": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int,
                              _c_int, _c_ptr]),
+    "swap_blocks": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int,
+                             _c_int, _c_int, _c_int, _c_ptr]),
     "pagedkv_check_decode_inputs": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int,
                                              _c_int, _c_ptr, _c_ptr]),
     "pagedkv_stream_read": (_c_int, [_c_ptr, _c_size, _c_ptr, _c_int, _c_ptr]),

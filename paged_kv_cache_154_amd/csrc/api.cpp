@@ -11,6 +11,7 @@
 #include "pagedkv.h"
 #include "pagedkv_internal.h"
 #include "stream_read.h"
+#include "swap_blocks.h"
 
 namespace {
 
@@ -30,6 +31,24 @@ bool supported_head_dim(int d) { return d == 64 || d == 128; }
 
 // Rows and quads of rows move in 16-byte vector accesses.
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+// The address a kernel uses for ptr: device (or managed) memory as it is,
+// pinned host memory through its device mapping; nullptr for memory the
+// device cannot reach (pageable host memory), which must never reach a
+// kernel. Clears the error a failed query leaves behind.
+void* device_view(const void* ptr) {
+  hipPointerAttribute_t a{};
+  if (hipPointerGetAttributes(&a, ptr) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  switch (a.type) {
+    case hipMemoryTypeDevice:
+    case hipMemoryTypeManaged: return const_cast<void*>(ptr);
+    case hipMemoryTypeHost: return a.devicePointer;
+    default: return nullptr;
+  }
+}
 
 // Query rows (q_len x group) one KV head's workgroup takes: a tile of 16 MFMA
 // columns per wave.
@@ -314,6 +333,33 @@ int reshape_and_cache_fp8(const void* key, const void* value, void* key_cache, v
   const hipError_t e = pkv::launch_reshape_and_cache_fp8(
       key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale, num_tokens, num_kv_heads,
       head_dim, src_dtype, (int64_t)num_blocks * block_size, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int swap_blocks(const void* src_key_cache, const void* src_value_cache, void* dst_key_cache,
+                void* dst_value_cache, const int64_t* block_mapping, int num_pairs, int src_num_blocks,
+                int dst_num_blocks, int block_size, int num_kv_heads, int head_dim, int dtype,
+                hipStream_t stream) {
+  if (num_pairs < 0) return PKV_ERR_SHAPE;
+  if (num_pairs == 0) return PKV_OK;
+  if (!src_key_cache || !src_value_cache || !dst_key_cache || !dst_value_cache || !block_mapping)
+    return PKV_ERR_NULL;
+  if (!aligned16(src_key_cache) || !aligned16(src_value_cache) || !aligned16(dst_key_cache) ||
+      !aligned16(dst_value_cache))
+    return PKV_ERR_SHAPE;
+  if (num_kv_heads <= 0 || src_num_blocks <= 0 || dst_num_blocks <= 0) return PKV_ERR_SHAPE;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) return PKV_ERR_UNSUPPORTED;
+  const void* sk = device_view(src_key_cache);
+  const void* sv = device_view(src_value_cache);
+  void* dk = device_view(dst_key_cache);
+  void* dv = device_view(dst_value_cache);
+  const void* bm = device_view(block_mapping);
+  if (!sk || !sv || !dk || !dv || !bm) return PKV_ERR_UNSUPPORTED;
+  const int64_t block_bytes = (int64_t)block_size * num_kv_heads * head_dim * eb;
+  const hipError_t e = pkv::launch_swap_blocks(sk, sv, dk, dv, static_cast<const int64_t*>(bm), num_pairs,
+                                               src_num_blocks, dst_num_blocks, block_bytes, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

@@ -5,6 +5,7 @@
 // and consecutive lanes touch consecutive addresses.
 
 #include "pagedkv_internal.h"
+#include "swap_blocks.h"
 
 namespace pkv {
 namespace {
@@ -105,6 +106,45 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
   }
 }
 
+// Whole-block moves between two pools of the same layout, K and V: preemption
+// by swapping out to a CPU swap space and back ("LLM inference engine
+// internals" sections 3.1-3.2). Either pool may be pinned host memory, read
+// or written by the kernel across the host link; one launch covers every
+// pair, each lane moving 4 chunks of 16 bytes per pass (all loads issued
+// before the stores) so that many host-link requests are in flight.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(
+    const uint4* __restrict__ src_k, const uint4* __restrict__ src_v, uint4* __restrict__ dst_k,
+    uint4* __restrict__ dst_v, const int64_t* __restrict__ block_mapping, int num_pairs,
+    int src_blocks, int dst_blocks, int64_t chunks_per_block) {
+  constexpr int U = 4;
+  const int64_t total = (int64_t)num_pairs * chunks_per_block;
+  const int64_t stride = (int64_t)gridDim.x * 256 * U;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * U + threadIdx.x; base < total; base += stride) {
+    uint4 k[U], v[U];
+    int64_t dk[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      dk[u] = -1;
+      const int64_t gid = base + (int64_t)u * 256;
+      if (gid >= total) continue;
+      const int64_t pr = gid / chunks_per_block;
+      const int64_t c = gid - pr * chunks_per_block;
+      const int64_t src = block_mapping[2 * pr];
+      const int64_t dst = block_mapping[2 * pr + 1];
+      if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) continue;
+      k[u] = src_k[src * chunks_per_block + c];
+      v[u] = src_v[src * chunks_per_block + c];
+      dk[u] = dst * chunks_per_block + c;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (dk[u] < 0) continue;
+      dst_k[dk[u]] = k[u];
+      dst_v[dk[u]] = v[u];
+    }
+  }
+}
+
 // One workgroup counts contract violations of decode inputs: table entries of
 // used logical blocks outside the pool, and lengths outside [0, max_seq_len].
 __global__ __launch_bounds__(256) void check_decode_inputs_kernel(
@@ -199,6 +239,21 @@ hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int64_t*
   copy_blocks_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
       static_cast<uint4*>(key_cache), static_cast<uint4*>(value_cache), block_mapping, num_pairs,
       num_blocks, chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap_blocks(const void* src_key, const void* src_value, void* dst_key,
+                              void* dst_value, const int64_t* block_mapping, int num_pairs,
+                              int src_blocks, int dst_blocks, int64_t block_bytes,
+                              hipStream_t stream) {
+  const int64_t chunks = block_bytes / 16;
+  const int64_t total = (int64_t)num_pairs * chunks;
+  int64_t grid = (total + 1023) / 1024;
+  if (grid > 4096) grid = 4096;
+  swap_blocks_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
+      static_cast<const uint4*>(src_key), static_cast<const uint4*>(src_value),
+      static_cast<uint4*>(dst_key), static_cast<uint4*>(dst_value), block_mapping, num_pairs,
+      src_blocks, dst_blocks, chunks);
   return hipGetLastError();
 }
 

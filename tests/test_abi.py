@@ -193,6 +193,14 @@ def test_partition_and_workspace_sizing():
     (lambda L: L.reshape_and_cache(FAKE, ctypes.c_void_p(0x1002), FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 2,
                                    None), SHAPE),                                  # misaligned
     (lambda L: L.copy_blocks(FAKE, FAKE, FAKE, 0, 10, 16, 8, 128, 2, None), OK),
+    (lambda L: L.swap_blocks(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 10, 5, 16, 8, 128, 2, None), OK),
+    (lambda L: L.swap_blocks(FAKE, FAKE, None, FAKE, FAKE, 3, 10, 5, 16, 8, 128, 2, None), NULL),
+    (lambda L: L.swap_blocks(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 10, 5, 16, 8, 128, 2, None), SHAPE),
+    (lambda L: L.swap_blocks(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 10, 0, 16, 8, 128, 2, None), SHAPE),
+    (lambda L: L.swap_blocks(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 10, 5, 12, 8, 128, 2, None), UNSUP),
+    (lambda L: L.swap_blocks(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 10, 5, 16, 8, 128, 9, None), UNSUP),
+    (lambda L: L.swap_blocks(FAKE, ctypes.c_void_p(0x1008), FAKE, FAKE, FAKE, 3, 10, 5, 16, 8, 128,
+                             2, None), SHAPE),
     (lambda L: L.copy_blocks(FAKE, FAKE, FAKE, 0, 10, 16, 8, 128, 3, None), OK),   # e4m3 bytes
     (lambda L: L.copy_blocks(FAKE, FAKE, FAKE, 3, 10, 16, 8, 128, 4, None), UNSUP),
     (lambda L: L.reshape_and_cache_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 16, 10, 2,
