@@ -203,6 +203,50 @@ def multi_query_rows(pkv, W, base, dev, q_lens=(2, 4, 8)):
     return rows
 
 
+def swap_rows(pkv, wl, dev, n_seqs=16, reps=20):
+    """Preemption by swapping on the Llama-3-8B-shaped pools: the blocks of
+    n_seqs sequences swapped out to pinned host pools and back in (one
+    swap_blocks call each way, medians over reps), beside the host link's own
+    rate: a contiguous device <-> pinned copy of the same bytes."""
+    import torch
+    bs = wl.block_size
+    blocks = [int(b) for s_ in range(n_seqs)
+              for b in wl.block_table[s_, :(int(wl.seq_lens[s_]) + bs - 1) // bs]]
+    n = len(blocks)
+    kc, vc = wl.key_cache.to(dev), wl.value_cache.to(dev)
+    hk = torch.empty((n,) + tuple(kc.shape[1:]), dtype=kc.dtype, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    out_map = torch.tensor([[b, i] for i, b in enumerate(blocks)], dtype=torch.int64, device=dev)
+    in_map = torch.tensor([[i, b] for i, b in enumerate(blocks)], dtype=torch.int64, device=dev)
+    nbytes = 2 * n * kc[0].numel() * kc.element_size()
+
+    def med_us(fn):
+        fn()
+        ev = _events(reps)
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return statistics.median(_us(ev))
+
+    t_out = med_us(lambda: pkv.swap_blocks(kc, vc, hk, hv, out_map))
+    t_in = med_us(lambda: pkv.swap_blocks(hk, hv, kc, vc, in_map))
+    dbuf = torch.empty(nbytes // 2, dtype=torch.int16, device=dev)
+    hbuf = torch.empty(nbytes // 2, dtype=torch.int16, pin_memory=True)
+    t_d2h = med_us(lambda: hbuf.copy_(dbuf, non_blocking=True))
+    t_h2d = med_us(lambda: dbuf.copy_(hbuf, non_blocking=True))
+    log(f"swap {n} blocks ({nbytes / 1e6:.1f} MB): out {t_out:.0f} us, in {t_in:.0f} us; "
+        f"link copies {t_d2h:.0f} / {t_h2d:.0f} us")
+    del kc, vc, dbuf
+    torch.cuda.empty_cache()
+    return {"sequences": n_seqs, "blocks": n, "bytes": nbytes,
+            "swap_out_us": round(t_out, 1), "swap_out_GBps": round(nbytes / t_out / 1e3, 2),
+            "swap_in_us": round(t_in, 1), "swap_in_GBps": round(nbytes / t_in / 1e3, 2),
+            "link_copy_d2h_GBps": round(nbytes / t_d2h / 1e3, 2),
+            "link_copy_h2d_GBps": round(nbytes / t_h2d / 1e3, 2)}
+
+
 def _events(n):
     import torch
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -417,6 +461,9 @@ def main():
     ap.add_argument("--kv-fp8", action="store_true",
                     help="an e4m3 KV cache (scales per KV head from the 16-bit pools): the "
                          "step is reshape_and_cache_fp8 + paged_attn_decode_fp8")
+    ap.add_argument("--swap", action="store_true",
+                    help="also time swap_blocks: 16 sequences' blocks to pinned host pools and "
+                         "back, beside contiguous copies over the host link")
     ap.add_argument("--multi-query", action="store_true",
                     help="also time the multi-query (speculative verification) pass, "
                          "q_len 2, 4 and 8, on the same lengths")
@@ -597,9 +644,11 @@ def main():
         peak = stream_read_peak(dev)
         res["measured_stream_read_GBps"] = round(peak, 1)
         res["roofline"]["frac_of_measured_stream_read"] = round(achieved / peak, 4)
-    if args.secondary or args.multi_query:
+    if args.secondary or args.multi_query or args.swap:
         del layers
         torch.cuda.empty_cache()
+    if args.swap:
+        res["swap"] = swap_rows(pkv, W.llama3_8b(), dev)
     if args.secondary:
         res["secondary"] = secondary(pkv, W, wl, dev)
     if args.multi_query:
