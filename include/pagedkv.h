@@ -201,6 +201,55 @@ int paged_attn_multi_query_fp8(void* out, const void* query, const void* key_cac
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * paged_attn_decode_shared_prefix - decode for groups of sequences that share
+ * a prefix of whole blocks (parallel sampling: the samples of one prompt
+ * point at the same physical blocks, "vLLM core concepts" section 4.2.2,
+ * "LLM inference engine internals" section 3.3; "PagedAttention principle"
+ * section 5), reading each shared block once per group instead of once per
+ * sample. Sequences g * group_size .. (g+1) * group_size - 1 form group g.
+ * Sequence s of group g attends over the prefix_lens[g] tokens of
+ * prefix_block_table[g] followed by the suffix_lens[s] tokens of
+ * suffix_block_table[s]:
+ *   out[s,h] = paged_attn_decode of s with the block table
+ *              prefix_block_table[g][0 .. prefix_lens[g]/block_size) ++ suffix_block_table[s]
+ *              and seq_len prefix_lens[g] + suffix_lens[s]
+ * (prefix_lens[g] a multiple of block_size: a partly filled shared block is
+ * copied on write before a sample writes to it). Computed as a multi-query
+ * pass over each group's prefix (the group's samples are its query rows), a
+ * decode pass over each suffix, and a merge of the two by their log-sum-exp.
+ *
+ *   out, query             [num_groups * group_size, num_heads, head_dim]
+ *   prefix_block_table     int32 [num_groups, max_prefix_blocks]; prefix_lens int32 [num_groups]
+ *   suffix_block_table     int32 [num_groups * group_size, max_suffix_blocks];
+ *                          suffix_lens int32 [num_groups * group_size]
+ *   max_prefix_len, max_suffix_len  host bounds of the lengths
+ *   group_size * (num_heads / num_kv_heads) <= 128
+ *   kv_dtype               PKV_F32, PKV_F16 or PKV_BF16 (query of the same type)
+ *   workspace              paged_attn_shared_prefix_workspace_size(...) bytes
+ * Status codes as for paged_attn_decode.
+ */
+int paged_attn_decode_shared_prefix(void* out, const void* query, const void* key_cache,
+                                    const void* value_cache, const int32_t* prefix_block_table,
+                                    const int32_t* prefix_lens, int num_groups, int group_size,
+                                    int max_prefix_blocks, int max_prefix_len,
+                                    const int32_t* suffix_block_table, const int32_t* suffix_lens,
+                                    int max_suffix_blocks, int max_suffix_len, int num_heads,
+                                    int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                    float scale, int kv_dtype, int out_dtype, int partition_size,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_attn_shared_prefix_workspace_size - bytes of workspace that
+ * paged_attn_decode_shared_prefix needs (its two passes' fp32 outputs and
+ * log-sum-exps, and the passes' own workspace). 0 when the arguments are
+ * invalid.
+ */
+size_t paged_attn_shared_prefix_workspace_size(int num_groups, int group_size, int num_heads,
+                                               int num_kv_heads, int head_dim, int block_size,
+                                               int max_prefix_len, int max_suffix_len,
+                                               int partition_size);
+
+/*
  * paged_attn_partition_tokens - the partition length paged_attn_decode uses
  * for these arguments (resolving partition_size = 0), or a negative
  * pkv_status for invalid arguments. A value >= max_seq_len means no split.

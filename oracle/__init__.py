@@ -20,6 +20,10 @@ Pins (checked by ``tests/test_oracle_*.py`` without a GPU):
     §2.3); every other byte unchanged.
   * ``copy_blocks``: destination equals the pre-call source, all else
     unchanged, and decode after a copy-on-write remap equals decode before.
+  * ``decode_shared_prefix``: on the prefix-sharing batch, the tables it
+    builds from each group's shared blocks and each sample's own blocks are
+    the samples' block tables, so it equals ``decode`` of the batch; a group
+    of one with an empty prefix is ``decode``.
   * ``swap_blocks``: destination blocks equal the source blocks, all else
     unchanged, the source untouched; swapping out and back in to other
     blocks, with the block table remapped, leaves decode unchanged; within
@@ -48,6 +52,7 @@ from .paged_attention import (  # noqa: F401
     copy_blocks,
     decode,
     decode_one,
+    decode_shared_prefix,
     kv_cache_bytes,
     multi_query,
     multi_query_one,

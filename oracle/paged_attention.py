@@ -260,6 +260,33 @@ def copy_blocks(key_cache, value_cache, block_mapping):
     return kc, vc
 
 
+def decode_shared_prefix(query, key_cache, value_cache, prefix_block_table, prefix_lens,
+                         suffix_block_table, suffix_lens, group_size: int, scale: float,
+                         seqs=None) -> np.ndarray:
+    """Decode for groups of ``group_size`` consecutive sequences sharing a
+    prefix of whole blocks (the samples of one prompt share its blocks:
+    [VC] §4.2.2, [EI] §3.3, [PP] §5): sequence s of group g = s // group_size
+    has the block table prefix_block_table[g][:prefix_lens[g] / bs] followed
+    by suffix_block_table[s], and length prefix_lens[g] + suffix_lens[s];
+    the result is ``decode`` of those tables, float64 ``[S, H, D]``."""
+    S = tuple(query.shape)[0]
+    nb, bs, hkv, d = _pool_shape(key_cache)
+    pt, pl = _to_np_int(prefix_block_table), _to_np_int(prefix_lens)
+    st, sl = _to_np_int(suffix_block_table), _to_np_int(suffix_lens)
+    width = pt.shape[1] + st.shape[1]
+    table = np.zeros((S, width), dtype=np.int64)
+    lens = np.zeros(S, dtype=np.int64)
+    for s in range(S):
+        g = s // group_size
+        if pl[g] % bs != 0:
+            raise ValueError("a shared prefix is made of whole blocks")
+        npb = int(pl[g]) // bs
+        row = list(pt[g, :npb]) + list(st[s])
+        table[s, :len(row)] = row
+        lens[s] = pl[g] + sl[s]
+    return decode(query, key_cache, value_cache, table, lens, scale, seqs=seqs)
+
+
 def swap_blocks(src_key, src_value, dst_key, dst_value, block_mapping):
     """Move whole blocks (K and V) from one pool to another; returns the new
     destination pools.

@@ -238,6 +238,49 @@ def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: tor
     check(st, "reshape_and_cache_fp8")
 
 
+def paged_attn_decode_shared_prefix(out: torch.Tensor, query: torch.Tensor,
+                                    key_cache: torch.Tensor, value_cache: torch.Tensor,
+                                    prefix_block_table: torch.Tensor, prefix_lens: torch.Tensor,
+                                    suffix_block_table: torch.Tensor, suffix_lens: torch.Tensor,
+                                    group_size: int, scale: float, max_prefix_len: int,
+                                    max_suffix_len: int, partition_size: int = 0,
+                                    workspace: torch.Tensor | None = None,
+                                    stream=None) -> torch.Tensor:
+    """Decode for groups of group_size consecutive sequences that share a
+    prefix of whole blocks: sequence s of group g attends over
+    prefix_block_table[g] (prefix_lens[g] tokens) then suffix_block_table[s]
+    (suffix_lens[s] tokens); each shared block is read once per group."""
+    _require(query.dim() == 3 and out.shape == query.shape, "query/out must be [S, H, D]")
+    _require(key_cache.dim() == 4 and value_cache.shape == key_cache.shape, "pool shape")
+    _require(query.dtype == key_cache.dtype == value_cache.dtype, "query and pools share a dtype")
+    for t in (prefix_block_table, prefix_lens, suffix_block_table, suffix_lens):
+        _require(t.dtype == torch.int32, "tables and lengths must be int32")
+    S, H, D = query.shape
+    NB, bs, Hkv, D2 = key_cache.shape
+    _require(D2 == D and group_size >= 1 and S % group_size == 0, "shapes / group size")
+    G = S // group_size
+    _require(prefix_block_table.dim() == 2 and prefix_block_table.shape[0] == G
+             and prefix_lens.shape == (G,), "prefix table [groups, blocks], lens [groups]")
+    _require(suffix_block_table.dim() == 2 and suffix_block_table.shape[0] == S
+             and suffix_lens.shape == (S,), "suffix table [S, blocks], lens [S]")
+    if workspace is None:
+        n = int(lib().paged_attn_shared_prefix_workspace_size(G, group_size, H, Hkv, D, bs,
+                                                              int(max_prefix_len),
+                                                              int(max_suffix_len),
+                                                              int(partition_size)))
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=query.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().paged_attn_decode_shared_prefix(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(prefix_block_table),
+        _ptr(prefix_lens), G, group_size, prefix_block_table.shape[1], int(max_prefix_len),
+        _ptr(suffix_block_table), _ptr(suffix_lens), suffix_block_table.shape[1],
+        int(max_suffix_len), H, Hkv, D, bs, NB, float(scale), dtype_code(query.dtype),
+        dtype_code(out.dtype), int(partition_size), _ptr(workspace), ws_bytes,
+        _stream(query, stream))
+    check(st, "paged_attn_decode_shared_prefix")
+    return out
+
+
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
                       value_cache: torch.Tensor, slot_mapping: torch.Tensor,
                       stream=None) -> None:

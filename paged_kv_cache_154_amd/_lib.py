@@ -37,6 +37,13 @@ SIGNATURES = {
                                             _c_int, _c_int, _c_int, _c_ptr, _c_size, _c_ptr]),
     "reshape_and_cache_fp8": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                        _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
+    "paged_attn_decode_shared_prefix": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                                 _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_ptr,
+                                                 _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                                 _c_int, _c_float, _c_int, _c_int, _c_int, _c_ptr,
+                                                 _c_size, _c_ptr]),
+    "paged_attn_shared_prefix_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int,
+                                                          _c_int, _c_int, _c_int, _c_int]),
     "paged_attn_partition_tokens": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "paged_attn_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                             _c_int]),

@@ -11,6 +11,7 @@
 #include "pagedkv.h"
 #include "pagedkv_internal.h"
 #include "stream_read.h"
+#include "shared_prefix.h"
 #include "swap_blocks.h"
 
 namespace {
@@ -146,7 +147,8 @@ int attention(void* out, const void* query, const void* key_cache, const void* v
               const int32_t* seq_lens, int num_seqs, int q_len, int num_heads, int num_kv_heads,
               int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
               int max_seq_len, float scale, int kv_dtype, int query_dtype, int out_dtype,
-              int partition_size, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+              int partition_size, void* workspace, size_t workspace_bytes, hipStream_t stream,
+              float* lse = nullptr, int causal = 1) {
   if (num_seqs < 0 || q_len < 1) return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !query || !key_cache || !value_cache || !block_table || !seq_lens)
@@ -210,6 +212,8 @@ int attention(void* out, const void* query, const void* key_cache, const void* v
   p.num_partitions = np;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
+  p.causal = causal;
+  p.lse = lse;
   const hipError_t e = pkv::launch_decode(p, kv_dtype, query_dtype, head_dim, block_size, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
@@ -227,9 +231,100 @@ size_t workspace_size(int num_seqs, int q_len, int num_heads, int num_kv_heads, 
                              cutting_for(max_seq_len, block_size, P).np);
 }
 
+// Shared-prefix decode: the prefix pass's and the suffix pass's fp32 outputs
+// and lse rows, each area 256-byte aligned, then one workspace that the two
+// passes use in turn (same stream).
+struct PrefixLayout {
+  size_t o_bytes, lse_bytes, inner_bytes;
+  size_t total() const { return 2 * o_bytes + 2 * lse_bytes + inner_bytes; }
+};
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+PrefixLayout prefix_layout(int num_groups, int group_size, int num_heads, int num_kv_heads,
+                           int head_dim, int block_size, int max_prefix_len, int max_suffix_len,
+                           int partition_size) {
+  PrefixLayout l{0, 0, 0};
+  const int64_t rows = (int64_t)num_groups * group_size * num_heads;
+  const size_t a = workspace_size(num_groups, group_size, num_heads, num_kv_heads, head_dim, block_size,
+                                  max_prefix_len, partition_size);
+  const size_t b = workspace_size(num_groups * group_size, 1, num_heads, num_kv_heads, head_dim, block_size,
+                                  max_suffix_len, partition_size);
+  if (a == 0 || b == 0) return l;
+  l.o_bytes = round256((size_t)rows * head_dim * sizeof(float));
+  l.lse_bytes = round256((size_t)rows * sizeof(float));
+  l.inner_bytes = a > b ? a : b;
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t paged_attn_shared_prefix_workspace_size(int num_groups, int group_size, int num_heads,
+                                               int num_kv_heads, int head_dim, int block_size,
+                                               int max_prefix_len, int max_suffix_len,
+                                               int partition_size) {
+  if (num_groups <= 0 || group_size <= 0 || (int64_t)num_groups * group_size > INT32_MAX / 2) return 0;
+  return prefix_layout(num_groups, group_size, num_heads, num_kv_heads, head_dim, block_size,
+                       max_prefix_len, max_suffix_len, partition_size)
+      .total();
+}
+
+int paged_attn_decode_shared_prefix(void* out, const void* query, const void* key_cache,
+                                    const void* value_cache, const int32_t* prefix_block_table,
+                                    const int32_t* prefix_lens, int num_groups, int group_size,
+                                    int max_prefix_blocks, int max_prefix_len,
+                                    const int32_t* suffix_block_table, const int32_t* suffix_lens,
+                                    int max_suffix_blocks, int max_suffix_len, int num_heads,
+                                    int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                    float scale, int kv_dtype, int out_dtype, int partition_size,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (num_groups < 0 || group_size < 1) return PKV_ERR_SHAPE;
+  if (num_groups == 0) return PKV_OK;
+  if ((int64_t)num_groups * group_size > INT32_MAX / 2) return PKV_ERR_SHAPE;
+  if (!out || !query || !key_cache || !value_cache || !prefix_block_table || !prefix_lens ||
+      !suffix_block_table || !suffix_lens)
+    return PKV_ERR_NULL;
+  if (kv_dtype == PKV_E4M3) return PKV_ERR_UNSUPPORTED;
+  if (out_dtype != kv_dtype && out_dtype != PKV_F32) return PKV_ERR_UNSUPPORTED;
+  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
+  const PrefixLayout l = prefix_layout(num_groups, group_size, num_heads, num_kv_heads, head_dim,
+                                       block_size, max_prefix_len, max_suffix_len, partition_size);
+  if (l.total() == 0) {
+    // the passes' own checks name what is wrong (group too large, sizes, partition)
+    const int st = attention(out, query, key_cache, value_cache, nullptr, nullptr, prefix_block_table,
+                             prefix_lens, num_groups, group_size, num_heads, num_kv_heads, head_dim,
+                             block_size, num_blocks, max_prefix_blocks, max_prefix_len, scale, kv_dtype,
+                             kv_dtype, PKV_F32, partition_size, nullptr, 0, stream, nullptr, 0);
+    return st != PKV_OK && st != PKV_ERR_WORKSPACE ? st : PKV_ERR_SHAPE;
+  }
+  if (!workspace || workspace_bytes < l.total()) return PKV_ERR_WORKSPACE;
+  if (!aligned16(out) || !aligned16(workspace)) return PKV_ERR_SHAPE;
+  unsigned char* w = static_cast<unsigned char*>(workspace);
+  float* o_pre = reinterpret_cast<float*>(w);
+  float* o_suf = reinterpret_cast<float*>(w + l.o_bytes);
+  float* lse_pre = reinterpret_cast<float*>(w + 2 * l.o_bytes);
+  float* lse_suf = reinterpret_cast<float*>(w + 2 * l.o_bytes + l.lse_bytes);
+  void* inner = w + 2 * l.o_bytes + 2 * l.lse_bytes;
+  const int num_seqs = num_groups * group_size;
+  // the prefix once per group: the group's samples are its query rows
+  // ([num_seqs, H, D] read as [num_groups, group_size, H, D]), all of them
+  // seeing the whole prefix
+  int st = attention(o_pre, query, key_cache, value_cache, nullptr, nullptr, prefix_block_table, prefix_lens,
+                     num_groups, group_size, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_prefix_blocks, max_prefix_len, scale, kv_dtype, kv_dtype, PKV_F32, partition_size,
+                     inner, l.inner_bytes, stream, lse_pre, 0);
+  if (st != PKV_OK) return st;
+  // each sample's own suffix
+  st = attention(o_suf, query, key_cache, value_cache, nullptr, nullptr, suffix_block_table, suffix_lens,
+                 num_seqs, 1, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_suffix_blocks,
+                 max_suffix_len, scale, kv_dtype, kv_dtype, PKV_F32, partition_size, inner, l.inner_bytes,
+                 stream, lse_suf, 1);
+  if (st != PKV_OK) return st;
+  const hipError_t e = pkv::launch_cascade_merge(out, o_pre, lse_pre, o_suf, lse_suf,
+                                                 (int64_t)num_seqs * num_heads, head_dim, out_dtype, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
 
 size_t paged_attn_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                                  int block_size, int max_seq_len, int partition_size) {

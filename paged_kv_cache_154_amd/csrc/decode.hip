@@ -282,6 +282,9 @@ constexpr float kRescaleSlack = 8.0f;
 // exact zero weights instead of NaN (2^(-inf - -inf)); the first attended
 // score replaces it, and 2^(kNoMax - score) is 0 like 2^-inf.
 constexpr float kNoMax = -1e30f;
+// log2 of a row's sum of weights, in the units of the scores (log2, scale
+// included): M + log2(den); kNoMax for a row that saw no position.
+__device__ inline float lse_of(float M, float den) { return den > 0.0f ? M + __log2f(den) : kNoMax; }
 
 // Per-lane state of one wave working through the tiles of one (sequence, KV
 // head): the query operand, the softmax state of head `col` and its O^T
@@ -777,6 +780,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
     for (int qi = tid; qi < R * DQ; qi += kThreads) {
       const int r = qi / DQ;
       store_out4<Tag>(p, row_of(r) * D + 4 * (qi - r * DQ), make_float4(0.f, 0.f, 0.f, 0.f));
+      if (p.lse && qi - r * DQ == 0) p.lse[row_of(r)] = kNoMax;
     }
     return;
   }
@@ -828,7 +832,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   const int myrow = 16 * cgroup + eng.col;
   const bool valid = myrow < R;
   eng.load_q(static_cast<const unsigned char*>(p.q) + row_of(valid ? myrow : 0) * Eng::QB, valid);
-  eng.lim = valid ? L - p.q_len + token_of(myrow) : L - 1;
+  eng.lim = valid && p.causal ? L - p.q_len + token_of(myrow) : L - 1;
   eng.reset();
   __syncthreads();
 
@@ -861,7 +865,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   using Yes = std::true_type;
   using No = std::false_type;
   const bool cached = shared || nct > 1;
-  if (p.q_len == 1) {
+  if (p.q_len == 1 || !p.causal) {
     if (cached) tiles(No{}, No{}); else tiles(Yes{}, No{});
   } else {
     if (cached) tiles(No{}, Yes{}); else tiles(Yes{}, Yes{});
@@ -941,6 +945,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
     const size_t row = row_of(r);
     if (nparts <= 1) {
       store_out4<Tag>(p, row * D + d, finish(num, den));
+      if (p.lse && d == 0) p.lse[row] = lse_of(M, den);
     } else {
       // agent-scope stores: written through to where every XCD reads them.
       // A partial's D values are kept as its quads' (0, 1) pairs, then their
@@ -1022,6 +1027,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
       }
     }
     store_out4<Tag>(p, row * D + d, finish(num, den));
+    if (p.lse && d == 0) p.lse[row] = lse_of(M, den);
   }
 }
 
@@ -1129,6 +1135,7 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
     c.num_seqs = p.num_seqs - s0 < chunk ? p.num_seqs - s0 : chunk;
     c.q = static_cast<const unsigned char*>(p.q) + (size_t)s0 * q_row * q_elem;
     c.out = static_cast<unsigned char*>(p.out) + (size_t)s0 * q_row * out_elem;
+    if (p.lse) c.lse = p.lse + (size_t)s0 * p.q_len * p.num_heads;
     c.block_table = p.block_table + (size_t)s0 * p.max_blocks;
     c.seq_lens = p.seq_lens + s0;
     const size_t lds =

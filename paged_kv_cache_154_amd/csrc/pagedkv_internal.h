@@ -36,6 +36,8 @@ struct DecodeParams {
   int num_partitions;  // partitions per sequence at most (ceil(max_seq_len / partition)), >= 1
   float scale_log2;    // scale * log2(e)
   int out_f32;         // 1: out is fp32; 0: out has the KV dtype
+  int causal;          // q_len > 1: 1 new token j sees positions <= L - q_len + j; 0 every row sees all L
+  float* lse;          // optional [S, q_len, H]: M + log2(sum of weights) per row, log2 units (or -1e30)
 };
 
 // Tokens a wave handles per step (one MFMA tile of keys).

@@ -346,6 +346,43 @@ def prefix_share(groups: int = 128, n: int = 3, prefix: int = 2048,
     return wl
 
 
+def shared_prefix_tables(wl: Workload, group_size: int):
+    """The batch's block tables split for shared-prefix decode: groups of
+    group_size consecutive sequences; a group's prefix is the longest run of
+    leading blocks that every member's table holds (and fills: at most the
+    shortest member's whole blocks), the rest of each table its suffix.
+    Returns prefix_table int32 [groups, max_prefix_blocks], prefix_lens int32
+    [groups], suffix_table int32 [S, max_suffix_blocks], suffix_lens int32 [S]."""
+    bs = wl.block_size
+    S = wl.num_seqs
+    if S % group_size:
+        raise ValueError("the batch is not a whole number of groups")
+    groups = S // group_size
+    lens = wl.seq_lens.astype(np.int64)
+    pre_rows, pre_lens, suf_rows, suf_lens = [], [], [], []
+    for g in range(groups):
+        members = range(g * group_size, (g + 1) * group_size)
+        full = min(int(lens[s]) // bs for s in members)
+        k = 0
+        while k < full and len({int(wl.block_table[s, k]) for s in members}) == 1:
+            k += 1
+        pre_rows.append(wl.block_table[g * group_size, :k].tolist())
+        pre_lens.append(k * bs)
+        for s in members:
+            nb = (int(lens[s]) + bs - 1) // bs
+            suf_rows.append(wl.block_table[s, k:nb].tolist())
+            suf_lens.append(int(lens[s]) - k * bs)
+    wp = max([len(r) for r in pre_rows] + [1])
+    ws = max([len(r) for r in suf_rows] + [1])
+    pt = np.zeros((groups, wp), dtype=np.int32)
+    st = np.zeros((S, ws), dtype=np.int32)
+    for g, r in enumerate(pre_rows):
+        pt[g, :len(r)] = r
+    for s, r in enumerate(suf_rows):
+        st[s, :len(r)] = r
+    return pt, np.array(pre_lens, dtype=np.int32), st, np.array(suf_lens, dtype=np.int32)
+
+
 def mixed_splitk() -> Workload:
     """Mixed batch: 16 sequences of 10000 tokens (20 turns x 500 tokens) and
     240 sequences uniform in [50, 2000], shuffled; 32 q / 8 KV heads,

@@ -358,6 +358,52 @@ def test_cow_fork_example_decode_unchanged_by_private_copy():
 
 
 # ----------------------------------------------------------------------------
+# decode_shared_prefix: groups of samples sharing a prefix of whole blocks
+# ----------------------------------------------------------------------------
+
+def test_shared_prefix_tables_rebuild_the_batch_and_decode_equally():
+    """Groups of 3 samples sharing 5 blocks and forking (the last shared
+    block copied for samples 1 and 2, as on fork): the split into each
+    group's common blocks and each sample's own blocks, joined again, gives
+    back every sample's table, so decode_shared_prefix equals decode."""
+    from paged_kv_cache_154_amd import workloads as W
+    bs, Hkv, D, H = 8, 2, 32, 4
+    rng = np.random.default_rng(12)
+    rows, lens = [], []
+    nxt = 0
+    for g in range(2):
+        shared = list(range(nxt, nxt + 5))
+        nxt += 5
+        for i in range(3):
+            last = shared[-1] if i == 0 else nxt
+            nxt += i > 0
+            own = list(range(nxt, nxt + 2))
+            nxt += 2
+            rows.append(shared[:-1] + [last] + own)
+            lens.append(5 * bs + int(rng.integers(0, 2 * bs + 1)))
+    width = max(len(r) for r in rows)
+    bt = np.zeros((6, width), dtype=np.int32)
+    for s, r in enumerate(rows):
+        bt[s, :len(r)] = r
+    kc = torch.randn(nxt + 1, bs, Hkv, D)
+    vc = torch.randn(nxt + 1, bs, Hkv, D)
+    q = torch.randn(6, H, D)
+    wl = W.Workload(name="t", seed=0, num_heads=H, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                    num_blocks=nxt + 1, max_blocks_per_seq=width, dtype=torch.float32, scale=0.2,
+                    seq_lens=np.array(lens, dtype=np.int32), block_table=bt, query=q,
+                    key_cache=kc, value_cache=vc)
+    pt, pl, st, sl = W.shared_prefix_tables(wl, 3)
+    assert pl.tolist() == [4 * bs, 4 * bs]          # block 4 is copied for samples 1, 2
+    ref = oracle.decode(q, kc, vc, bt, np.array(lens), 0.2)
+    got = oracle.decode_shared_prefix(q, kc, vc, pt, pl, st, sl, 3, 0.2)
+    assert np.array_equal(got, ref)
+    # a group of one with an empty prefix is plain decode
+    none = oracle.decode_shared_prefix(q, kc, vc, np.zeros((6, 1), np.int32), np.zeros(6, np.int32),
+                                       bt, np.array(lens), 1, 0.2)
+    assert np.array_equal(none, ref)
+
+
+# ----------------------------------------------------------------------------
 # swap_blocks: preemption by swapping to a CPU swap space and back
 # ----------------------------------------------------------------------------
 
