@@ -372,6 +372,64 @@ def fp8_scales(pool):
     return (a.amax(dim=(0, 1, 3)) / 448.0).clamp_min(1e-6).contiguous()
 
 
+def prefix_share_rows(pkv, W, dev, calls=100, warm=10):
+    """The prefix-sharing workload (128 groups x 3 samples, 2032 shared
+    tokens per group after the copy-on-write step): decode of the batch and
+    shared-prefix decode of the same batch (each group's shared blocks read
+    once), each call timed cold after a 1 GiB streaming read, medians; GB/s
+    on the logical bytes (every sample's whole context) and on the distinct
+    bytes (shared blocks once)."""
+    import torch
+    wl = W.make(4)
+    kc, vc = wl.key_cache.to(dev), wl.value_cache.to(dev)
+    pkv.copy_blocks(kc, vc, torch.from_numpy(wl.block_mapping).to(dev))
+    q = wl.query.to(dev)
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    sl = torch.from_numpy(wl.seq_lens).to(dev)
+    pt, pl, st, sl2 = [torch.from_numpy(x).to(dev) for x in W.shared_prefix_tables(wl, 3)]
+    out = torch.empty(wl.query.shape, dtype=wl.dtype, device=dev)
+    ws = pkv.workspace_for(q, kc, wl.max_seq_len, 0)
+    fbuf = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    fsink = torch.empty(8192, dtype=torch.int32, device=dev)
+    mp, ms = int(pl.max()), int(sl2.max())
+    n = pkv.lib().paged_attn_shared_prefix_workspace_size(128, 3, wl.num_heads, wl.num_kv_heads,
+                                                          wl.head_dim, wl.block_size, mp, ms, 0)
+    ws2 = torch.empty(n, dtype=torch.uint8, device=dev)
+    fns = {"decode": lambda: pkv.paged_attn_decode(out, q, kc, vc, bt, sl, wl.scale,
+                                                   wl.max_seq_len, 0, ws),
+           "shared_prefix": lambda: pkv.paged_attn_decode_shared_prefix(
+               out, q, kc, vc, pt, pl, st, sl2, 3, wl.scale, mp, ms, 0, ws2)}
+    logical = wl.kv_bytes()
+    distinct = layout_stats(wl)["kv_bytes_distinct"]
+    res = {"logical_kv_bytes": logical, "distinct_kv_bytes": distinct}
+    for name, fn in fns.items():
+        for _ in range(warm):
+            fn()
+        ev = _events(calls)
+        for a, b in ev:
+            pkv.stream_read(fbuf, fsink, 8192)
+            a.record()
+            fn()
+            b.record()
+        w0, w1 = _events(1)[0]
+        w0.record()
+        for _ in range(warm):
+            fn()
+        w1.record()
+        torch.cuda.synchronize()
+        p10, p50, p90 = _pcts(_us(ev))
+        res[name] = {"cold_us_p10_p50_p90": [p10, p50, p90],
+                     "warm_mean_us": round(w0.elapsed_time(w1) * 1e3 / warm, 2),
+                     "logical_GBps": round(logical / p50 / 1e3, 1),
+                     "distinct_GBps": round(distinct / p50 / 1e3, 1)}
+        log(f"prefix share, {name}: cold median {p50:.1f} us")
+    res["speedup"] = round(res["decode"]["cold_us_p10_p50_p90"][1]
+                           / res["shared_prefix"]["cold_us_p10_p50_p90"][1], 3)
+    del kc, vc, fbuf
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline_fp8(wl, ks, vs, n_seqs=8, budget_s=20.0):
     """The CPU oracle on the e4m3 step for a sample of the batch: the first
     n_seqs sequences' blocks quantised beforehand (not timed), then the timed
@@ -461,6 +519,8 @@ def main():
     ap.add_argument("--kv-fp8", action="store_true",
                     help="an e4m3 KV cache (scales per KV head from the 16-bit pools): the "
                          "step is reshape_and_cache_fp8 + paged_attn_decode_fp8")
+    ap.add_argument("--prefix-share", action="store_true",
+                    help="also time the prefix-sharing batch: decode vs shared-prefix decode")
     ap.add_argument("--swap", action="store_true",
                     help="also time swap_blocks: 16 sequences' blocks to pinned host pools and "
                          "back, beside contiguous copies over the host link")
@@ -644,11 +704,13 @@ def main():
         peak = stream_read_peak(dev)
         res["measured_stream_read_GBps"] = round(peak, 1)
         res["roofline"]["frac_of_measured_stream_read"] = round(achieved / peak, 4)
-    if args.secondary or args.multi_query or args.swap:
+    if args.secondary or args.multi_query or args.swap or args.prefix_share:
         del layers
         torch.cuda.empty_cache()
     if args.swap:
         res["swap"] = swap_rows(pkv, W.llama3_8b(), dev)
+    if args.prefix_share:
+        res["prefix_share"] = prefix_share_rows(pkv, W, dev)
     if args.secondary:
         res["secondary"] = secondary(pkv, W, wl, dev)
     if args.multi_query:
