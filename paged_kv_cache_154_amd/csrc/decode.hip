@@ -289,7 +289,15 @@ __device__ inline float lse_of(float M, float den) { return den > 0.0f ? M + __l
 // Per-lane state of one wave working through the tiles of one (sequence, KV
 // head): the query operand, the softmax state of head `col` and its O^T
 // accumulators.
-template <class Tag, int D, int BS>
+//
+// P4 (e4m3 rows of 128 elements, at most 4 query rows per KV head): P.V runs
+// on the 4x4x1 fp32 MFMA, 16 blocks of 4 x 4, so that only the 4 columns of
+// the query rows are computed instead of the 16 of the 16x16x4 one. V is
+// loaded per token pair: lanes 0-31 take the first token, 32-63 the second,
+// 4 codes (4 head-dim elements) per lane; lane 4b + h then accumulates head
+// h over head-dim 16 (b % 8) + 4 i + c in acc[c][i], and the halves b and
+// b + 8 (the pair's two tokens) are summed when O goes to LDS.
+template <class Tag, int D, int BS, bool P4 = false>
 struct TileEngine {
   using Tr = KV<Tag>;
   static constexpr int E = Tr::kBytes;
@@ -308,6 +316,8 @@ struct TileEngine {
   static constexpr int KCL = RB / 256;     // 16-byte chunks per lane per token (K rows whole)
   static constexpr int KTS = RB + 16;      // LDS row stride of the K tile
   static constexpr int KT_BYTES = kKLds ? 16 * KTS : 0;  // one wave's K tile
+  static_assert(!P4 || (kF8 && D == 128), "the 4x4x1 P.V form takes e4m3 rows of 128 elements");
+  static constexpr int NACC = P4 ? 4 : VPL;  // O^T accumulator tiles
 
   int col;  // MFMA column: query row within the KV head's rows
   int grp;  // lane group 0..3
@@ -315,7 +325,7 @@ struct TileEngine {
   uint4 qv[NKL];
   float m;     // running max of head `col` (log2 units)
   float lsum;  // this lane's share of the running sum of weights
-  f32x4 acc[VPL];  // acc[j][i] = O[head col][VPL * (4 * grp + i) + j]
+  f32x4 acc[NACC];  // acc[j][i] = O[head col][VPL * (4 * grp + i) + j] (P4: as above)
 
   __device__ void init(int lane) {
     col = lane & 15;
@@ -339,18 +349,24 @@ struct TileEngine {
     m = kNoMax;
     lsum = 0.0f;
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NACC; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One tile of tokens cs .. cs+15 (cs a multiple of 16, cs <= t_last).
-  // row_off(t) is the byte offset of token t's row for this KV head (t <= t_last);
-  // kt is the wave's LDS tile (KT_BYTES); nt selects non-temporal loads;
-  // causal applies the column's own limit `lim` as well (several new tokens).
-  template <bool nt, bool causal, class RowOff>
-  __device__ void step(const unsigned char* kbase, const unsigned char* vbase, int cs, int t_last,
-                       uint32_t slot_bytes, float scale_log2, RowOff row_off, unsigned char* kt) {
+  // The registers of one tile's K and V, as loaded.
+  struct Tile {
     uint4 kr[NKL];
-    uint32_t vr[4][VW];
+    uint32_t vr[P4 ? 1 : 4][P4 ? 1 : VW];
+    uint32_t vq[P4 ? 8 : 1];  // P4: codes of token cs + 2 q + (lane >> 5), 4 per lane
+  };
+
+  // Loads of the tile of tokens cs .. cs+15 (cs a multiple of 16, cs <=
+  // t_last; tokens past t_last read t_last's row). row_off(t) is the byte
+  // offset of token t's row for this KV head (t <= t_last); nt selects
+  // non-temporal loads.
+  template <bool nt, class RowOff>
+  __device__ void issue(Tile& g, const unsigned char* kbase, const unsigned char* vbase, int cs, int t_last,
+                        uint32_t slot_bytes, RowOff row_off) {
+    uint4 (&kr)[NKL] = g.kr;
     // rows of tokens t4 .. t4+3: a 4-aligned group never crosses a block
     const int t4 = min(cs + 4 * grp, t_last);
     const uint64_t off4 = row_off(t4);
@@ -382,11 +398,47 @@ struct TileEngine {
         for (int i = 0; i < NKL; ++i) kr[i] = *reinterpret_cast<const uint4*>(kp + 64 * i);
       }
     }
-    const unsigned char* vp = vbase + off4 + col * (VPL * E);
+    if constexpr (P4) {
+      const int lane = col + 16 * grp;
+      const int h2 = lane >> 5;
+      const unsigned char* vp = vbase + 4 * (lane & 31);
+      if constexpr (BS % 16 == 0) {  // the whole tile in one block
+        const unsigned char* vt = vp + row_off(cs);
+        const uint32_t rt = (uint32_t)(t_last - cs);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      load_words<nt, VW>(vr[r], vp + (uint32_t)((uint32_t)r < room ? r : room) * slot_bytes);
-    __builtin_amdgcn_sched_barrier(0);  // every load of the tile in flight first
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t r = (uint32_t)(2 * q + h2);
+          g.vq[q] = NTL<nt>::ld(reinterpret_cast<const uint32_t*>(vt + (r < rt ? r : rt) * slot_bytes));
+        }
+      } else {  // 4-aligned groups of tokens (never across a block)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int ta = min(cs + 4 * a, t_last);
+          const unsigned char* vt = vp + row_off(ta);
+          const uint32_t ra = (uint32_t)(t_last - ta);
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            const uint32_t r = (uint32_t)(2 * b + h2);
+            g.vq[2 * a + b] = NTL<nt>::ld(reinterpret_cast<const uint32_t*>(vt + (r < ra ? r : ra) * slot_bytes));
+          }
+        }
+      }
+    } else {
+      const unsigned char* vp = vbase + off4 + col * (VPL * E);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        load_words<nt, VW>(g.vr[r], vp + (uint32_t)((uint32_t)r < room ? r : room) * slot_bytes);
+    }
+  }
+
+  // The tile's scores, softmax update and P.V, on the registers `issue`
+  // filled for the tile at cs (every score past t_last is masked, so a tile
+  // wholly past the end changes nothing). kt is the wave's LDS tile
+  // (KT_BYTES); causal applies the column's own limit `lim` as well
+  // (several new tokens).
+  template <bool causal>
+  __device__ void consume(Tile& g, int cs, int t_last, float scale_log2, unsigned char* kt) {
+    uint4 (&kr)[NKL] = g.kr;
     if constexpr (kF8) {
 #pragma unroll
       for (int u = NKR - 1; u >= 0; --u) {  // from the top: slot u is read before it is written
@@ -429,8 +481,10 @@ struct TileEngine {
       const float m_new = fmaxf(m, cmax);
       const float alpha = fast_exp2(m - m_new);
       lsum *= alpha;
+      // P4: lane 4b + h holds sums of head h, whose alpha is lane h's
+      const float a_acc = P4 ? __shfl(alpha, (col + 16 * grp) & 3) : alpha;
 #pragma unroll
-      for (int j = 0; j < VPL; ++j) acc[j] *= alpha;
+      for (int j = 0; j < NACC; ++j) acc[j] *= a_acc;
       m = m_new;
     }
 #pragma unroll
@@ -439,12 +493,67 @@ struct TileEngine {
       lsum += s[r];
     }
 
-    // O^T += V^T P^T, 4 tokens per MFMA
+    if constexpr (P4) {
+      // token pair q: the weights of tokens cs + 2q and cs + 2q + 1 sit in
+      // lanes 16 (q / 2) + h (head h), registers 2 (q % 2) and 2 (q % 2) + 1;
+      // each half of the wave takes its token's, then one 4x4x1 MFMA per
+      // code of the lane's V word
+      const int lane = col + 16 * grp;
+      const bool second = lane >= 32;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+      for (int q = 0; q < 8; ++q) {
+        const int src = 16 * (q >> 1) + (lane & 3);
+        const float w0 = __shfl(s[2 * (q & 1)], src);
+        const float w1 = __shfl(s[2 * (q & 1) + 1], src);
+        const float w = second ? w1 : w0;
 #pragma unroll
-      for (int j = 0; j < VPL; ++j)
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(Tr::elem(vr[r], j), s[r], acc[j], 0, 0, 0);
+        for (int c = 0; c < 4; ++c)
+          acc[c] = __builtin_amdgcn_mfma_f32_4x4x1f32(f8_at(g.vq[q], c), w, acc[c], 0, 0, 0);
+      }
+    } else {
+      // O^T += V^T P^T, 4 tokens per MFMA
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < VPL; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(Tr::elem(g.vr[r], j), s[r], acc[j], 0, 0, 0);
+    }
+  }
+
+  // One tile: every load in flight, then the math.
+  template <bool nt, bool causal, class RowOff>
+  __device__ void step(const unsigned char* kbase, const unsigned char* vbase, int cs, int t_last,
+                       uint32_t slot_bytes, float scale_log2, RowOff row_off, unsigned char* kt) {
+    Tile g;
+    issue<nt>(g, kbase, vbase, cs, t_last, slot_bytes, row_off);
+    __builtin_amdgcn_sched_barrier(0);  // every load of the tile in flight first
+    consume<causal>(g, cs, t_last, scale_log2, kt);
+  }
+
+  // The wave's unnormalised O rows to LDS: head h's row at o0 + h * ost.
+  // Called by every lane; writes the rows of this lane's column when `valid`
+  // (P4: the rows h < rows).
+  __device__ void write_o(float* o0, int ost, bool valid, int rows) {
+    if constexpr (P4) {
+      const int lane = col + 16 * grp;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[c][i] += __shfl_xor(acc[c][i], 32);
+      const int h = lane & 3;
+      if (lane < 32 && h < rows) {
+        float* orow = o0 + (size_t)h * ost + 16 * (lane >> 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<float4*>(orow + 4 * i) = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
+      }
+    } else if (valid) {
+      float* orow = o0 + (size_t)col * ost;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) orow[d_of(i, j)] = acc[j][i];
+    }
   }
 
   // Sum of weights of head col over all tokens seen (all 4 lane groups).
@@ -753,14 +862,13 @@ __host__ __device__ inline int lds_total_bytes(int D, int R, int span, int BS, i
 // the workspace and arrives at the (sequence, KV head) word; the last to
 // arrive merges every partition's partials and writes out. With `draw`,
 // thread 0 takes a ticket from the counter for the workgroup's next item.
-template <class Tag, int D, int BS>
+template <class Tag, int D, int BS, bool P4>
 __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char* smem, int lds_main,
                                             int seq, int L, int kvh, int part, int tid, int wave,
                                             bool draw, int& ticket) {
   const int lane = tid & 63;
-  using Eng = TileEngine<Tag, D, BS>;
+  using Eng = TileEngine<Tag, D, BS, P4>;
   constexpr int RB = Eng::RB;
-  constexpr int VPL = Eng::VPL;
   constexpr int DQ = D / 4;  // quads (4 consecutive head-dim elements) per row
   const int G = p.group;
   const int R = p.q_len * G;  // query rows of this KV head: (token j, head g) -> j * G + g
@@ -896,17 +1004,11 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   float* s_o = reinterpret_cast<float*>(smem);
   float* s_m = reinterpret_cast<float*>(smem + lds_main);
   float* s_l = s_m + kWaves * 16;
-  if (valid) {
-    if (eng.grp == 0) {
-      s_m[wave * 16 + eng.col] = eng.m;
-      s_l[wave * 16 + eng.col] = lsum;
-    }
-    float* orow = s_o + (size_t)(wave * RW + eng.col) * OST;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < VPL; ++j) orow[eng.d_of(i, j)] = eng.acc[j][i];
+  if (valid && eng.grp == 0) {
+    s_m[wave * 16 + eng.col] = eng.m;
+    s_l[wave * 16 + eng.col] = lsum;
   }
+  eng.write_o(s_o + (size_t)(wave * RW) * OST, OST, valid, RW);
   __syncthreads();
 
   // One quad of one row per thread and pass: the group's waves combined with
@@ -1036,13 +1138,13 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
 // workgroup whose next item is a counter one draws a ticket while it merges
 // its current item; every ticket advances the counter, so every workgroup
 // ends.
-template <class Tag, int D, int BS>
+template <class Tag, int D, int BS, bool P4>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEU<Tag, D>::value)))
 void decode_partition_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int wave = uniform(threadIdx.x >> 6);
   const int span = p.partition < p.max_seq_len ? p.partition : p.max_seq_len;
-  const int lds_main = lds_main_bytes(D, p.q_len * p.group, span, BS, TileEngine<Tag, D, BS>::KT_BYTES);
+  const int lds_main = lds_main_bytes(D, p.q_len * p.group, span, BS, TileEngine<Tag, D, BS, P4>::KT_BYTES);
   // Two slots for the next item, used alternately: an item may pass no
   // barrier (a zero-length sequence), and a slot is rewritten only after the
   // barrier that follows every wave's read of it. The third int is the
@@ -1074,7 +1176,7 @@ void decode_partition_kernel(DecodeParams p) {
     // hoisted out of this loop and held in registers across the tiles.
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    decode_item<Tag, D, BS>(p, smem, lds_main, seq, uniform(pl.len[seq]), kvh, part, tid, wave, draw, ticket);
+    decode_item<Tag, D, BS, P4>(p, smem, lds_main, seq, uniform(pl.len[seq]), kvh, part, tid, wave, draw, ticket);
     if (threadIdx.x == 0) {
       const int64_t nx = !draw ? (int64_t)nxt_static : (ticket >= 0 ? (int64_t)ws + ticket : (int64_t)total);
       s_next[parity] = (nx >= 0 && nx < total) ? (int)nx : total;
@@ -1112,10 +1214,11 @@ int resident_workgroups(const void* kernel, size_t lds) {
   return n;
 }
 
-template <class Tag, int D, int BS>
-hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
+template <class Tag, int D, int BS, bool P4>
+hipError_t launch_p(const DecodeParams& p, hipStream_t stream) {
+  using Eng = TileEngine<Tag, D, BS, P4>;
   const int span = p.partition < p.max_seq_len ? p.partition : p.max_seq_len;
-  const void* kfn = reinterpret_cast<const void*>(&decode_partition_kernel<Tag, D, BS>);
+  const void* kfn = reinterpret_cast<const void*>(&decode_partition_kernel<Tag, D, BS, P4>);
   const size_t q_row = (size_t)p.q_len * p.num_heads * D;  // elements per sequence
   const size_t q_elem = (size_t)KV<Tag>::kQBytes;  // the output, unless fp32, has the query's type
   const size_t out_elem = p.out_f32 ? 4 : q_elem;
@@ -1125,7 +1228,7 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   // so that two workgroups fit per CU, when the rest of it leaves room.
   int chunk = kMaxSeqsPerLaunch;
   {
-    const int fixed = lds_total_bytes(D, p.q_len * p.group, span, BS, TileEngine<Tag, D, BS>::KT_BYTES, 0);
+    const int fixed = lds_total_bytes(D, p.q_len * p.group, span, BS, Eng::KT_BYTES, 0);
     const int room = (kLdsPerWorkgroup - fixed - 32) / 10;
     if (room < chunk) chunk = room > 256 ? room : 256;
   }
@@ -1139,16 +1242,26 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
     c.block_table = p.block_table + (size_t)s0 * p.max_blocks;
     c.seq_lens = p.seq_lens + s0;
     const size_t lds =
-        (size_t)lds_total_bytes(D, c.q_len * c.group, span, BS, TileEngine<Tag, D, BS>::KT_BYTES, c.num_seqs);
+        (size_t)lds_total_bytes(D, c.q_len * c.group, span, BS, Eng::KT_BYTES, c.num_seqs);
     const int64_t max_items = (int64_t)c.num_seqs * c.num_kv_heads * c.num_partitions;
     int64_t grid = resident_workgroups(kfn, lds);
     if (grid > max_items) grid = max_items;
     if (grid >= 8) grid = grid / 8 * 8;  // whole rounds over the 8 XCDs
-    decode_partition_kernel<Tag, D, BS><<<dim3((unsigned)grid), dim3(kThreads), lds, stream>>>(c);
+    decode_partition_kernel<Tag, D, BS, P4><<<dim3((unsigned)grid), dim3(kThreads), lds, stream>>>(c);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// e4m3 rows of 128 elements with at most 4 query rows per KV head take the
+// 4x4x1 P.V form; everything else the 16x16x4 one.
+template <class Tag, int D, int BS>
+hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
+  if constexpr (KV<Tag>::kF8 && D == 128) {
+    if (p.q_len * p.group <= 4) return launch_p<Tag, D, BS, true>(p, stream);
+  }
+  return launch_p<Tag, D, BS, false>(p, stream);
 }
 
 template <class Tag, int D>
