@@ -215,8 +215,11 @@ int paged_attn_multi_query_fp8(void* out, const void* query, const void* key_cac
  *              and seq_len prefix_lens[g] + suffix_lens[s]
  * (prefix_lens[g] a multiple of block_size: a partly filled shared block is
  * copied on write before a sample writes to it). Computed as a multi-query
- * pass over each group's prefix (the group's samples are its query rows), a
- * decode pass over each suffix, and a merge of the two by their log-sum-exp.
+ * pass over each group's prefix (the group's samples are its query rows) and
+ * a decode pass over each suffix, in one launch (the suffixes' items follow
+ * the prefixes' as workgroups run out of them; two launches when the batch
+ * exceeds one launch's work list), then a merge of the two by their
+ * log-sum-exp.
  *
  *   out, query             [num_groups * group_size, num_heads, head_dim]
  *   prefix_block_table     int32 [num_groups, max_prefix_blocks]; prefix_lens int32 [num_groups]
@@ -241,7 +244,7 @@ int paged_attn_decode_shared_prefix(void* out, const void* query, const void* ke
 /*
  * paged_attn_shared_prefix_workspace_size - bytes of workspace that
  * paged_attn_decode_shared_prefix needs (its two passes' fp32 outputs and
- * log-sum-exps, and the passes' own workspace). 0 when the arguments are
+ * log-sum-exps, and a workspace for each pass). 0 when the arguments are
  * invalid.
  */
 size_t paged_attn_shared_prefix_workspace_size(int num_groups, int group_size, int num_heads,

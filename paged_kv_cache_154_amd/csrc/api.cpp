@@ -141,14 +141,15 @@ namespace {
 // Every attention entry point: q_len new tokens per sequence (1 for decode),
 // query and out [num_seqs, q_len, num_heads, head_dim]. The query has
 // query_dtype: the KV dtype, or fp16/bf16 over an e4m3 pool (which takes a
-// K and a V scale per KV head).
+// K and a V scale per KV head). With `prepared`, the checked launch
+// parameters are stored there and nothing is launched.
 int attention(void* out, const void* query, const void* key_cache, const void* value_cache,
               const float* k_scale, const float* v_scale, const int32_t* block_table,
               const int32_t* seq_lens, int num_seqs, int q_len, int num_heads, int num_kv_heads,
               int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
               int max_seq_len, float scale, int kv_dtype, int query_dtype, int out_dtype,
               int partition_size, void* workspace, size_t workspace_bytes, hipStream_t stream,
-              float* lse = nullptr, int causal = 1) {
+              float* lse = nullptr, int causal = 1, pkv::DecodeParams* prepared = nullptr) {
   if (num_seqs < 0 || q_len < 1) return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !query || !key_cache || !value_cache || !block_table || !seq_lens)
@@ -214,6 +215,10 @@ int attention(void* out, const void* query, const void* key_cache, const void* v
   p.out_f32 = out_dtype == PKV_F32 ? 1 : 0;
   p.causal = causal;
   p.lse = lse;
+  if (prepared) {
+    *prepared = p;
+    return PKV_OK;
+  }
   const hipError_t e = pkv::launch_decode(p, kv_dtype, query_dtype, head_dim, block_size, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
@@ -232,17 +237,17 @@ size_t workspace_size(int num_seqs, int q_len, int num_heads, int num_kv_heads, 
 }
 
 // Shared-prefix decode: the prefix pass's and the suffix pass's fp32 outputs
-// and lse rows, each area 256-byte aligned, then one workspace that the two
-// passes use in turn (same stream).
+// and lse rows, then the prefix pass's workspace and the suffix pass's (both
+// passes run in one launch), each area 256-byte aligned.
 struct PrefixLayout {
-  size_t o_bytes, lse_bytes, inner_bytes;
-  size_t total() const { return 2 * o_bytes + 2 * lse_bytes + inner_bytes; }
+  size_t o_bytes, lse_bytes, pre_bytes, suf_bytes;
+  size_t total() const { return 2 * o_bytes + 2 * lse_bytes + pre_bytes + suf_bytes; }
 };
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 PrefixLayout prefix_layout(int num_groups, int group_size, int num_heads, int num_kv_heads,
                            int head_dim, int block_size, int max_prefix_len, int max_suffix_len,
                            int partition_size) {
-  PrefixLayout l{0, 0, 0};
+  PrefixLayout l{0, 0, 0, 0};
   const int64_t rows = (int64_t)num_groups * group_size * num_heads;
   const size_t a = workspace_size(num_groups, group_size, num_heads, num_kv_heads, head_dim, block_size,
                                   max_prefix_len, partition_size);
@@ -251,7 +256,8 @@ PrefixLayout prefix_layout(int num_groups, int group_size, int num_heads, int nu
   if (a == 0 || b == 0) return l;
   l.o_bytes = round256((size_t)rows * head_dim * sizeof(float));
   l.lse_bytes = round256((size_t)rows * sizeof(float));
-  l.inner_bytes = a > b ? a : b;
+  l.pre_bytes = round256(a);
+  l.suf_bytes = b;
   return l;
 }
 
@@ -305,24 +311,35 @@ int paged_attn_decode_shared_prefix(void* out, const void* query, const void* ke
   float* o_suf = reinterpret_cast<float*>(w + l.o_bytes);
   float* lse_pre = reinterpret_cast<float*>(w + 2 * l.o_bytes);
   float* lse_suf = reinterpret_cast<float*>(w + 2 * l.o_bytes + l.lse_bytes);
-  void* inner = w + 2 * l.o_bytes + 2 * l.lse_bytes;
+  void* ws_pre = w + 2 * l.o_bytes + 2 * l.lse_bytes;
+  void* ws_suf = static_cast<unsigned char*>(ws_pre) + l.pre_bytes;
   const int num_seqs = num_groups * group_size;
   // the prefix once per group: the group's samples are its query rows
   // ([num_seqs, H, D] read as [num_groups, group_size, H, D]), all of them
   // seeing the whole prefix
+  pkv::DecodeParams pre{}, suf{};
   int st = attention(o_pre, query, key_cache, value_cache, nullptr, nullptr, prefix_block_table, prefix_lens,
                      num_groups, group_size, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_prefix_blocks, max_prefix_len, scale, kv_dtype, kv_dtype, PKV_F32, partition_size,
-                     inner, l.inner_bytes, stream, lse_pre, 0);
+                     ws_pre, l.pre_bytes, stream, lse_pre, 0, &pre);
   if (st != PKV_OK) return st;
   // each sample's own suffix
   st = attention(o_suf, query, key_cache, value_cache, nullptr, nullptr, suffix_block_table, suffix_lens,
                  num_seqs, 1, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_suffix_blocks,
-                 max_suffix_len, scale, kv_dtype, kv_dtype, PKV_F32, partition_size, inner, l.inner_bytes,
-                 stream, lse_suf, 1);
+                 max_suffix_len, scale, kv_dtype, kv_dtype, PKV_F32, partition_size, ws_suf, l.suf_bytes,
+                 stream, lse_suf, 1, &suf);
   if (st != PKV_OK) return st;
-  const hipError_t e = pkv::launch_cascade_merge(out, o_pre, lse_pre, o_suf, lse_suf,
-                                                 (int64_t)num_seqs * num_heads, head_dim, out_dtype, stream);
+  // both passes in one launch, the suffixes filling the prefix pass's
+  // ramp-down; one after the other when they do not fit one launch
+  hipError_t e = pkv::launch_decode_pair(pre, suf, kv_dtype, head_dim, block_size, stream);
+  if (e == hipErrorNotSupported) {
+    (void)hipGetLastError();
+    e = pkv::launch_decode(pre, kv_dtype, kv_dtype, head_dim, block_size, stream);
+    if (e == hipSuccess) e = pkv::launch_decode(suf, kv_dtype, kv_dtype, head_dim, block_size, stream);
+  }
+  if (e != hipSuccess) return PKV_ERR_HIP;
+  e = pkv::launch_cascade_merge(out, o_pre, lse_pre, o_suf, lse_suf, (int64_t)num_seqs * num_heads, head_dim,
+                                out_dtype, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

@@ -1133,36 +1133,31 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   }
 }
 
-// Persistent: a grid of as many workgroups as fit on the GPU at once (a
-// multiple of 8), each working through its items of the schedule above. A
-// workgroup whose next item is a counter one draws a ticket while it merges
-// its current item; every ticket advances the counter, so every workgroup
-// ends.
+// The items of one pass (a launch's work list `pl` over the parameters p),
+// taken in turn by this workgroup: from item b of a static first round
+// (then static rounds or counter tickets, as above), or, with `dynamic`,
+// every item from the counter. `parity` alternates the two next-item slots
+// across passes.
 template <class Tag, int D, int BS, bool P4>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEU<Tag, D>::value)))
-void decode_partition_kernel(DecodeParams p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int wave = uniform(threadIdx.x >> 6);
-  const int span = p.partition < p.max_seq_len ? p.partition : p.max_seq_len;
-  const int lds_main = lds_main_bytes(D, p.q_len * p.group, span, BS, TileEngine<Tag, D, BS, P4>::KT_BYTES);
-  // Two slots for the next item, used alternately: an item may pass no
-  // barrier (a zero-length sequence), and a slot is rewritten only after the
-  // barrier that follows every wave's read of it. The third int is the
-  // merge flag of decode_item, the fourth is free.
-  int* s_next = reinterpret_cast<int*>(smem + lds_main + 2 * kWaves * 16 * 4);
-  if (blockIdx.x == 0 && threadIdx.x == 0) install_epoch(p.work, p.epoch);
-  if (p.num_partitions > 1) tag_arrival_words(p);
-  Plan pl = plan_at(reinterpret_cast<unsigned char*>(s_next + 4), p.num_seqs);
-  build_plan(p, pl, reinterpret_cast<uint64_t*>(smem));
+__device__ __forceinline__ void run_items(const DecodeParams& p, const Plan& pl, unsigned char* smem, int lds_main,
+                                          int* s_next, int wave, bool dynamic, int& parity) {
   const int entries = pl.n_full + pl.S;
   const int total = entries * p.num_kv_heads;
   const int grid = (int)gridDim.x;
-  const int ws = static_end(total, grid, 8 * pl.n_long >= 7 * entries);
+  const int ws = dynamic ? 0 : static_end(total, grid, 8 * pl.n_long >= 7 * entries);
   const int b = (int)blockIdx.x;
-
-  int parity = 0;
+  int w = b;
+  if (dynamic) {
+    if (threadIdx.x == 0) {
+      const int t = take_ticket(p.work, p.epoch);
+      s_next[parity] = (t >= 0 && t < total) ? t : total;
+    }
+    __syncthreads();
+    w = uniform(s_next[parity]);
+    parity ^= 1;
+  }
   int round = 0;  // static round of the current item
-  for (int w = b; (unsigned)w < (unsigned)total; parity ^= 1) {
+  for (; (unsigned)w < (unsigned)total; parity ^= 1) {
     const int e = w / p.num_kv_heads;
     const int kvh = w - e * p.num_kv_heads;
     int seq, part;
@@ -1184,6 +1179,72 @@ void decode_partition_kernel(DecodeParams p) {
     __syncthreads();
     w = uniform(s_next[parity]);
   }
+}
+
+// Persistent: a grid of as many workgroups as fit on the GPU at once (a
+// multiple of 8), each working through its items of the schedule above. A
+// workgroup whose next item is a counter one draws a ticket while it merges
+// its current item; every ticket advances the counter, so every workgroup
+// ends.
+template <class Tag, int D, int BS, bool P4>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEU<Tag, D>::value)))
+void decode_partition_kernel(DecodeParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int wave = uniform(threadIdx.x >> 6);
+  const int span = p.partition < p.max_seq_len ? p.partition : p.max_seq_len;
+  const int lds_main = lds_main_bytes(D, p.q_len * p.group, span, BS, TileEngine<Tag, D, BS, P4>::KT_BYTES);
+  // Two slots for the next item, used alternately: an item may pass no
+  // barrier (a zero-length sequence), and a slot is rewritten only after the
+  // barrier that follows every wave's read of it. The third int is the
+  // merge flag of decode_item, the fourth is free.
+  int* s_next = reinterpret_cast<int*>(smem + lds_main + 2 * kWaves * 16 * 4);
+  if (blockIdx.x == 0 && threadIdx.x == 0) install_epoch(p.work, p.epoch);
+  if (p.num_partitions > 1) tag_arrival_words(p);
+  Plan pl = plan_at(reinterpret_cast<unsigned char*>(s_next + 4), p.num_seqs);
+  build_plan(p, pl, reinterpret_cast<uint64_t*>(smem));
+  int parity = 0;
+  run_items<Tag, D, BS, P4>(p, pl, smem, lds_main, s_next, wave, false, parity);
+}
+
+// LDS of a two-pass launch: the larger main area of the two passes, then the
+// (m, l) slots and next-item slots, then both work lists.
+__host__ __device__ inline int pair_lds_main(int D, int BS, int kt_bytes, const DecodeParams& a,
+                                             const DecodeParams& b) {
+  const int la = lds_main_bytes(D, a.q_len * a.group, a.partition < a.max_seq_len ? a.partition : a.max_seq_len,
+                                BS, kt_bytes);
+  const int lb = lds_main_bytes(D, b.q_len * b.group, b.partition < b.max_seq_len ? b.partition : b.max_seq_len,
+                                BS, kt_bytes);
+  return la > lb ? la : lb;
+}
+
+// Two passes over the same pools in one launch (shared-prefix decode: the
+// groups' prefixes, then the samples' own blocks). Every workgroup works
+// through the first pass's items as the partition kernel does, then takes
+// the second pass's items from that pass's own counter, so the first pass's
+// ramp-down is filled with the second pass's (short) items instead of
+// ending the launch. Each pass has its own epoch, counter, work list and
+// split-K workspace.
+template <class Tag, int D, int BS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEU<Tag, D>::value)))
+void decode_pair_kernel(DecodeParams p0, DecodeParams p1) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int wave = uniform(threadIdx.x >> 6);
+  const int lds_main = pair_lds_main(D, BS, TileEngine<Tag, D, BS>::KT_BYTES, p0, p1);
+  int* s_next = reinterpret_cast<int*>(smem + lds_main + 2 * kWaves * 16 * 4);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    install_epoch(p0.work, p0.epoch);
+    install_epoch(p1.work, p1.epoch);
+  }
+  if (p0.num_partitions > 1) tag_arrival_words(p0);
+  if (p1.num_partitions > 1) tag_arrival_words(p1);
+  unsigned char* plans = reinterpret_cast<unsigned char*>(s_next + 4);
+  Plan pl0 = plan_at(plans, p0.num_seqs);
+  Plan pl1 = plan_at(plans + plan_bytes(p0.num_seqs), p1.num_seqs);
+  build_plan(p0, pl0, reinterpret_cast<uint64_t*>(smem));
+  build_plan(p1, pl1, reinterpret_cast<uint64_t*>(smem));
+  int parity = 0;
+  run_items<Tag, D, BS, false>(p0, pl0, smem, lds_main, s_next, wave, false, parity);
+  run_items<Tag, D, BS, false>(p1, pl1, smem, lds_main, s_next, wave, true, parity);
 }
 
 // ============================================================================
@@ -1264,6 +1325,47 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   return launch_p<Tag, D, BS, false>(p, stream);
 }
 
+// Two passes in one launch when both fit one launch's work list and LDS
+// budget; hipErrorNotSupported otherwise (the caller then runs them one
+// after the other).
+template <class Tag, int D, int BS>
+hipError_t launch_pair_t(DecodeParams a, DecodeParams b, hipStream_t stream) {
+  if (a.num_seqs > kMaxSeqsPerLaunch || b.num_seqs > kMaxSeqsPerLaunch) return hipErrorNotSupported;
+  const int kt = TileEngine<Tag, D, BS>::KT_BYTES;
+  const size_t lds = (size_t)pair_lds_main(D, BS, kt, a, b) + 2 * kWaves * 16 * 4 + 16 + plan_bytes(a.num_seqs) +
+                     plan_bytes(b.num_seqs);
+  if (lds > (size_t)kLdsPerWorkgroup) return hipErrorNotSupported;
+  a.epoch = next_launch_epoch();
+  b.epoch = next_launch_epoch();
+  const void* kfn = reinterpret_cast<const void*>(&decode_pair_kernel<Tag, D, BS>);
+  const int64_t max_items = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions +
+                            (int64_t)b.num_seqs * b.num_kv_heads * b.num_partitions;
+  int64_t grid = resident_workgroups(kfn, lds);
+  if (grid > max_items) grid = max_items;
+  if (grid >= 8) grid = grid / 8 * 8;
+  decode_pair_kernel<Tag, D, BS><<<dim3((unsigned)grid), dim3(kThreads), lds, stream>>>(a, b);
+  return hipGetLastError();
+}
+
+template <class Tag, int D>
+hipError_t launch_pair_bs(const DecodeParams& a, const DecodeParams& b, int bs, hipStream_t stream) {
+  switch (bs) {
+    case 8: return launch_pair_t<Tag, D, 8>(a, b, stream);
+    case 16: return launch_pair_t<Tag, D, 16>(a, b, stream);
+    case 32: return launch_pair_t<Tag, D, 32>(a, b, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class Tag>
+hipError_t launch_pair_d(const DecodeParams& a, const DecodeParams& b, int d, int bs, hipStream_t stream) {
+  switch (d) {
+    case 64: return launch_pair_bs<Tag, 64>(a, b, bs, stream);
+    case 128: return launch_pair_bs<Tag, 128>(a, b, bs, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <class Tag, int D>
 hipError_t launch_bs(const DecodeParams& p, int bs, hipStream_t stream) {
   switch (bs) {
@@ -1296,6 +1398,16 @@ hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int query_dtype, i
       if (query_dtype == 2) return launch_d<E4M3BF16Tag>(p, head_dim, block_size, stream);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_pair(const DecodeParams& a, const DecodeParams& b, int kv_dtype, int head_dim,
+                              int block_size, hipStream_t stream) {
+  switch (kv_dtype) {
+    case 0: return launch_pair_d<F32Tag>(a, b, head_dim, block_size, stream);
+    case 1: return launch_pair_d<F16Tag>(a, b, head_dim, block_size, stream);
+    case 2: return launch_pair_d<BF16Tag>(a, b, head_dim, block_size, stream);
+    default: return hipErrorNotSupported;
   }
 }
 

@@ -126,3 +126,23 @@ def test_prefix_share_workload_reads_each_shared_block_once():
                                   torch.from_numpy(wl.seq_lens).to(DEV), wl.scale, wl.max_seq_len)
             torch.cuda.synchronize()
             assert (dec - out).abs().max().item() <= 1e-5
+
+
+def test_shared_prefix_beyond_one_launch_runs_the_passes_in_turn():
+    """2 100 samples (700 groups of 3) exceed one launch's work list, so the
+    prefix and suffix passes run as two launches instead of one; sampled
+    sequences against the oracle."""
+    groups, n = 700, 3
+    rng = np.random.default_rng(5)
+    pblocks = (1 + rng.integers(0, 4, groups)).tolist()
+    slens = rng.integers(0, 40, groups * n).tolist()
+    q, kc, vc, pt, pl, st, sl = _grouped(77, groups, n, pblocks, slens, 8, 2, 64, 16, torch.bfloat16)
+    seqs = sorted(set([0, 1, 2, 3, 1000, 2047, 2048, 2049, 2099] + rng.integers(0, groups * n, 9).tolist()))
+    ref = oracle.decode_shared_prefix(q, kc, vc, pt, pl, st, sl, n, 0.125, seqs=seqs)
+    d = [torch.from_numpy(x).to(DEV) for x in (pt, pl, st, sl)]
+    say(f"shared prefix, {groups * n} samples (two launches)")
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    pkv.paged_attn_decode_shared_prefix(out, q.to(DEV), kc.to(DEV), vc.to(DEV), *d, n, 0.125,
+                                        int(pl.max()), int(sl.max()))
+    torch.cuda.synchronize()
+    assert max_err(out, ref, seqs) <= TOL[torch.bfloat16]
