@@ -174,17 +174,16 @@ struct KVe4m3 {
   static constexpr int kQBytes = 2;
   static constexpr bool kF8 = true;
   __device__ static inline f32x4 qk(const uint4& k, const uint4& q, f32x4 acc) { return Q16::qk(k, q, acc); }
-  // four codes -> two words of 16-bit values (element order kept)
+  // four codes -> two words of 16-bit values (element order kept): the
+  // scaled pair conversions at scale 1, one instruction per two codes (exact
+  // for every code; checked on MI355X against the format's values, NaN kept)
   __device__ static inline void widen4(uint32_t w, uint32_t& lo, uint32_t& hi) {
-    const f32x2v a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-    const f32x2v b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
     if constexpr (kBF) {
-      // bf16 is the upper half of the fp32 (exact here)
-      lo = __builtin_amdgcn_perm(__float_as_uint(a.y), __float_as_uint(a.x), 0x07060302u);
-      hi = __builtin_amdgcn_perm(__float_as_uint(b.y), __float_as_uint(b.x), 0x07060302u);
+      lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+      hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
     } else {
-      lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a.x, a.y));
-      hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(b.x, b.y));
+      lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+      hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
     }
   }
   // 16 codes -> the two 8-element key chunks of the 16-bit MFMA
@@ -506,17 +505,38 @@ struct TileEngine {
         const float w0 = __shfl(s[2 * (q & 1)], src);
         const float w1 = __shfl(s[2 * (q & 1) + 1], src);
         const float w = second ? w1 : w0;
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc[c] = __builtin_amdgcn_mfma_f32_4x4x1f32(f8_at(g.vq[q], c), w, acc[c], 0, 0, 0);
+        // the word's 4 codes widened two at a time
+        const f32x2v v01 = __builtin_amdgcn_cvt_pk_f32_fp8(g.vq[q], false);
+        const f32x2v v23 = __builtin_amdgcn_cvt_pk_f32_fp8(g.vq[q], true);
+        acc[0] = __builtin_amdgcn_mfma_f32_4x4x1f32(v01.x, w, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_4x4x1f32(v01.y, w, acc[1], 0, 0, 0);
+        acc[2] = __builtin_amdgcn_mfma_f32_4x4x1f32(v23.x, w, acc[2], 0, 0, 0);
+        acc[3] = __builtin_amdgcn_mfma_f32_4x4x1f32(v23.y, w, acc[3], 0, 0, 0);
       }
     } else {
       // O^T += V^T P^T, 4 tokens per MFMA
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (kF8) {  // the row's codes widened two at a time
+          float e[VPL];
 #pragma unroll
-        for (int j = 0; j < VPL; ++j)
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(Tr::elem(g.vr[r], j), s[r], acc[j], 0, 0, 0);
+          for (int u = 0; u < VPL / 4; ++u) {
+            const f32x2v a = __builtin_amdgcn_cvt_pk_f32_fp8(g.vr[r][u], false);
+            const f32x2v b = __builtin_amdgcn_cvt_pk_f32_fp8(g.vr[r][u], true);
+            e[4 * u] = a.x;
+            e[4 * u + 1] = a.y;
+            e[4 * u + 2] = b.x;
+            e[4 * u + 3] = b.y;
+          }
+#pragma unroll
+          for (int j = 0; j < VPL; ++j)
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(e[j], s[r], acc[j], 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int j = 0; j < VPL; ++j)
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(Tr::elem(g.vr[r], j), s[r], acc[j], 0, 0, 0);
+        }
+      }
     }
   }
 
