@@ -50,6 +50,11 @@ extern "C" {
 /* Same type as HIP's hipStream_t (an opaque handle). */
 typedef struct ihipStream_t* hipStream_t;
 #endif
+#ifndef PAGEDKV_EVENT_T_DEFINED
+#define PAGEDKV_EVENT_T_DEFINED
+/* Same type as HIP's hipEvent_t (an opaque handle). */
+typedef struct ihipEvent_t* hipEvent_t;
+#endif
 
 enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_E4M3 = 3 };
 
@@ -384,6 +389,28 @@ int pagedkv_check_decode_inputs(const int32_t* block_table,
  */
 int pagedkv_stream_read(const void* src, size_t bytes, uint32_t* sink, int grid,
                         hipStream_t stream);
+
+/*
+ * paged_attn_timed - measurement aid: the attention of paged_attn_decode
+ * (q_len 1, kv_dtype PKV_F32/F16/BF16, query of the KV dtype, no scales),
+ * paged_attn_multi_query (q_len > 1), paged_attn_decode_fp8 or
+ * paged_attn_multi_query_fp8 (kv_dtype PKV_E4M3 with k_scale, v_scale and a
+ * query_dtype of PKV_F16 or PKV_BF16), with the same arguments, checks and
+ * results as those calls, and two HIP events that the caller created
+ * (hipEventCreate): start is set to the start of the call's first kernel
+ * launch and stop to the end of its last one, by the launches themselves
+ * (hipExtLaunchKernel), so that hipEventElapsedTime(start, stop) is the
+ * kernels' own time, without the dispatch latency of separately recorded
+ * events. k_scale / v_scale may be NULL for the 16-bit dtypes.
+ * Returns PKV_ERR_NULL when an event is NULL.
+ */
+int paged_attn_timed(void* out, const void* query, const void* key_cache, const void* value_cache,
+                     const float* k_scale, const float* v_scale, const int32_t* block_table,
+                     const int32_t* seq_lens, int num_seqs, int q_len, int num_heads,
+                     int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                     int max_blocks_per_seq, int max_seq_len, float scale, int kv_dtype,
+                     int query_dtype, int out_dtype, int partition_size, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
 /* pagedkv_status_string - a static, NUL-terminated name for a status code. */
 const char* pagedkv_status_string(int status);

@@ -35,6 +35,8 @@ block_table int32 ``[num_seqs, max_blocks_per_seq]``; seq_lens int32
 
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from ._lib import (PKV_BF16, PKV_E4M3, PKV_F16, PKV_F32, LIB_PATH, PagedKVError,  # noqa: F401
@@ -113,7 +115,7 @@ def workspace_for(query: torch.Tensor, key_cache: torch.Tensor, max_seq_len: int
 
 def _attention(name: str, out, query, key_cache, value_cache, block_table, seq_lens, scale,
                max_seq_len, partition_size, workspace, stream, k_scale=None,
-               v_scale=None) -> torch.Tensor:
+               v_scale=None, events=None) -> torch.Tensor:
     multi = "multi_query" in name
     f8 = name.endswith("_fp8")
     want = 4 if multi else 3
@@ -145,6 +147,23 @@ def _attention(name: str, out, query, key_cache, value_cache, block_table, seq_l
     if workspace is None:
         workspace = workspace_for(query, key_cache, max_seq_len, partition_size)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if events is not None:
+        # the same attention through paged_attn_timed: the launches set the
+        # two events to the kernels' own start and end
+        start, stop = events
+        for ev in (start, stop):
+            if ev.cuda_event == 0:          # created on first record
+                ev.record(torch.cuda.current_stream(query.device))
+        q_dt = dtype_code(query.dtype)
+        st = lib().paged_attn_timed(
+            _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+            _ptr(k_scale) if f8 else None, _ptr(v_scale) if f8 else None, _ptr(block_table),
+            _ptr(seq_lens), S, Q, H, Hkv, D, bs, NB, block_table.shape[1], int(max_seq_len),
+            float(scale), PKV_E4M3 if f8 else q_dt, q_dt, dtype_code(out.dtype), int(partition_size),
+            _ptr(workspace), ws_bytes, _stream(query, stream), ctypes.c_void_p(start.cuda_event),
+            ctypes.c_void_p(stop.cuda_event))
+        check(st, "paged_attn_timed")
+        return out
     head = [_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache)]
     if f8:
         head += [_ptr(k_scale), _ptr(v_scale)]
@@ -164,22 +183,25 @@ def paged_attn_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.T
                       value_cache: torch.Tensor, block_table: torch.Tensor,
                       seq_lens: torch.Tensor, scale: float, max_seq_len: int,
                       partition_size: int = 0, workspace: torch.Tensor | None = None,
-                      stream=None) -> torch.Tensor:
+                      stream=None, events=None) -> torch.Tensor:
     """Decode attention of one query token per sequence over the paged pool.
 
     ``workspace`` must hold ``paged_attn_workspace_size(...)`` bytes (the
     item counter and split-K partials; no initialisation needed); later calls
     on the same stream can reuse it. With ``workspace=None`` one is allocated
-    by torch."""
+    by torch. ``events=(start, stop)`` (torch.cuda.Event(enable_timing=True))
+    runs the same call through paged_attn_timed: the launches themselves set
+    the events to the kernels' start and end (a measurement aid)."""
     return _attention("paged_attn_decode", out, query, key_cache, value_cache, block_table,
-                      seq_lens, scale, max_seq_len, partition_size, workspace, stream)
+                      seq_lens, scale, max_seq_len, partition_size, workspace, stream,
+                      events=events)
 
 
 def paged_attn_multi_query(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
                            value_cache: torch.Tensor, block_table: torch.Tensor,
                            seq_lens: torch.Tensor, scale: float, max_seq_len: int,
                            partition_size: int = 0, workspace: torch.Tensor | None = None,
-                           stream=None) -> torch.Tensor:
+                           stream=None, events=None) -> torch.Tensor:
     """Causal attention of the last ``q_len`` tokens of each sequence (query
     ``[S, q_len, H, D]``; their K/V already written to the pool): new token j
     sees positions ``0 .. seq_len - q_len + j``. ``q_len * (H / Hkv)`` must be
@@ -187,19 +209,20 @@ def paged_attn_multi_query(out: torch.Tensor, query: torch.Tensor, key_cache: to
     ``paged_attn_multi_query_workspace_size``."""
     return _attention("paged_attn_multi_query", out, query, key_cache, value_cache,
                       block_table, seq_lens, scale, max_seq_len, partition_size, workspace,
-                      stream)
+                      stream, events=events)
 
 
 def paged_attn_decode_fp8(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
                           value_cache: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor,
                           block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float,
                           max_seq_len: int, partition_size: int = 0,
-                          workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                          workspace: torch.Tensor | None = None, stream=None,
+                          events=None) -> torch.Tensor:
     """Decode over e4m3 pools: code * k_scale[kv head] and code * v_scale[kv head]
     stand for K and V. query bf16/fp16 [S, H, D]; out of the query's type or fp32."""
     return _attention("paged_attn_decode_fp8", out, query, key_cache, value_cache, block_table,
                       seq_lens, scale, max_seq_len, partition_size, workspace, stream,
-                      k_scale, v_scale)
+                      k_scale, v_scale, events=events)
 
 
 def paged_attn_multi_query_fp8(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
@@ -207,11 +230,11 @@ def paged_attn_multi_query_fp8(out: torch.Tensor, query: torch.Tensor, key_cache
                                v_scale: torch.Tensor, block_table: torch.Tensor,
                                seq_lens: torch.Tensor, scale: float, max_seq_len: int,
                                partition_size: int = 0, workspace: torch.Tensor | None = None,
-                               stream=None) -> torch.Tensor:
+                               stream=None, events=None) -> torch.Tensor:
     """paged_attn_multi_query over e4m3 pools (query [S, q_len, H, D])."""
     return _attention("paged_attn_multi_query_fp8", out, query, key_cache, value_cache,
                       block_table, seq_lens, scale, max_seq_len, partition_size, workspace,
-                      stream, k_scale, v_scale)
+                      stream, k_scale, v_scale, events=events)
 
 
 def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,

@@ -25,6 +25,8 @@ SIGNATURES = {
                                         _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                         _c_int, _c_int, _c_float, _c_int, _c_int, _c_int, _c_ptr,
                                         _c_size, _c_ptr]),
+    "paged_attn_timed": (_c_int, [_c_ptr] * 8 + [_c_int] * 9 + [_c_float] + [_c_int] * 4
+                         + [_c_ptr, _c_size, _c_ptr, _c_ptr, _c_ptr]),
     "paged_attn_multi_query_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int,
                                                         _c_int, _c_int, _c_int]),
     "paged_attn_decode_fp8": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,

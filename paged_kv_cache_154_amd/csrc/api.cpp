@@ -149,7 +149,8 @@ int attention(void* out, const void* query, const void* key_cache, const void* v
               int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
               int max_seq_len, float scale, int kv_dtype, int query_dtype, int out_dtype,
               int partition_size, void* workspace, size_t workspace_bytes, hipStream_t stream,
-              float* lse = nullptr, int causal = 1, pkv::DecodeParams* prepared = nullptr) {
+              float* lse = nullptr, int causal = 1, pkv::DecodeParams* prepared = nullptr,
+              hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
   if (num_seqs < 0 || q_len < 1) return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !query || !key_cache || !value_cache || !block_table || !seq_lens)
@@ -219,7 +220,8 @@ int attention(void* out, const void* query, const void* key_cache, const void* v
     *prepared = p;
     return PKV_OK;
   }
-  const hipError_t e = pkv::launch_decode(p, kv_dtype, query_dtype, head_dim, block_size, stream);
+  const hipError_t e = pkv::launch_decode(p, kv_dtype, query_dtype, head_dim, block_size, stream, ev_start,
+                                          ev_stop);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -354,6 +356,21 @@ size_t paged_attn_multi_query_workspace_size(int num_seqs, int q_len, int num_he
                                              int partition_size) {
   return workspace_size(num_seqs, q_len, num_heads, num_kv_heads, head_dim, block_size, max_seq_len,
                         partition_size);
+}
+
+int paged_attn_timed(void* out, const void* query, const void* key_cache, const void* value_cache,
+                     const float* k_scale, const float* v_scale, const int32_t* block_table,
+                     const int32_t* seq_lens, int num_seqs, int q_len, int num_heads,
+                     int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                     int max_blocks_per_seq, int max_seq_len, float scale, int kv_dtype,
+                     int query_dtype, int out_dtype, int partition_size, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  if (!start || !stop) return PKV_ERR_NULL;
+  if (kv_dtype != PKV_E4M3 && (k_scale || v_scale)) return PKV_ERR_UNSUPPORTED;  // scales are e4m3's
+  return attention(out, query, key_cache, value_cache, k_scale, v_scale, block_table, seq_lens, num_seqs,
+                   q_len, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                   max_seq_len, scale, kv_dtype, query_dtype, out_dtype, partition_size, workspace,
+                   workspace_bytes, stream, nullptr, 1, nullptr, start, stop);
 }
 
 int paged_attn_decode(void* out, const void* query, const void* key_cache, const void* value_cache,

@@ -54,6 +54,8 @@
 
 #include "pagedkv_internal.h"
 
+#include <hip/hip_ext.h>
+
 #include <math.h>
 
 #include <mutex>
@@ -1296,7 +1298,7 @@ int resident_workgroups(const void* kernel, size_t lds) {
 }
 
 template <class Tag, int D, int BS, bool P4>
-hipError_t launch_p(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_p(const DecodeParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   using Eng = TileEngine<Tag, D, BS, P4>;
   const int span = p.partition < p.max_seq_len ? p.partition : p.max_seq_len;
   const void* kfn = reinterpret_cast<const void*>(&decode_partition_kernel<Tag, D, BS, P4>);
@@ -1328,7 +1330,13 @@ hipError_t launch_p(const DecodeParams& p, hipStream_t stream) {
     int64_t grid = resident_workgroups(kfn, lds);
     if (grid > max_items) grid = max_items;
     if (grid >= 8) grid = grid / 8 * 8;  // whole rounds over the 8 XCDs
-    decode_partition_kernel<Tag, D, BS, P4><<<dim3((unsigned)grid), dim3(kThreads), lds, stream>>>(c);
+    hipEvent_t ev0 = s0 == 0 ? start : nullptr;                 // the first launch's start
+    hipEvent_t ev1 = s0 + c.num_seqs >= p.num_seqs ? stop : nullptr;  // the last one's end
+    if (ev0 || ev1)
+      hipExtLaunchKernelGGL(decode_partition_kernel<Tag, D, BS, P4>, dim3((unsigned)grid), dim3(kThreads),
+                            (uint32_t)lds, stream, ev0, ev1, 0u, c);
+    else
+      decode_partition_kernel<Tag, D, BS, P4><<<dim3((unsigned)grid), dim3(kThreads), lds, stream>>>(c);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1338,11 +1346,11 @@ hipError_t launch_p(const DecodeParams& p, hipStream_t stream) {
 // e4m3 rows of 128 elements with at most 4 query rows per KV head take the
 // 4x4x1 P.V form; everything else the 16x16x4 one.
 template <class Tag, int D, int BS>
-hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_t(const DecodeParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if constexpr (KV<Tag>::kF8 && D == 128) {
-    if (p.q_len * p.group <= 4) return launch_p<Tag, D, BS, true>(p, stream);
+    if (p.q_len * p.group <= 4) return launch_p<Tag, D, BS, true>(p, stream, start, stop);
   }
-  return launch_p<Tag, D, BS, false>(p, stream);
+  return launch_p<Tag, D, BS, false>(p, stream, start, stop);
 }
 
 // Two passes in one launch when both fit one launch's work list and LDS
@@ -1387,20 +1395,20 @@ hipError_t launch_pair_d(const DecodeParams& a, const DecodeParams& b, int d, in
 }
 
 template <class Tag, int D>
-hipError_t launch_bs(const DecodeParams& p, int bs, hipStream_t stream) {
+hipError_t launch_bs(const DecodeParams& p, int bs, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   switch (bs) {
-    case 8: return launch_t<Tag, D, 8>(p, stream);
-    case 16: return launch_t<Tag, D, 16>(p, stream);
-    case 32: return launch_t<Tag, D, 32>(p, stream);
+    case 8: return launch_t<Tag, D, 8>(p, stream, start, stop);
+    case 16: return launch_t<Tag, D, 16>(p, stream, start, stop);
+    case 32: return launch_t<Tag, D, 32>(p, stream, start, stop);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <class Tag>
-hipError_t launch_d(const DecodeParams& p, int d, int bs, hipStream_t stream) {
+hipError_t launch_d(const DecodeParams& p, int d, int bs, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   switch (d) {
-    case 64: return launch_bs<Tag, 64>(p, bs, stream);
-    case 128: return launch_bs<Tag, 128>(p, bs, stream);
+    case 64: return launch_bs<Tag, 64>(p, bs, stream, start, stop);
+    case 128: return launch_bs<Tag, 128>(p, bs, stream, start, stop);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1408,14 +1416,14 @@ hipError_t launch_d(const DecodeParams& p, int d, int bs, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int query_dtype, int head_dim,
-                         int block_size, hipStream_t stream) {
+                         int block_size, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   switch (kv_dtype) {
-    case 0: return launch_d<F32Tag>(p, head_dim, block_size, stream);
-    case 1: return launch_d<F16Tag>(p, head_dim, block_size, stream);
-    case 2: return launch_d<BF16Tag>(p, head_dim, block_size, stream);
+    case 0: return launch_d<F32Tag>(p, head_dim, block_size, stream, start, stop);
+    case 1: return launch_d<F16Tag>(p, head_dim, block_size, stream, start, stop);
+    case 2: return launch_d<BF16Tag>(p, head_dim, block_size, stream, start, stop);
     case 3:
-      if (query_dtype == 1) return launch_d<E4M3F16Tag>(p, head_dim, block_size, stream);
-      if (query_dtype == 2) return launch_d<E4M3BF16Tag>(p, head_dim, block_size, stream);
+      if (query_dtype == 1) return launch_d<E4M3F16Tag>(p, head_dim, block_size, stream, start, stop);
+      if (query_dtype == 2) return launch_d<E4M3BF16Tag>(p, head_dim, block_size, stream, start, stop);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }

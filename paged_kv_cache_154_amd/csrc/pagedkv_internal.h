@@ -58,8 +58,11 @@ uint32_t next_launch_epoch();
 
 // kv_dtype: 0 fp32, 1 fp16, 2 bf16 (the query's type too), 3 e4m3 with a
 // query of type query_dtype (1 fp16 or 2 bf16).
+// start / stop (optional): events updated with the start of the first launch
+// and the end of the last (hipExtLaunchKernel's own timestamps).
 hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int query_dtype, int head_dim,
-                         int block_size, hipStream_t stream);
+                         int block_size, hipStream_t stream, hipEvent_t start = nullptr,
+                         hipEvent_t stop = nullptr);
 
 // Two passes over the same pools (fp32, fp16 or bf16; one query dtype) in one
 // launch, the second's items taken after the first's: a.work and b.work are

@@ -136,6 +136,31 @@ def test_decode_fp8_host_checks(kw, code):
     assert _decode_fp8(**kw) == code
 
 
+def _timed(**kw):
+    a = dict(out=FAKE, query=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, bt=FAKE, sl=FAKE, S=4, Q=1,
+             H=32, Hkv=8, D=128, bs=16, NB=100, MB=16, maxlen=256, scale=0.088, kvdt=2, qdt=2,
+             outdt=2, P=0, ws=None, wsb=0, start=FAKE, stop=FAKE)
+    a.update(kw)
+    return _lib.lib().paged_attn_timed(a["out"], a["query"], a["k"], a["v"], a["ks"], a["vs"], a["bt"],
+                                       a["sl"], a["S"], a["Q"], a["H"], a["Hkv"], a["D"], a["bs"],
+                                       a["NB"], a["MB"], a["maxlen"], a["scale"], a["kvdt"], a["qdt"],
+                                       a["outdt"], a["P"], a["ws"], a["wsb"], None, a["start"],
+                                       a["stop"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(start=None), NULL),                  # both events are required
+    (dict(stop=None), NULL),
+    (dict(ks=FAKE, vs=FAKE), UNSUP),           # scales belong to e4m3 pools
+    (dict(kvdt=3), NULL),                      # an e4m3 pool without its scales
+    (dict(kvdt=3, ks=FAKE, vs=FAKE, qdt=0, outdt=0), UNSUP),
+    (dict(Q=0), SHAPE),
+    (dict(ws=None, wsb=0, S=4), WS),           # the checks of the plain calls apply
+])
+def test_timed_host_checks(kw, code):
+    assert _timed(**kw) == code
+
+
 def test_sixteen_bit_entry_points_refuse_e4m3_pools():
     assert _decode(kvdt=3, outdt=3) == UNSUP
     assert _decode(kvdt=3, outdt=0) == UNSUP
