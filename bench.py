@@ -286,7 +286,8 @@ def per_config(pkv, W, dev, calls=200, warm=20):
     """Every page-shaped workload (configs 2-5): each decode call timed cold
     (a 1 GiB streaming read evicts L2 and the Infinity Cache before it,
     outside the events; a read, because a write flush leaves dirty lines
-    whose write-back would be charged to the call), median and p10/p90, a
+    whose write-back would be charged to the call) by the kernel's own start
+    and end (events its launch sets, paged_attn_timed), median and p10/p90, a
     warm back-to-back mean, and the cache ops of the step (mean of
     back-to-back calls: one event pair per call would dwarf a few-us kernel)."""
     import torch
@@ -338,9 +339,8 @@ def per_config(pkv, W, dev, calls=200, warm=20):
             ev = _events(calls)
             for a, b in ev:
                 flush()
-                a.record()
-                pkv.paged_attn_decode(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
-                b.record()
+                pkv.paged_attn_decode(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws,
+                                      events=(a, b))
             w0, w1 = _events(1)[0]
             w0.record()
             for _ in range(warm):
