@@ -247,6 +247,28 @@ int paged_attn_decode_shared_prefix(void* out, const void* query, const void* ke
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * paged_attn_decode_shared_prefix_fp8 - paged_attn_decode_shared_prefix over
+ * e4m3 pools (reshape_and_cache_fp8's format: a code stands for code *
+ * k_scale[kv head] in key_cache, code * v_scale[kv head] in value_cache;
+ * "LLM inference optimisation in practice", section 6.2, and the groups'
+ * sharing as above). query and out as for paged_attn_decode_fp8: query of
+ * query_dtype PKV_F16 or PKV_BF16, out of the query's type or PKV_F32.
+ * k_scale, v_scale: fp32 [num_kv_heads] device arrays (NULL: PKV_ERR_NULL).
+ * The two passes run as two launches. Workspace: the size that
+ * paged_attn_shared_prefix_workspace_size gives for the same arguments.
+ */
+int paged_attn_decode_shared_prefix_fp8(void* out, const void* query, const void* key_cache,
+                                        const void* value_cache, const float* k_scale,
+                                        const float* v_scale, const int32_t* prefix_block_table,
+                                        const int32_t* prefix_lens, int num_groups, int group_size,
+                                        int max_prefix_blocks, int max_prefix_len,
+                                        const int32_t* suffix_block_table, const int32_t* suffix_lens,
+                                        int max_suffix_blocks, int max_suffix_len, int num_heads,
+                                        int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                        float scale, int query_dtype, int out_dtype, int partition_size,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * paged_attn_shared_prefix_workspace_size - bytes of workspace that
  * paged_attn_decode_shared_prefix needs (its two passes' fp32 outputs and
  * log-sum-exps, and a workspace for each pass). 0 when the arguments are

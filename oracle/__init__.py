@@ -40,7 +40,8 @@ Pins (checked by ``tests/test_oracle_*.py`` without a GPU):
     finite code, the quotient formed in fp32; the scatter's placement and
     negative slots; attention over pools of small integers (exact in e4m3)
     equal to ``decode``, k_scale and v_scale acting as scalings; multi-query
-    rows equal to decodes of their prefixes; planted mistakes (scales
+    rows equal to decodes of their prefixes; shared-prefix decode equal to
+    ``decode_fp8`` over the joined tables; planted mistakes (scales
     swapped or dividing, exponent bias 8, no subnormals, ties away from
     even, no saturation) each fail a pin.
 No function here is "parity unpinned".

@@ -29,7 +29,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .paged_attention import decode, multi_query
+from .paged_attention import decode, decode_shared_prefix, multi_query
 
 E4M3_MAX = 448.0
 E4M3_NAN = 0x7F
@@ -139,3 +139,14 @@ def multi_query_fp8(query, key_cache, value_cache, k_scale, v_scale, block_table
     """Multi-query (q_len new tokens, causal) over an e4m3 pool."""
     return multi_query(query, dequantize(key_cache, k_scale), dequantize(value_cache, v_scale),
                        block_table, seq_lens, scale, seqs=seqs)
+
+
+def decode_shared_prefix_fp8(query, key_cache, value_cache, k_scale, v_scale, prefix_block_table,
+                             prefix_lens, suffix_block_table, suffix_lens, group_size: int,
+                             scale: float, seqs=None) -> np.ndarray:
+    """Shared-prefix decode (groups of samples reading one prefix of whole
+    blocks, then each its own blocks) over an e4m3 pool: the shared-prefix
+    oracle of the paged_attention module on the dequantised K and V."""
+    return decode_shared_prefix(query, dequantize(key_cache, k_scale), dequantize(value_cache, v_scale),
+                                prefix_block_table, prefix_lens, suffix_block_table, suffix_lens,
+                                group_size, scale, seqs=seqs)

@@ -268,14 +268,27 @@ def paged_attn_decode_shared_prefix(out: torch.Tensor, query: torch.Tensor,
                                     group_size: int, scale: float, max_prefix_len: int,
                                     max_suffix_len: int, partition_size: int = 0,
                                     workspace: torch.Tensor | None = None,
-                                    stream=None) -> torch.Tensor:
+                                    stream=None, k_scale: torch.Tensor | None = None,
+                                    v_scale: torch.Tensor | None = None) -> torch.Tensor:
     """Decode for groups of group_size consecutive sequences that share a
     prefix of whole blocks: sequence s of group g attends over
     prefix_block_table[g] (prefix_lens[g] tokens) then suffix_block_table[s]
-    (suffix_lens[s] tokens); each shared block is read once per group."""
+    (suffix_lens[s] tokens); each shared block is read once per group. With
+    k_scale and v_scale (fp32 [num_kv_heads]) the pools hold e4m3 codes
+    (paged_attn_decode_shared_prefix_fp8) and the query is fp16 or bf16."""
+    f8 = k_scale is not None or v_scale is not None
     _require(query.dim() == 3 and out.shape == query.shape, "query/out must be [S, H, D]")
     _require(key_cache.dim() == 4 and value_cache.shape == key_cache.shape, "pool shape")
-    _require(query.dtype == key_cache.dtype == value_cache.dtype, "query and pools share a dtype")
+    if f8:
+        _require(dtype_code(key_cache.dtype) == PKV_E4M3 and key_cache.dtype == value_cache.dtype,
+                 "e4m3 pools must be uint8 or float8_e4m3fn")
+        _require(query.dtype in (torch.float16, torch.bfloat16), "the query must be fp16 or bf16")
+        _require(k_scale is not None and v_scale is not None and k_scale.dtype == torch.float32
+                 and v_scale.dtype == torch.float32
+                 and k_scale.shape == v_scale.shape == (key_cache.shape[2],),
+                 "k_scale and v_scale must be fp32 [num_kv_heads]")
+    else:
+        _require(query.dtype == key_cache.dtype == value_cache.dtype, "query and pools share a dtype")
     for t in (prefix_block_table, prefix_lens, suffix_block_table, suffix_lens):
         _require(t.dtype == torch.int32, "tables and lengths must be int32")
     S, H, D = query.shape
@@ -293,14 +306,16 @@ def paged_attn_decode_shared_prefix(out: torch.Tensor, query: torch.Tensor,
                                                               int(partition_size)))
         workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=query.device)
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib().paged_attn_decode_shared_prefix(
-        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(prefix_block_table),
+    name = "paged_attn_decode_shared_prefix_fp8" if f8 else "paged_attn_decode_shared_prefix"
+    scales = [_ptr(k_scale), _ptr(v_scale)] if f8 else []
+    st = getattr(lib(), name)(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), *scales, _ptr(prefix_block_table),
         _ptr(prefix_lens), G, group_size, prefix_block_table.shape[1], int(max_prefix_len),
         _ptr(suffix_block_table), _ptr(suffix_lens), suffix_block_table.shape[1],
         int(max_suffix_len), H, Hkv, D, bs, NB, float(scale), dtype_code(query.dtype),
         dtype_code(out.dtype), int(partition_size), _ptr(workspace), ws_bytes,
         _stream(query, stream))
-    check(st, "paged_attn_decode_shared_prefix")
+    check(st, name)
     return out
 
 

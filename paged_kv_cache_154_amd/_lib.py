@@ -44,6 +44,9 @@ SIGNATURES = {
                                                  _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                                  _c_int, _c_float, _c_int, _c_int, _c_int, _c_ptr,
                                                  _c_size, _c_ptr]),
+    "paged_attn_decode_shared_prefix_fp8": (_c_int, [_c_ptr] * 8 + [_c_int] * 4 + [_c_ptr, _c_ptr]
+                                            + [_c_int] * 7 + [_c_float] + [_c_int] * 3
+                                            + [_c_ptr, _c_size, _c_ptr]),
     "paged_attn_shared_prefix_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int,
                                                           _c_int, _c_int, _c_int, _c_int]),
     "paged_attn_partition_tokens": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int]),

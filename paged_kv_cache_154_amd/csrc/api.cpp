@@ -277,33 +277,40 @@ size_t paged_attn_shared_prefix_workspace_size(int num_groups, int group_size, i
       .total();
 }
 
-int paged_attn_decode_shared_prefix(void* out, const void* query, const void* key_cache,
-                                    const void* value_cache, const int32_t* prefix_block_table,
-                                    const int32_t* prefix_lens, int num_groups, int group_size,
-                                    int max_prefix_blocks, int max_prefix_len,
-                                    const int32_t* suffix_block_table, const int32_t* suffix_lens,
-                                    int max_suffix_blocks, int max_suffix_len, int num_heads,
-                                    int num_kv_heads, int head_dim, int block_size, int num_blocks,
-                                    float scale, int kv_dtype, int out_dtype, int partition_size,
-                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared-prefix decode over a 16-bit or fp32 pool (query of the KV dtype, no
+// scales) or an e4m3 pool (k_scale, v_scale; query_dtype fp16 or bf16).
+int shared_prefix(void* out, const void* query, const void* key_cache, const void* value_cache,
+                  const float* k_scale, const float* v_scale, const int32_t* prefix_block_table,
+                  const int32_t* prefix_lens, int num_groups, int group_size, int max_prefix_blocks,
+                  int max_prefix_len, const int32_t* suffix_block_table, const int32_t* suffix_lens,
+                  int max_suffix_blocks, int max_suffix_len, int num_heads, int num_kv_heads,
+                  int head_dim, int block_size, int num_blocks, float scale, int kv_dtype,
+                  int query_dtype, int out_dtype, int partition_size, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
   if (num_groups < 0 || group_size < 1) return PKV_ERR_SHAPE;
   if (num_groups == 0) return PKV_OK;
   if ((int64_t)num_groups * group_size > INT32_MAX / 2) return PKV_ERR_SHAPE;
   if (!out || !query || !key_cache || !value_cache || !prefix_block_table || !prefix_lens ||
       !suffix_block_table || !suffix_lens)
     return PKV_ERR_NULL;
-  if (kv_dtype == PKV_E4M3) return PKV_ERR_UNSUPPORTED;
-  if (out_dtype != kv_dtype && out_dtype != PKV_F32) return PKV_ERR_UNSUPPORTED;
+  if (kv_dtype == PKV_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_NULL;
+  if (kv_dtype == PKV_E4M3 ? (query_dtype != PKV_F16 && query_dtype != PKV_BF16) : query_dtype != kv_dtype)
+    return PKV_ERR_UNSUPPORTED;
+  if (out_dtype != query_dtype && out_dtype != PKV_F32) return PKV_ERR_UNSUPPORTED;
   if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
   if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
   const PrefixLayout l = prefix_layout(num_groups, group_size, num_heads, num_kv_heads, head_dim,
                                        block_size, max_prefix_len, max_suffix_len, partition_size);
   if (l.total() == 0) {
     // the passes' own checks name what is wrong (group too large, sizes, partition)
-    const int st = attention(out, query, key_cache, value_cache, nullptr, nullptr, prefix_block_table,
+    const int st = attention(out, query, key_cache, value_cache, k_scale, v_scale, prefix_block_table,
                              prefix_lens, num_groups, group_size, num_heads, num_kv_heads, head_dim,
                              block_size, num_blocks, max_prefix_blocks, max_prefix_len, scale, kv_dtype,
-                             kv_dtype, PKV_F32, partition_size, nullptr, 0, stream, nullptr, 0);
+                             query_dtype, PKV_F32, partition_size, nullptr, 0, stream, nullptr, 0);
     return st != PKV_OK && st != PKV_ERR_WORKSPACE ? st : PKV_ERR_SHAPE;
   }
   if (!workspace || workspace_bytes < l.total()) return PKV_ERR_WORKSPACE;
@@ -320,29 +327,68 @@ int paged_attn_decode_shared_prefix(void* out, const void* query, const void* ke
   // ([num_seqs, H, D] read as [num_groups, group_size, H, D]), all of them
   // seeing the whole prefix
   pkv::DecodeParams pre{}, suf{};
-  int st = attention(o_pre, query, key_cache, value_cache, nullptr, nullptr, prefix_block_table, prefix_lens,
+  int st = attention(o_pre, query, key_cache, value_cache, k_scale, v_scale, prefix_block_table, prefix_lens,
                      num_groups, group_size, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                     max_prefix_blocks, max_prefix_len, scale, kv_dtype, kv_dtype, PKV_F32, partition_size,
-                     ws_pre, l.pre_bytes, stream, lse_pre, 0, &pre);
+                     max_prefix_blocks, max_prefix_len, scale, kv_dtype, query_dtype, PKV_F32,
+                     partition_size, ws_pre, l.pre_bytes, stream, lse_pre, 0, &pre);
   if (st != PKV_OK) return st;
   // each sample's own suffix
-  st = attention(o_suf, query, key_cache, value_cache, nullptr, nullptr, suffix_block_table, suffix_lens,
+  st = attention(o_suf, query, key_cache, value_cache, k_scale, v_scale, suffix_block_table, suffix_lens,
                  num_seqs, 1, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_suffix_blocks,
-                 max_suffix_len, scale, kv_dtype, kv_dtype, PKV_F32, partition_size, ws_suf, l.suf_bytes,
-                 stream, lse_suf, 1, &suf);
+                 max_suffix_len, scale, kv_dtype, query_dtype, PKV_F32, partition_size, ws_suf,
+                 l.suf_bytes, stream, lse_suf, 1, &suf);
   if (st != PKV_OK) return st;
   // both passes in one launch, the suffixes filling the prefix pass's
-  // ramp-down; one after the other when they do not fit one launch
+  // ramp-down; one after the other when they do not fit one launch (or over
+  // an e4m3 pool, whose suffix pass has its own 4x4x1 instance)
   hipError_t e = pkv::launch_decode_pair(pre, suf, kv_dtype, head_dim, block_size, stream);
   if (e == hipErrorNotSupported) {
     (void)hipGetLastError();
-    e = pkv::launch_decode(pre, kv_dtype, kv_dtype, head_dim, block_size, stream);
-    if (e == hipSuccess) e = pkv::launch_decode(suf, kv_dtype, kv_dtype, head_dim, block_size, stream);
+    e = pkv::launch_decode(pre, kv_dtype, query_dtype, head_dim, block_size, stream);
+    if (e == hipSuccess) e = pkv::launch_decode(suf, kv_dtype, query_dtype, head_dim, block_size, stream);
   }
   if (e != hipSuccess) return PKV_ERR_HIP;
   e = pkv::launch_cascade_merge(out, o_pre, lse_pre, o_suf, lse_suf, (int64_t)num_seqs * num_heads, head_dim,
                                 out_dtype, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode_shared_prefix(void* out, const void* query, const void* key_cache,
+                                    const void* value_cache, const int32_t* prefix_block_table,
+                                    const int32_t* prefix_lens, int num_groups, int group_size,
+                                    int max_prefix_blocks, int max_prefix_len,
+                                    const int32_t* suffix_block_table, const int32_t* suffix_lens,
+                                    int max_suffix_blocks, int max_suffix_len, int num_heads,
+                                    int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                    float scale, int kv_dtype, int out_dtype, int partition_size,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (kv_dtype == PKV_E4M3) return PKV_ERR_UNSUPPORTED;  // needs the scales: the _fp8 entry point
+  return shared_prefix(out, query, key_cache, value_cache, nullptr, nullptr, prefix_block_table, prefix_lens,
+                       num_groups, group_size, max_prefix_blocks, max_prefix_len, suffix_block_table,
+                       suffix_lens, max_suffix_blocks, max_suffix_len, num_heads, num_kv_heads, head_dim,
+                       block_size, num_blocks, scale, kv_dtype, kv_dtype, out_dtype, partition_size,
+                       workspace, workspace_bytes, stream);
+}
+
+int paged_attn_decode_shared_prefix_fp8(void* out, const void* query, const void* key_cache,
+                                        const void* value_cache, const float* k_scale,
+                                        const float* v_scale, const int32_t* prefix_block_table,
+                                        const int32_t* prefix_lens, int num_groups, int group_size,
+                                        int max_prefix_blocks, int max_prefix_len,
+                                        const int32_t* suffix_block_table, const int32_t* suffix_lens,
+                                        int max_suffix_blocks, int max_suffix_len, int num_heads,
+                                        int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                        float scale, int query_dtype, int out_dtype, int partition_size,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return shared_prefix(out, query, key_cache, value_cache, k_scale, v_scale, prefix_block_table, prefix_lens,
+                       num_groups, group_size, max_prefix_blocks, max_prefix_len, suffix_block_table,
+                       suffix_lens, max_suffix_blocks, max_suffix_len, num_heads, num_kv_heads, head_dim,
+                       block_size, num_blocks, scale, PKV_E4M3, query_dtype, out_dtype, partition_size,
+                       workspace, workspace_bytes, stream);
 }
 
 size_t paged_attn_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,

@@ -161,6 +161,30 @@ def test_timed_host_checks(kw, code):
     assert _timed(**kw) == code
 
 
+def _shared_fp8(**kw):
+    a = dict(out=FAKE, query=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, pt=FAKE, pl=FAKE, G=2, n=3,
+             mpb=8, mpl=128, st=FAKE, sl=FAKE, msb=4, msl=64, H=32, Hkv=8, D=128, bs=16, NB=100,
+             scale=0.088, qdt=2, outdt=0, P=0, ws=None, wsb=0)
+    a.update(kw)
+    return _lib.lib().paged_attn_decode_shared_prefix_fp8(
+        a["out"], a["query"], a["k"], a["v"], a["ks"], a["vs"], a["pt"], a["pl"], a["G"], a["n"],
+        a["mpb"], a["mpl"], a["st"], a["sl"], a["msb"], a["msl"], a["H"], a["Hkv"], a["D"], a["bs"],
+        a["NB"], a["scale"], a["qdt"], a["outdt"], a["P"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(G=0, out=None), OK),
+    (dict(ks=None), NULL),
+    (dict(vs=None), NULL),
+    (dict(qdt=0), UNSUP),                      # fp32 query over an e4m3 pool
+    (dict(qdt=1, outdt=2), UNSUP),             # fp16 query, bf16 output
+    (dict(n=0), SHAPE),
+    (dict(), WS),                              # no workspace
+])
+def test_shared_prefix_fp8_host_checks(kw, code):
+    assert _shared_fp8(**kw) == code
+
+
 def test_sixteen_bit_entry_points_refuse_e4m3_pools():
     assert _decode(kvdt=3, outdt=3) == UNSUP
     assert _decode(kvdt=3, outdt=0) == UNSUP

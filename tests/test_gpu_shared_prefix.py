@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import fp8_kv as F
 import paged_kv_cache_154_amd as pkv
 from paged_kv_cache_154_amd import workloads as W
 from gpu_common import DEV, TOL, max_err, say
@@ -146,3 +147,28 @@ def test_shared_prefix_beyond_one_launch_runs_the_passes_in_turn():
                                         int(pl.max()), int(sl.max()))
     torch.cuda.synchronize()
     assert max_err(out, ref, seqs) <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("qdt,G", [(torch.bfloat16, 4), (torch.float16, 2)])
+def test_shared_prefix_fp8_matches_oracle(qdt, G):
+    """e4m3 pools (quantised by the oracle, a scale per KV head): the two
+    passes over the codes and the merge against the oracle's shared-prefix
+    decode over the dequantised pools; both output types."""
+    H, Hkv = 8 * G, 8
+    q, kc, vc, pt, pl, st, sl = _grouped(31 + G, 3, 3, [12, 1, 40], [0, 7, 16, 33, 200, 1, 9, 0, 150],
+                                         H, Hkv, 128, 16, qdt)
+    ks = (kc.float().abs().amax(dim=(0, 1, 3)) / 448.0).clamp_min(1e-6)
+    vs = (vc.float().abs().amax(dim=(0, 1, 3)) / 448.0).clamp_min(1e-6)
+    k8 = F.quantize(kc, ks.numpy().reshape(1, 1, Hkv, 1))
+    v8 = F.quantize(vc, vs.numpy().reshape(1, 1, Hkv, 1))
+    ref = F.decode_shared_prefix_fp8(q, k8, v8, ks.numpy(), vs.numpy(), pt, pl, st, sl, 3, 0.09)
+    d = [torch.from_numpy(x).to(DEV) for x in (pt, pl, st, sl)]
+    k8d, v8d = torch.from_numpy(k8).to(DEV), torch.from_numpy(v8).to(DEV)
+    for out_dt in (qdt, torch.float32):
+        say(f"shared prefix e4m3, query {qdt}, out {out_dt}")
+        out = torch.empty(q.shape, dtype=out_dt, device=DEV)
+        pkv.paged_attn_decode_shared_prefix(out, q.to(DEV), k8d, v8d, *d, 3, 0.09, int(pl.max()),
+                                            int(sl.max()), k_scale=ks.to(DEV), v_scale=vs.to(DEV))
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all()
+        assert max_err(out, ref) <= TOL[qdt], (qdt, out_dt)

@@ -149,6 +149,26 @@ def test_multi_query_fp8_row_is_decode_fp8_of_its_prefix():
         assert np.allclose(out[:, j], ref, rtol=0, atol=1e-12)
 
 
+def test_shared_prefix_fp8_is_decode_fp8_over_the_joined_tables():
+    """Two groups of two samples: each sample's row equals decode over its
+    group's prefix blocks followed by its own, with the same scales."""
+    rng = np.random.default_rng(8)
+    nb, bs, hkv, d, H = 12, 4, 2, 16, 4
+    kq = F.e4m3_encode(rng.standard_normal((nb, bs, hkv, d)).astype(np.float32))
+    vq = F.e4m3_encode(rng.standard_normal((nb, bs, hkv, d)).astype(np.float32))
+    q = torch.from_numpy(rng.standard_normal((4, H, d)).astype(np.float32))
+    ks, vs = np.array([0.5, 1.5], np.float32), np.array([1.25, 0.75], np.float32)
+    pt = np.array([[5, 2], [9, 0]], dtype=np.int32)
+    pl = np.array([8, 4], dtype=np.int32)
+    st = np.array([[1, 3], [7, 0], [11, 0], [6, 10]], dtype=np.int32)
+    sl = np.array([5, 3, 0, 8], dtype=np.int32)
+    out = F.decode_shared_prefix_fp8(q, kq, vq, ks, vs, pt, pl, st, sl, 2, 0.4)
+    joined = np.array([[5, 2, 1, 3], [5, 2, 7, 0], [9, 11, 0, 0], [9, 6, 10, 0]], dtype=np.int32)
+    lens = np.array([13, 11, 4, 12], dtype=np.int32)
+    ref = F.decode_fp8(q, kq, vq, ks, vs, joined, lens, 0.4)
+    assert np.allclose(out, ref, rtol=0, atol=1e-12)
+
+
 def _table_pins_hold(t) -> bool:
     """The landmark and torch checks above, on a given value table."""
     codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
