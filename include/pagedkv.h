@@ -424,7 +424,8 @@ int pagedkv_stream_read(const void* src, size_t bytes, uint32_t* sink, int grid,
  * (hipExtLaunchKernel), so that hipEventElapsedTime(start, stop) is the
  * kernels' own time, without the dispatch latency of separately recorded
  * events. k_scale / v_scale may be NULL for the 16-bit dtypes.
- * Returns PKV_ERR_NULL when an event is NULL.
+ * Returns PKV_ERR_NULL when an event is NULL; with num_seqs = 0 nothing is
+ * launched and the events are left as they are.
  */
 int paged_attn_timed(void* out, const void* query, const void* key_cache, const void* value_cache,
                      const float* k_scale, const float* v_scale, const int32_t* block_table,
