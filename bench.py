@@ -378,7 +378,8 @@ def prefix_share_rows(pkv, W, dev, calls=100, warm=10):
     shared-prefix decode of the same batch (each group's shared blocks read
     once), each call timed cold after a 1 GiB streaming read, medians; GB/s
     on the logical bytes (every sample's whole context) and on the distinct
-    bytes (shared blocks once)."""
+    bytes (shared blocks once). The same two calls over the pools stored as
+    e4m3 codes (quantised once, a scale per KV head; half the bytes)."""
     import torch
     wl = W.make(4)
     kc, vc = wl.key_cache.to(dev), wl.value_cache.to(dev)
@@ -395,14 +396,25 @@ def prefix_share_rows(pkv, W, dev, calls=100, warm=10):
     n = pkv.lib().paged_attn_shared_prefix_workspace_size(128, 3, wl.num_heads, wl.num_kv_heads,
                                                           wl.head_dim, wl.block_size, mp, ms, 0)
     ws2 = torch.empty(n, dtype=torch.uint8, device=dev)
+    NB, bs, Hkv, D = kc.shape
+    ks, vs = fp8_scales(kc), fp8_scales(vc)
+    k8 = torch.empty(kc.shape, dtype=torch.uint8, device=dev)
+    v8 = torch.empty_like(k8)
+    pkv.reshape_and_cache_fp8(kc.view(-1, Hkv, D), vc.view(-1, Hkv, D), k8, v8,
+                              torch.arange(NB * bs, dtype=torch.int64, device=dev), ks, vs)
     fns = {"decode": lambda: pkv.paged_attn_decode(out, q, kc, vc, bt, sl, wl.scale,
                                                    wl.max_seq_len, 0, ws),
            "shared_prefix": lambda: pkv.paged_attn_decode_shared_prefix(
-               out, q, kc, vc, pt, pl, st, sl2, 3, wl.scale, mp, ms, 0, ws2)}
+               out, q, kc, vc, pt, pl, st, sl2, 3, wl.scale, mp, ms, 0, ws2),
+           "decode_e4m3": lambda: pkv.paged_attn_decode_fp8(out, q, k8, v8, ks, vs, bt, sl, wl.scale,
+                                                            wl.max_seq_len, 0, ws),
+           "shared_prefix_e4m3": lambda: pkv.paged_attn_decode_shared_prefix(
+               out, q, k8, v8, pt, pl, st, sl2, 3, wl.scale, mp, ms, 0, ws2, k_scale=ks, v_scale=vs)}
     logical = wl.kv_bytes()
     distinct = layout_stats(wl)["kv_bytes_distinct"]
     res = {"logical_kv_bytes": logical, "distinct_kv_bytes": distinct}
     for name, fn in fns.items():
+        half = 2 if name.endswith("e4m3") else 1   # one byte per element
         for _ in range(warm):
             fn()
         ev = _events(calls)
@@ -420,12 +432,14 @@ def prefix_share_rows(pkv, W, dev, calls=100, warm=10):
         p10, p50, p90 = _pcts(_us(ev))
         res[name] = {"cold_us_p10_p50_p90": [p10, p50, p90],
                      "warm_mean_us": round(w0.elapsed_time(w1) * 1e3 / warm, 2),
-                     "logical_GBps": round(logical / p50 / 1e3, 1),
-                     "distinct_GBps": round(distinct / p50 / 1e3, 1)}
+                     "logical_GBps": round(logical / half / p50 / 1e3, 1),
+                     "distinct_GBps": round(distinct / half / p50 / 1e3, 1)}
         log(f"prefix share, {name}: cold median {p50:.1f} us")
     res["speedup"] = round(res["decode"]["cold_us_p10_p50_p90"][1]
                            / res["shared_prefix"]["cold_us_p10_p50_p90"][1], 3)
-    del kc, vc, fbuf
+    res["speedup_e4m3"] = round(res["decode_e4m3"]["cold_us_p10_p50_p90"][1]
+                                / res["shared_prefix_e4m3"]["cold_us_p10_p50_p90"][1], 3)
+    del kc, vc, k8, v8, fbuf
     torch.cuda.empty_cache()
     return res
 
