@@ -254,7 +254,7 @@ int paged_attn_decode_shared_prefix(void* out, const void* query, const void* ke
  * sharing as above). query and out as for paged_attn_decode_fp8: query of
  * query_dtype PKV_F16 or PKV_BF16, out of the query's type or PKV_F32.
  * k_scale, v_scale: fp32 [num_kv_heads] device arrays (NULL: PKV_ERR_NULL).
- * The two passes run as two launches. Workspace: the size that
+ * Workspace: the size that
  * paged_attn_shared_prefix_workspace_size gives for the same arguments.
  */
 int paged_attn_decode_shared_prefix_fp8(void* out, const void* query, const void* key_cache,

@@ -339,9 +339,8 @@ int shared_prefix(void* out, const void* query, const void* key_cache, const voi
                  l.suf_bytes, stream, lse_suf, 1, &suf);
   if (st != PKV_OK) return st;
   // both passes in one launch, the suffixes filling the prefix pass's
-  // ramp-down; one after the other when they do not fit one launch (or over
-  // an e4m3 pool, whose suffix pass has its own 4x4x1 instance)
-  hipError_t e = pkv::launch_decode_pair(pre, suf, kv_dtype, head_dim, block_size, stream);
+  // ramp-down; one after the other when they do not fit one launch
+  hipError_t e = pkv::launch_decode_pair(pre, suf, kv_dtype, query_dtype, head_dim, block_size, stream);
   if (e == hipErrorNotSupported) {
     (void)hipGetLastError();
     e = pkv::launch_decode(pre, kv_dtype, query_dtype, head_dim, block_size, stream);

@@ -1245,8 +1245,9 @@ __host__ __device__ inline int pair_lds_main(int D, int BS, int kt_bytes, const 
 // the second pass's items from that pass's own counter, so the first pass's
 // ramp-down is filled with the second pass's (short) items instead of
 // ending the launch. Each pass has its own epoch, counter, work list and
-// split-K workspace.
-template <class Tag, int D, int BS>
+// split-K workspace. P4B: the second pass takes the 4x4x1 P.V instance
+// (e4m3 rows of 128 elements, at most 4 query rows per KV head).
+template <class Tag, int D, int BS, bool P4B>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEU<Tag, D>::value)))
 void decode_pair_kernel(DecodeParams p0, DecodeParams p1) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1266,7 +1267,7 @@ void decode_pair_kernel(DecodeParams p0, DecodeParams p1) {
   build_plan(p1, pl1, reinterpret_cast<uint64_t*>(smem));
   int parity = 0;
   run_items<Tag, D, BS, false>(p0, pl0, smem, lds_main, s_next, wave, false, parity);
-  run_items<Tag, D, BS, false>(p1, pl1, smem, lds_main, s_next, wave, true, parity);
+  run_items<Tag, D, BS, P4B>(p1, pl1, smem, lds_main, s_next, wave, true, parity);
 }
 
 // ============================================================================
@@ -1356,8 +1357,8 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream, hipEvent_t start,
 // Two passes in one launch when both fit one launch's work list and LDS
 // budget; hipErrorNotSupported otherwise (the caller then runs them one
 // after the other).
-template <class Tag, int D, int BS>
-hipError_t launch_pair_t(DecodeParams a, DecodeParams b, hipStream_t stream) {
+template <class Tag, int D, int BS, bool P4B>
+hipError_t launch_pair_p(DecodeParams a, DecodeParams b, hipStream_t stream) {
   if (a.num_seqs > kMaxSeqsPerLaunch || b.num_seqs > kMaxSeqsPerLaunch) return hipErrorNotSupported;
   const int kt = TileEngine<Tag, D, BS>::KT_BYTES;
   const size_t lds = (size_t)pair_lds_main(D, BS, kt, a, b) + 2 * kWaves * 16 * 4 + 16 + plan_bytes(a.num_seqs) +
@@ -1365,14 +1366,24 @@ hipError_t launch_pair_t(DecodeParams a, DecodeParams b, hipStream_t stream) {
   if (lds > (size_t)kLdsPerWorkgroup) return hipErrorNotSupported;
   a.epoch = next_launch_epoch();
   b.epoch = next_launch_epoch();
-  const void* kfn = reinterpret_cast<const void*>(&decode_pair_kernel<Tag, D, BS>);
+  const void* kfn = reinterpret_cast<const void*>(&decode_pair_kernel<Tag, D, BS, P4B>);
   const int64_t max_items = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions +
                             (int64_t)b.num_seqs * b.num_kv_heads * b.num_partitions;
   int64_t grid = resident_workgroups(kfn, lds);
   if (grid > max_items) grid = max_items;
   if (grid >= 8) grid = grid / 8 * 8;
-  decode_pair_kernel<Tag, D, BS><<<dim3((unsigned)grid), dim3(kThreads), lds, stream>>>(a, b);
+  decode_pair_kernel<Tag, D, BS, P4B><<<dim3((unsigned)grid), dim3(kThreads), lds, stream>>>(a, b);
   return hipGetLastError();
+}
+
+// The first pass always takes the 16x16x4 P.V instance; the second the
+// 4x4x1 one where the single-pass launch would.
+template <class Tag, int D, int BS>
+hipError_t launch_pair_t(const DecodeParams& a, const DecodeParams& b, hipStream_t stream) {
+  if constexpr (KV<Tag>::kF8 && D == 128) {
+    if (b.q_len * b.group <= 4) return launch_pair_p<Tag, D, BS, true>(a, b, stream);
+  }
+  return launch_pair_p<Tag, D, BS, false>(a, b, stream);
 }
 
 template <class Tag, int D>
@@ -1429,12 +1440,16 @@ hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int query_dtype, i
   }
 }
 
-hipError_t launch_decode_pair(const DecodeParams& a, const DecodeParams& b, int kv_dtype, int head_dim,
-                              int block_size, hipStream_t stream) {
+hipError_t launch_decode_pair(const DecodeParams& a, const DecodeParams& b, int kv_dtype, int query_dtype,
+                              int head_dim, int block_size, hipStream_t stream) {
   switch (kv_dtype) {
     case 0: return launch_pair_d<F32Tag>(a, b, head_dim, block_size, stream);
     case 1: return launch_pair_d<F16Tag>(a, b, head_dim, block_size, stream);
     case 2: return launch_pair_d<BF16Tag>(a, b, head_dim, block_size, stream);
+    case 3:
+      if (query_dtype == 1) return launch_pair_d<E4M3F16Tag>(a, b, head_dim, block_size, stream);
+      if (query_dtype == 2) return launch_pair_d<E4M3BF16Tag>(a, b, head_dim, block_size, stream);
+      return hipErrorNotSupported;
     default: return hipErrorNotSupported;
   }
 }

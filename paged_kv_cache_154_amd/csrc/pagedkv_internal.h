@@ -64,12 +64,12 @@ hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int query_dtype, i
                          int block_size, hipStream_t stream, hipEvent_t start = nullptr,
                          hipEvent_t stop = nullptr);
 
-// Two passes over the same pools (fp32, fp16 or bf16; one query dtype) in one
-// launch, the second's items taken after the first's: a.work and b.work are
-// separate workspaces. hipErrorNotSupported when they do not fit one launch
-// (then nothing is launched).
-hipError_t launch_decode_pair(const DecodeParams& a, const DecodeParams& b, int kv_dtype, int head_dim,
-                              int block_size, hipStream_t stream);
+// Two passes over the same pools (dtypes as for launch_decode) in one launch,
+// the second's items taken after the first's: a.work and b.work are separate
+// workspaces. hipErrorNotSupported when they do not fit one launch (then
+// nothing is launched).
+hipError_t launch_decode_pair(const DecodeParams& a, const DecodeParams& b, int kv_dtype, int query_dtype,
+                              int head_dim, int block_size, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value,
                                         void* key_cache, void* value_cache,
