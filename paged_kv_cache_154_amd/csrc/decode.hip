@@ -923,30 +923,6 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
     return;
   }
 
-  // ---- stage this partition's slice of the block-table row --------------
-  int* s_bt = reinterpret_cast<int*>(smem);
-  const int lb0 = t_begin / BS;
-  const int nlb = (t_end + BS - 1) / BS - lb0;
-  {
-    const int32_t* row = p.block_table + (size_t)seq * p.max_blocks + lb0;
-    for (int i = tid; i < nlb; i += kThreads) {
-      const int b = row[i];
-      s_bt[i] = ((unsigned)b < (unsigned)p.num_blocks) ? b : 0;  // never leave the pool
-    }
-  }
-
-  // Blocks shared with the neighbouring sequences of the batch (samples
-  // forked from one prompt sit next to each other) are read with caching
-  // loads so that the neighbours find them in L2; everything else streams
-  // with non-temporal loads. Only the speed depends on this guess.
-  bool shared = false;
-  {
-    const int32_t* mine = p.block_table + (size_t)seq * p.max_blocks + lb0;
-    const int b0 = mine[0];
-    if (seq > 0) shared |= mine[-p.max_blocks] == b0;
-    if (seq + 1 < p.num_seqs) shared |= mine[p.max_blocks] == b0;
-  }
-
   // Column groups: with more than 16 query rows the rows are cut into tiles
   // of 16 MFMA columns and the waves into as many groups; the waves of group
   // g keep rows 16 g .. 16 g + 15 and share out the key tiles among
@@ -961,9 +937,35 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   eng.init(lane);
   const int myrow = 16 * cgroup + eng.col;
   const bool valid = myrow < R;
+
+  // ---- stage this partition's slice of the block-table row --------------
+  // Every global load of the item's start (the query rows, the slice, the
+  // neighbours' entries of the caching guess below) is issued, unconditional
+  // and in bounds, before any of them is used: the start costs one round
+  // trip to memory instead of one per dependent load.
   eng.load_q(static_cast<const unsigned char*>(p.q) + row_of(valid ? myrow : 0) * Eng::QB, valid);
+  int* s_bt = reinterpret_cast<int*>(smem);
+  const int lb0 = t_begin / BS;
+  const int nlb = (t_end + BS - 1) / BS - lb0;  // >= 1
+  const int32_t* row = p.block_table + (size_t)seq * p.max_blocks + lb0;
+  const int32_t* prev = seq > 0 ? row - p.max_blocks : row;
+  const int32_t* next = seq + 1 < p.num_seqs ? row + p.max_blocks : row;
+  const int e0 = row[tid < nlb ? tid : nlb - 1];
+  const int b0 = row[0];
+  const int bprev = prev[0];
+  const int bnext = next[0];
   eng.lim = valid && p.causal ? L - p.q_len + token_of(myrow) : L - 1;
   eng.reset();
+  if (tid < nlb) s_bt[tid] = ((unsigned)e0 < (unsigned)p.num_blocks) ? e0 : 0;  // never leave the pool
+  for (int i = tid + kThreads; i < nlb; i += kThreads) {
+    const int b = row[i];
+    s_bt[i] = ((unsigned)b < (unsigned)p.num_blocks) ? b : 0;
+  }
+  // Blocks shared with the neighbouring sequences of the batch (samples
+  // forked from one prompt sit next to each other) are read with caching
+  // loads so that the neighbours find them in L2; everything else streams
+  // with non-temporal loads. Only the speed depends on this guess.
+  const bool shared = (seq > 0 && bprev == b0) || (seq + 1 < p.num_seqs && bnext == b0);
   __syncthreads();
 
   unsigned char* kt = smem + bt_lds_bytes(p.partition < p.max_seq_len ? p.partition : p.max_seq_len, BS) +
