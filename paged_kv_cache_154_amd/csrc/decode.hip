@@ -678,12 +678,17 @@ __device__ void build_plan(const DecodeParams& p, Plan& pl, uint64_t* xw) {
   int a_of[kSeqsPerThread], c_of[kSeqsPerThread];
   int na = 0;
   uint64_t cls = 0;
+  // every length this thread needs, loaded before any is used (in bounds:
+  // sequence S-1 stands in for the ones past the end)
+  int len_of[kSeqsPerThread];
+#pragma unroll
+  for (int k = 0; k < kSeqsPerThread; ++k) len_of[k] = p.seq_lens[min(s0 + k, S - 1)];
 #pragma unroll
   for (int k = 0; k < kSeqsPerThread; ++k) {
     a_of[k] = c_of[k] = 0;
     const int s = s0 + k;
     if (k < K && s < S) {
-      const int L = clamp_len(p.seq_lens[s], p.max_seq_len);
+      const int L = clamp_len(len_of[k], p.max_seq_len);
       pl.len[s] = L;
       if (L == 0) {
         c_of[k] = kClasses;
