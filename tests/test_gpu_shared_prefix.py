@@ -149,25 +149,28 @@ def test_shared_prefix_beyond_one_launch_runs_the_passes_in_turn():
     assert max_err(out, ref, seqs) <= TOL[torch.bfloat16]
 
 
-@pytest.mark.parametrize("qdt,G", [(torch.bfloat16, 4), (torch.float16, 2)])
-def test_shared_prefix_fp8_matches_oracle(qdt, G):
+# the second pass's 4x4x1 P.V form (head_dim 128, <= 4 rows per KV head)
+# and the 16x16x4 one (8 rows per KV head; head_dim 64)
+@pytest.mark.parametrize("qdt,G,D", [(torch.bfloat16, 4, 128), (torch.float16, 2, 128),
+                                     (torch.float16, 8, 128), (torch.bfloat16, 4, 64)])
+def test_shared_prefix_fp8_matches_oracle(qdt, G, D):
     """e4m3 pools (quantised by the oracle, a scale per KV head): the two
     passes over the codes and the merge against the oracle's shared-prefix
     decode over the dequantised pools; both output types."""
     H, Hkv = 8 * G, 8
-    q, kc, vc, pt, pl, st, sl = _grouped(31 + G, 3, 3, [12, 1, 40], [0, 7, 16, 33, 200, 1, 9, 0, 150],
-                                         H, Hkv, 128, 16, qdt)
+    q, kc, vc, pt, pl, st, sl = _grouped(31 + G + D, 3, 3, [12, 1, 40], [0, 7, 16, 33, 200, 1, 9, 0, 150],
+                                         H, Hkv, D, 16, qdt)
     ks = (kc.float().abs().amax(dim=(0, 1, 3)) / 448.0).clamp_min(1e-6)
     vs = (vc.float().abs().amax(dim=(0, 1, 3)) / 448.0).clamp_min(1e-6)
     k8 = F.quantize(kc, ks.numpy().reshape(1, 1, Hkv, 1))
     v8 = F.quantize(vc, vs.numpy().reshape(1, 1, Hkv, 1))
-    ref = F.decode_shared_prefix_fp8(q, k8, v8, ks.numpy(), vs.numpy(), pt, pl, st, sl, 3, 0.09)
+    ref = F.decode_shared_prefix_fp8(q, k8, v8, ks.numpy(), vs.numpy(), pt, pl, st, sl, 3, D ** -0.5)
     d = [torch.from_numpy(x).to(DEV) for x in (pt, pl, st, sl)]
     k8d, v8d = torch.from_numpy(k8).to(DEV), torch.from_numpy(v8).to(DEV)
     for out_dt in (qdt, torch.float32):
-        say(f"shared prefix e4m3, query {qdt}, out {out_dt}")
+        say(f"shared prefix e4m3, query {qdt}, G {G}, D {D}, out {out_dt}")
         out = torch.empty(q.shape, dtype=out_dt, device=DEV)
-        pkv.paged_attn_decode_shared_prefix(out, q.to(DEV), k8d, v8d, *d, 3, 0.09, int(pl.max()),
+        pkv.paged_attn_decode_shared_prefix(out, q.to(DEV), k8d, v8d, *d, 3, D ** -0.5, int(pl.max()),
                                             int(sl.max()), k_scale=ks.to(DEV), v_scale=vs.to(DEV))
         torch.cuda.synchronize()
         assert torch.isfinite(out).all()
