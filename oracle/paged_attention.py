@@ -25,8 +25,6 @@ is used below):
 
 from __future__ import annotations
 
-import math
-
 import numpy as np
 import torch
 
@@ -332,7 +330,3 @@ def blocks_needed(num_tokens: int, block_size: int) -> int:
     ([IO] §2.1, BlockTable.num_blocks; [PP] §3, BlockManager.allocate)."""
     return (num_tokens + block_size - 1) // block_size
 
-
-def softmax_scale(head_dim: int) -> float:
-    """The pages' score scale 1/sqrt(head_dim) ([PP] §2.2)."""
-    return 1.0 / math.sqrt(head_dim)
