@@ -11,8 +11,14 @@
  * Conventions for every entry point:
  *   - Every pointer is a DEVICE pointer (memory of the current HIP device),
  *     dense and row-major; no strides. The caller allocates and owns all of
- *     it, including the split-K workspace. The library allocates nothing and
- *     keeps no state between calls; calls are reentrant.
+ *     it, including the workspace. The library allocates nothing, and the
+ *     only host state it keeps is a cache of how many workgroups of each
+ *     kernel fit on a device (a property of the device). Per-call state lives
+ *     in the caller's workspace (see paged_attn_decode): calls with separate
+ *     workspaces are independent and may run concurrently; calls in order on
+ *     one stream may share one. A call may be captured into a HIP graph and
+ *     the graph replayed: every launch leaves its workspace's control area
+ *     as it found it (zero).
  *   - Query, output, key/value rows, pools and the workspace move in 16-byte
  *     vector accesses: those pointers must be 16-byte aligned (every torch
  *     or hipMalloc allocation is), else the call returns PKV_ERR_SHAPE.
@@ -106,14 +112,23 @@ enum pkv_status {
  *                When one partition covers max_seq_len it may hold at most
  *                16384 tokens; a splitting partition likewise.
  *   workspace    device scratch of at least paged_attn_workspace_size(...)
- *                bytes for the same arguments (always needed: its first 256
- *                bytes hold the decode kernel's item counter; the rest holds
- *                the split-K partials and one arrival word per (sequence, KV
- *                head); the counter and the arrival words carry a per-call
- *                tag, so stale contents are recognised). Its contents need
- *                no initialisation and are garbage after. Calls that may run at the same time need
- *                separate workspaces; calls in order on one stream can share
- *                one.
+ *                bytes for the same arguments (always needed). It begins
+ *                with a control area that MUST BE ZERO when the workspace is
+ *                first used: the decode kernel's control word (items taken,
+ *                workgroups finished) and, when sequences are split, one
+ *                arrival count per (sequence, KV head). Every call sets the
+ *                control area back to zero before its last kernel ends, so
+ *                zeroing once (hipMemset after hipMalloc) serves every later
+ *                call, and a call captured into a HIP graph can be replayed
+ *                any number of times. The control area is the first C bytes,
+ *                C = 256 + (split ? roundup(4 * min(num_seqs, 2048) *
+ *                num_kv_heads, 256) : 0); the rest holds the split-K
+ *                partials and may hold anything (it is garbage after a
+ *                call). A nonzero control area is a contract violation: the
+ *                kernels still stay inside the buffers, but items are skipped
+ *                or merged early and the output is unspecified. Calls that
+ *                may run at the same time need separate workspaces; calls in
+ *                order on one stream can share one.
  * Supported: head_dim 64 or 128; block_size 8, 16 or 32; 1 <= G <= 16;
  * num_blocks * block_size < 2^31.
  */
@@ -270,9 +285,15 @@ int paged_attn_decode_shared_prefix_fp8(void* out, const void* query, const void
 
 /*
  * paged_attn_shared_prefix_workspace_size - bytes of workspace that
- * paged_attn_decode_shared_prefix needs (its two passes' fp32 outputs and
- * log-sum-exps, and a workspace for each pass). 0 when the arguments are
- * invalid.
+ * paged_attn_decode_shared_prefix needs: the control areas of its two passes
+ * first, then their fp32 outputs and log-sum-exps and their split-K
+ * partials. As for paged_attn_decode, the control area must be zero before
+ * the workspace's first use and every call leaves it zero again: it is the
+ * first C_pre + C_suf bytes, where C_pre is the control area (as
+ * paged_attn_decode states it) of num_groups sequences of at most
+ * max_prefix_len tokens and C_suf that of num_groups * group_size sequences
+ * of at most max_suffix_len tokens, each split as paged_attn_partition_tokens
+ * gives for its own arguments. 0 when the arguments are invalid.
  */
 size_t paged_attn_shared_prefix_workspace_size(int num_groups, int group_size, int num_heads,
                                                int num_kv_heads, int head_dim, int block_size,
@@ -292,12 +313,13 @@ int paged_attn_partition_tokens(int num_seqs, int num_kv_heads, int block_size,
 
 /*
  * paged_attn_workspace_size - bytes of workspace paged_attn_decode needs for
- * these arguments: a 256-byte header and, when sequences are split, fp32
- * (max, sum) pairs and head_dim weighted-V partial sums per (sequence, head,
- * partition) and a 64-bit arrival word per (sequence, KV head), for
- * min(num_seqs, 2048) sequences (larger batches run as several launches of
- * at most 2048 sequences that reuse them). 0 when the arguments are invalid
- * or num_seqs is 0.
+ * these arguments: the control area (a 256-byte header and, when sequences
+ * are split, a 32-bit arrival count per (sequence, KV head), padded to 256
+ * bytes) and, when split, fp32 (max, sum) pairs and head_dim weighted-V
+ * partial sums per (sequence, head, partition), for min(num_seqs, 2048)
+ * sequences (larger batches run as several launches of at most 2048
+ * sequences that reuse them). 0 when the arguments are invalid or num_seqs
+ * is 0.
  */
 size_t paged_attn_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
                                  int head_dim, int block_size, int max_seq_len,
@@ -397,6 +419,29 @@ int pagedkv_check_decode_inputs(const int32_t* block_table,
                                 int block_size, int num_blocks,
                                 int max_blocks_per_seq, int max_seq_len,
                                 int32_t* counts, hipStream_t stream);
+
+/*
+ * pagedkv_check_cache_op_inputs - the contract check of reshape_and_cache's
+ * slot_mapping and copy_blocks' block_mapping that those calls do not make.
+ * Slots come from the block engine's append_slot, which hands out each slot
+ * once ("LLM inference engine internals" section 2.3), and the scheduler's
+ * blocks_to_copy names fresh destination blocks (the same page, section
+ * 3.1). Counts on the device, into counts (device int32[4], cleared by the
+ * call):
+ *   counts[0]  slots >= num_blocks * block_size (negative slots are
+ *              "no slot" and not counted)
+ *   counts[1]  slots inside the pool that repeat an earlier token's slot
+ *   counts[2]  pairs with a source or destination outside [0, num_blocks)
+ *   counts[3]  pairs (ids in range) whose destination is the source of any
+ *              pair (its own included) or the destination of an earlier pair
+ * Either list may be empty (num_tokens or num_pairs 0, its pointer then may
+ * be NULL). Cost grows with the square of each list's length (it is meant
+ * for checked runs, not the fast path). Asynchronous like the others; read
+ * counts after the stream has finished.
+ */
+int pagedkv_check_cache_op_inputs(const int64_t* slot_mapping, int num_tokens, int block_size,
+                                  int num_blocks, const int64_t* block_mapping, int num_pairs,
+                                  int32_t* counts, hipStream_t stream);
 
 /*
  * pagedkv_stream_read - measurement aid, not part of the decode path: reads

@@ -69,6 +69,25 @@ def _stream(t: torch.Tensor, stream) -> int | None:
     return None
 
 
+def _torch_stream(t: torch.Tensor, stream):
+    """The torch stream a call on ``t`` runs on: ``stream`` (a torch stream or
+    a raw handle) or the current one. Buffers the binding allocates for a
+    call are allocated on it, so the caching allocator does not hand them to
+    other streams while the call's kernels may still use them."""
+    if stream is None:
+        return torch.cuda.current_stream(t.device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(getattr(stream, "cuda_stream", stream)), device=t.device)
+
+
+def _zeroed_on(t: torch.Tensor, stream, nbytes: int) -> torch.Tensor:
+    """A zero-filled uint8 device buffer allocated and cleared on the call's
+    stream (the workspace's control area must be zero at its first use)."""
+    with torch.cuda.stream(_torch_stream(t, stream)):
+        return torch.zeros(nbytes, dtype=torch.uint8, device=t.device)
+
+
 def _require(cond: bool, msg: str) -> None:
     if not cond:
         raise ValueError(msg)
@@ -98,9 +117,12 @@ def paged_attn_multi_query_workspace_size(num_seqs: int, q_len: int, num_heads: 
 
 
 def workspace_for(query: torch.Tensor, key_cache: torch.Tensor, max_seq_len: int,
-                  partition_size: int = 0) -> torch.Tensor | None:
-    """A device buffer big enough for paged_attn_decode (query ``[S, H, D]``)
-    or paged_attn_multi_query (query ``[S, q_len, H, D]``) with these shapes."""
+                  partition_size: int = 0, stream=None) -> torch.Tensor | None:
+    """A zero-filled device buffer big enough for paged_attn_decode (query
+    ``[S, H, D]``) or paged_attn_multi_query (query ``[S, q_len, H, D]``) with
+    these shapes, allocated on the call's stream. Every call leaves the
+    workspace's control area zero again, so one buffer serves any number of
+    later calls in order on that stream (graph replays included)."""
     if query.dim() == 3:
         S, H, D = query.shape
         Q = 1
@@ -110,7 +132,30 @@ def workspace_for(query: torch.Tensor, key_cache: torch.Tensor, max_seq_len: int
     n = paged_attn_multi_query_workspace_size(S, Q, H, Hkv, D, bs, max_seq_len, partition_size)
     if n == 0:
         return None
-    return torch.empty(n, dtype=torch.uint8, device=query.device)
+    return _zeroed_on(query, stream, n)
+
+
+def workspace_control_bytes(num_seqs: int, num_kv_heads: int, head_dim: int, block_size: int,
+                            max_seq_len: int, partition_size: int = 0) -> int:
+    """Bytes at the start of a decode / multi-query workspace that must be
+    zero at its first use (the control area; include/pagedkv.h): 256, plus
+    the arrival counts padded to 256 bytes when sequences are split."""
+    P = paged_attn_partition_tokens(num_seqs, num_kv_heads, block_size, max_seq_len,
+                                    partition_size)
+    if P >= max_seq_len:
+        return 256
+    return 256 + (4 * min(num_seqs, 2048) * num_kv_heads + 255) // 256 * 256
+
+
+def shared_prefix_control_bytes(num_groups: int, group_size: int, num_kv_heads: int,
+                                head_dim: int, block_size: int, max_prefix_len: int,
+                                max_suffix_len: int, partition_size: int = 0) -> int:
+    """Bytes at the start of a shared-prefix workspace that must be zero at its
+    first use: the prefix pass's control area, then the suffix pass's."""
+    return (workspace_control_bytes(num_groups, num_kv_heads, head_dim, block_size,
+                                    max_prefix_len, partition_size)
+            + workspace_control_bytes(num_groups * group_size, num_kv_heads, head_dim, block_size,
+                                      max_suffix_len, partition_size))
 
 
 def _attention(name: str, out, query, key_cache, value_cache, block_table, seq_lens, scale,
@@ -145,7 +190,7 @@ def _attention(name: str, out, query, key_cache, value_cache, block_table, seq_l
     _require(block_table.dim() == 2 and block_table.shape[0] == S and seq_lens.shape == (S,),
              "block_table must be [S, max_blocks] and seq_lens [S]")
     if workspace is None:
-        workspace = workspace_for(query, key_cache, max_seq_len, partition_size)
+        workspace = workspace_for(query, key_cache, max_seq_len, partition_size, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if events is not None:
         # the same attention through paged_attn_timed: the launches set the
@@ -187,9 +232,10 @@ def paged_attn_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.T
     """Decode attention of one query token per sequence over the paged pool.
 
     ``workspace`` must hold ``paged_attn_workspace_size(...)`` bytes (the
-    item counter and split-K partials; no initialisation needed); later calls
-    on the same stream can reuse it. With ``workspace=None`` one is allocated
-    by torch. ``events=(start, stop)`` (torch.cuda.Event(enable_timing=True))
+    control area, zero before the first use and left zero by every call, and
+    the split-K partials); later calls on the same stream can reuse it
+    (``workspace_for`` makes one). With ``workspace=None`` a zeroed one is
+    allocated by torch on the call's stream. ``events=(start, stop)`` (torch.cuda.Event(enable_timing=True))
     runs the same call through paged_attn_timed: the launches themselves set
     the events to the kernels' start and end (a measurement aid)."""
     return _attention("paged_attn_decode", out, query, key_cache, value_cache, block_table,
@@ -205,8 +251,8 @@ def paged_attn_multi_query(out: torch.Tensor, query: torch.Tensor, key_cache: to
     """Causal attention of the last ``q_len`` tokens of each sequence (query
     ``[S, q_len, H, D]``; their K/V already written to the pool): new token j
     sees positions ``0 .. seq_len - q_len + j``. ``q_len * (H / Hkv)`` must be
-    at most 16. Workspace rules as for paged_attn_decode, sized by
-    ``paged_attn_multi_query_workspace_size``."""
+    at most 128 (the query rows of one KV head). Workspace rules as for
+    paged_attn_decode, sized by ``paged_attn_multi_query_workspace_size``."""
     return _attention("paged_attn_multi_query", out, query, key_cache, value_cache,
                       block_table, seq_lens, scale, max_seq_len, partition_size, workspace,
                       stream, events=events)
@@ -304,7 +350,7 @@ def paged_attn_decode_shared_prefix(out: torch.Tensor, query: torch.Tensor,
                                                               int(max_prefix_len),
                                                               int(max_suffix_len),
                                                               int(partition_size)))
-        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=query.device)
+        workspace = _zeroed_on(query, stream, max(n, 256))
     ws_bytes = workspace.numel() * workspace.element_size()
     name = "paged_attn_decode_shared_prefix_fp8" if f8 else "paged_attn_decode_shared_prefix"
     scales = [_ptr(k_scale), _ptr(v_scale)] if f8 else []
@@ -381,15 +427,47 @@ def swap_blocks(src_key_cache: torch.Tensor, src_value_cache: torch.Tensor,
 
 def check_decode_inputs(block_table: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
                         num_blocks: int, max_seq_len: int, stream=None) -> tuple[int, int]:
-    """(bad block-table entries, bad lengths), counted on the device; syncs."""
-    counts = torch.empty(2, dtype=torch.int32, device=block_table.device)
+    """(bad block-table entries, bad lengths), counted on the device; waits
+    for the call's stream."""
+    ts = _torch_stream(block_table, stream)
+    with torch.cuda.stream(ts):
+        counts = torch.empty(2, dtype=torch.int32, device=block_table.device)
     S = block_table.shape[0]
     st = lib().pagedkv_check_decode_inputs(_ptr(block_table), _ptr(seq_lens), S, block_size,
                                            num_blocks, block_table.shape[1], max_seq_len,
-                                           _ptr(counts), _stream(block_table, stream))
+                                           _ptr(counts), ts.cuda_stream)
     check(st, "pagedkv_check_decode_inputs")
+    ts.synchronize()
     c = counts.cpu()
     return int(c[0]), int(c[1])
+
+
+def check_cache_op_inputs(slot_mapping: torch.Tensor | None, block_mapping: torch.Tensor | None,
+                          block_size: int, num_blocks: int,
+                          stream=None) -> tuple[int, int, int, int]:
+    """(slots outside the pool, repeated slots, pairs with an id outside the
+    pool, pairs whose destination is a source or repeats), counted on the
+    device for reshape_and_cache's slot_mapping (int64 [T]) and copy_blocks'
+    block_mapping (int64 [P, 2]); either may be None. Waits for the call's
+    stream."""
+    ref = slot_mapping if slot_mapping is not None else block_mapping
+    _require(ref is not None, "give slot_mapping or block_mapping")
+    if slot_mapping is not None:
+        _require(slot_mapping.dtype == torch.int64 and slot_mapping.dim() == 1,
+                 "slot_mapping must be int64 [T]")
+    if block_mapping is not None:
+        _require(block_mapping.dtype == torch.int64 and block_mapping.dim() == 2
+                 and block_mapping.shape[1] == 2, "block_mapping must be int64 [P, 2]")
+    ts = _torch_stream(ref, stream)
+    with torch.cuda.stream(ts):
+        counts = torch.empty(4, dtype=torch.int32, device=ref.device)
+    T = 0 if slot_mapping is None else slot_mapping.shape[0]
+    P = 0 if block_mapping is None else block_mapping.shape[0]
+    st = lib().pagedkv_check_cache_op_inputs(_ptr(slot_mapping), T, int(block_size), int(num_blocks),
+                                             _ptr(block_mapping), P, _ptr(counts), ts.cuda_stream)
+    check(st, "pagedkv_check_cache_op_inputs")
+    ts.synchronize()
+    return tuple(int(x) for x in counts.cpu())
 
 
 def stream_read(buf: torch.Tensor, sink: torch.Tensor, grid: int, stream=None) -> None:

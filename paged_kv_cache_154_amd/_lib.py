@@ -60,6 +60,8 @@ SIGNATURES = {
                              _c_int, _c_int, _c_int, _c_ptr]),
     "pagedkv_check_decode_inputs": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int,
                                              _c_int, _c_ptr, _c_ptr]),
+    "pagedkv_check_cache_op_inputs": (_c_int, [_c_ptr, _c_int, _c_int, _c_int, _c_ptr, _c_int,
+                                               _c_ptr, _c_ptr]),
     "pagedkv_stream_read": (_c_int, [_c_ptr, _c_size, _c_ptr, _c_int, _c_ptr]),
     "pagedkv_status_string": (ctypes.c_char_p, [_c_int]),
 }

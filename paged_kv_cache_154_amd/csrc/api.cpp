@@ -5,9 +5,6 @@
 #include <math.h>
 #include <stdint.h>
 
-#include <atomic>
-#include <chrono>
-
 #include "pagedkv.h"
 #include "pagedkv_internal.h"
 #include "stream_read.h"
@@ -105,23 +102,32 @@ Cutting cutting_for(int max_seq_len, int block_size, int P) {
   return c;
 }
 
-// Workspace layout: a 256-byte header (the partition kernel's item counter,
-// tagged with the launch's epoch), then, when sequences are split, fp32 O partials
-// [S', q_len, H, NP, D] (the D values of one partial in the kernel's own
-// order), (m, l) pairs [S', q_len, H, NP, 2] and one 64-bit arrival word per
-// (sequence, KV head) [S', Hkv] (also epoch-tagged), for S' = min(S, the
-// sequences of one launch); launches run in order and reuse them.
+// Workspace layout: the control area, then the split-K partials.
+//   * control area (zero before the first use; every call leaves it zero
+//     again): a 256-byte header whose first 64-bit word is the partition
+//     kernel's control word (item counter and finished workgroups), then,
+//     when sequences are split, one 32-bit arrival count per (sequence, KV
+//     head) [S', Hkv], padded to a multiple of 256 bytes;
+//   * partials (any contents; garbage after a call), when split: fp32 O
+//     [S', q_len, H, NP, D] (the D values of one partial in the kernel's own
+//     order) and (m, l) pairs [S', q_len, H, NP, 2];
+// for S' = min(S, the sequences of one launch); launches run in order and
+// reuse them.
 constexpr size_t kHeaderBytes = 256;
 
-size_t split_workspace_bytes(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int np) {
-  if (np <= 1) return 0;
-  const int s = num_seqs < pkv::kMaxSeqsPerLaunch ? num_seqs : pkv::kMaxSeqsPerLaunch;
-  return (size_t)s * num_heads * np * (size_t)(head_dim + 2) * sizeof(float) +
-         (size_t)s * num_kv_heads * sizeof(unsigned long long);
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+int launch_seqs(int num_seqs) { return num_seqs < pkv::kMaxSeqsPerLaunch ? num_seqs : pkv::kMaxSeqsPerLaunch; }
+
+size_t control_bytes_for(int num_seqs, int num_kv_heads, int np) {
+  if (np <= 1) return kHeaderBytes;
+  return kHeaderBytes + round256((size_t)launch_seqs(num_seqs) * num_kv_heads * sizeof(uint32_t));
 }
 
 size_t workspace_bytes_for(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int np) {
-  return kHeaderBytes + split_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, np);
+  const size_t ctl = control_bytes_for(num_seqs, num_kv_heads, np);
+  if (np <= 1) return ctl;
+  return ctl + (size_t)launch_seqs(num_seqs) * num_heads * np * (size_t)(head_dim + 2) * sizeof(float);
 }
 
 }  // namespace
@@ -150,7 +156,7 @@ int attention(void* out, const void* query, const void* key_cache, const void* v
               int max_seq_len, float scale, int kv_dtype, int query_dtype, int out_dtype,
               int partition_size, void* workspace, size_t workspace_bytes, hipStream_t stream,
               float* lse = nullptr, int causal = 1, pkv::DecodeParams* prepared = nullptr,
-              hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
+              hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr, void* partials = nullptr) {
   if (num_seqs < 0 || q_len < 1) return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !query || !key_cache || !value_cache || !block_table || !seq_lens)
@@ -177,12 +183,15 @@ int attention(void* out, const void* query, const void* key_cache, const void* v
   const int np = cut.np;
   // the items of one launch and its item counter (which overshoots by up to
   // the grid) stay in int32
-  const int s_launch = num_seqs < pkv::kMaxSeqsPerLaunch ? num_seqs : pkv::kMaxSeqsPerLaunch;
+  const int s_launch = launch_seqs(num_seqs);
   if ((int64_t)s_launch * num_kv_heads * np > (int64_t)INT32_MAX - (1 << 24)) return PKV_ERR_SHAPE;
-  const size_t need = workspace_bytes_for(num_seqs, q_len * num_heads, num_kv_heads, head_dim, np);
+  // with `partials` (shared-prefix decode) the workspace is the control area
+  // alone and the partials are elsewhere
+  const size_t ctl = control_bytes_for(num_seqs, num_kv_heads, np);
+  const size_t need = partials ? ctl : workspace_bytes_for(num_seqs, q_len * num_heads, num_kv_heads, head_dim, np);
   if (workspace == nullptr || workspace_bytes < need) return PKV_ERR_WORKSPACE;
   if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache) ||
-      !aligned16(workspace))
+      !aligned16(workspace) || (partials && !aligned16(partials)))
     return PKV_ERR_SHAPE;
 
   pkv::DecodeParams p{};
@@ -197,10 +206,10 @@ int attention(void* out, const void* query, const void* key_cache, const void* v
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   p.work = reinterpret_cast<unsigned long long*>(ws);
   if (np > 1) {
-    const int s = num_seqs < pkv::kMaxSeqsPerLaunch ? num_seqs : pkv::kMaxSeqsPerLaunch;
-    p.ws_o = reinterpret_cast<float*>(ws + kHeaderBytes);
+    const int s = launch_seqs(num_seqs);
+    p.arrive = reinterpret_cast<uint32_t*>(ws + kHeaderBytes);
+    p.ws_o = reinterpret_cast<float*>(partials ? static_cast<unsigned char*>(partials) : ws + ctl);
     p.ws_ml = p.ws_o + (size_t)s * q_len * num_heads * np * head_dim;
-    p.arrive = reinterpret_cast<unsigned long long*>(p.ws_ml + (size_t)s * q_len * num_heads * np * 2);
   }
   p.num_seqs = num_seqs;
   p.q_len = q_len;
@@ -225,41 +234,62 @@ int attention(void* out, const void* query, const void* key_cache, const void* v
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
-size_t workspace_size(int num_seqs, int q_len, int num_heads, int num_kv_heads, int head_dim,
-                      int block_size, int max_seq_len, int partition_size) {
-  if (num_seqs <= 0 || q_len < 1 || num_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return 0;
+// Bytes of the control area and of the partials of a decode / multi-query
+// workspace for these arguments; both 0 when the arguments are invalid.
+struct WorkspaceParts {
+  size_t ctl, partials;
+  size_t total() const { return ctl + partials; }
+};
+
+WorkspaceParts workspace_parts(int num_seqs, int q_len, int num_heads, int num_kv_heads, int head_dim,
+                               int block_size, int max_seq_len, int partition_size) {
+  WorkspaceParts w{0, 0};
+  if (num_seqs <= 0 || q_len < 1 || num_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return w;
   if (num_heads % num_kv_heads != 0 || q_len > kMaxQueryRows ||
       q_len * (num_heads / num_kv_heads) > kMaxQueryRows)
-    return 0;
-  if (!supported_head_dim(head_dim)) return 0;
+    return w;
+  if (!supported_head_dim(head_dim)) return w;
   const int P = resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
-  if (P < 0) return 0;
-  return workspace_bytes_for(num_seqs, q_len * num_heads, num_kv_heads, head_dim,
-                             cutting_for(max_seq_len, block_size, P).np);
+  if (P < 0) return w;
+  const int np = cutting_for(max_seq_len, block_size, P).np;
+  w.ctl = control_bytes_for(num_seqs, num_kv_heads, np);
+  w.partials = workspace_bytes_for(num_seqs, q_len * num_heads, num_kv_heads, head_dim, np) - w.ctl;
+  return w;
 }
 
-// Shared-prefix decode: the prefix pass's and the suffix pass's fp32 outputs
-// and lse rows, then the prefix pass's workspace and the suffix pass's (both
-// passes run in one launch), each area 256-byte aligned.
+size_t workspace_size(int num_seqs, int q_len, int num_heads, int num_kv_heads, int head_dim,
+                      int block_size, int max_seq_len, int partition_size) {
+  return workspace_parts(num_seqs, q_len, num_heads, num_kv_heads, head_dim, block_size, max_seq_len,
+                         partition_size)
+      .total();
+}
+
+// Shared-prefix decode workspace: the control areas of the prefix pass and of
+// the suffix pass first (together the area that must be zero at first use),
+// then the two passes' fp32 outputs and lse rows, then the prefix pass's
+// partials and the suffix pass's (both passes run in one launch); every area
+// 256-byte aligned.
 struct PrefixLayout {
-  size_t o_bytes, lse_bytes, pre_bytes, suf_bytes;
-  size_t total() const { return 2 * o_bytes + 2 * lse_bytes + pre_bytes + suf_bytes; }
+  size_t ctl_pre, ctl_suf, o_bytes, lse_bytes, part_pre, part_suf;
+  size_t control() const { return ctl_pre + ctl_suf; }
+  size_t total() const { return control() + 2 * o_bytes + 2 * lse_bytes + part_pre + part_suf; }
 };
-size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 PrefixLayout prefix_layout(int num_groups, int group_size, int num_heads, int num_kv_heads,
                            int head_dim, int block_size, int max_prefix_len, int max_suffix_len,
                            int partition_size) {
-  PrefixLayout l{0, 0, 0, 0};
+  PrefixLayout l{0, 0, 0, 0, 0, 0};
   const int64_t rows = (int64_t)num_groups * group_size * num_heads;
-  const size_t a = workspace_size(num_groups, group_size, num_heads, num_kv_heads, head_dim, block_size,
-                                  max_prefix_len, partition_size);
-  const size_t b = workspace_size(num_groups * group_size, 1, num_heads, num_kv_heads, head_dim, block_size,
-                                  max_suffix_len, partition_size);
-  if (a == 0 || b == 0) return l;
+  const WorkspaceParts a = workspace_parts(num_groups, group_size, num_heads, num_kv_heads, head_dim, block_size,
+                                           max_prefix_len, partition_size);
+  const WorkspaceParts b = workspace_parts(num_groups * group_size, 1, num_heads, num_kv_heads, head_dim,
+                                           block_size, max_suffix_len, partition_size);
+  if (a.ctl == 0 || b.ctl == 0) return l;
+  l.ctl_pre = a.ctl;  // multiples of 256
+  l.ctl_suf = b.ctl;
   l.o_bytes = round256((size_t)rows * head_dim * sizeof(float));
   l.lse_bytes = round256((size_t)rows * sizeof(float));
-  l.pre_bytes = round256(a);
-  l.suf_bytes = b;
+  l.part_pre = round256(a.partials);
+  l.part_suf = b.partials;
   return l;
 }
 
@@ -316,12 +346,15 @@ int shared_prefix(void* out, const void* query, const void* key_cache, const voi
   if (!workspace || workspace_bytes < l.total()) return PKV_ERR_WORKSPACE;
   if (!aligned16(out) || !aligned16(workspace)) return PKV_ERR_SHAPE;
   unsigned char* w = static_cast<unsigned char*>(workspace);
-  float* o_pre = reinterpret_cast<float*>(w);
-  float* o_suf = reinterpret_cast<float*>(w + l.o_bytes);
-  float* lse_pre = reinterpret_cast<float*>(w + 2 * l.o_bytes);
-  float* lse_suf = reinterpret_cast<float*>(w + 2 * l.o_bytes + l.lse_bytes);
-  void* ws_pre = w + 2 * l.o_bytes + 2 * l.lse_bytes;
-  void* ws_suf = static_cast<unsigned char*>(ws_pre) + l.pre_bytes;
+  void* ctl_pre = w;
+  void* ctl_suf = w + l.ctl_pre;
+  unsigned char* o0 = w + l.control();
+  float* o_pre = reinterpret_cast<float*>(o0);
+  float* o_suf = reinterpret_cast<float*>(o0 + l.o_bytes);
+  float* lse_pre = reinterpret_cast<float*>(o0 + 2 * l.o_bytes);
+  float* lse_suf = reinterpret_cast<float*>(o0 + 2 * l.o_bytes + l.lse_bytes);
+  void* part_pre = o0 + 2 * l.o_bytes + 2 * l.lse_bytes;
+  void* part_suf = static_cast<unsigned char*>(part_pre) + l.part_pre;
   const int num_seqs = num_groups * group_size;
   // the prefix once per group: the group's samples are its query rows
   // ([num_seqs, H, D] read as [num_groups, group_size, H, D]), all of them
@@ -330,13 +363,14 @@ int shared_prefix(void* out, const void* query, const void* key_cache, const voi
   int st = attention(o_pre, query, key_cache, value_cache, k_scale, v_scale, prefix_block_table, prefix_lens,
                      num_groups, group_size, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_prefix_blocks, max_prefix_len, scale, kv_dtype, query_dtype, PKV_F32,
-                     partition_size, ws_pre, l.pre_bytes, stream, lse_pre, 0, &pre);
+                     partition_size, ctl_pre, l.ctl_pre, stream, lse_pre, 0, &pre, nullptr, nullptr,
+                     part_pre);
   if (st != PKV_OK) return st;
   // each sample's own suffix
   st = attention(o_suf, query, key_cache, value_cache, k_scale, v_scale, suffix_block_table, suffix_lens,
                  num_seqs, 1, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_suffix_blocks,
-                 max_suffix_len, scale, kv_dtype, query_dtype, PKV_F32, partition_size, ws_suf,
-                 l.suf_bytes, stream, lse_suf, 1, &suf);
+                 max_suffix_len, scale, kv_dtype, query_dtype, PKV_F32, partition_size, ctl_suf,
+                 l.ctl_suf, stream, lse_suf, 1, &suf, nullptr, nullptr, part_suf);
   if (st != PKV_OK) return st;
   // both passes in one launch, the suffixes filling the prefix pass's
   // ramp-down; one after the other when they do not fit one launch
@@ -568,6 +602,18 @@ int pagedkv_check_decode_inputs(const int32_t* block_table, const int32_t* seq_l
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+int pagedkv_check_cache_op_inputs(const int64_t* slot_mapping, int num_tokens, int block_size,
+                                  int num_blocks, const int64_t* block_mapping, int num_pairs,
+                                  int32_t* counts, hipStream_t stream) {
+  if (num_tokens < 0 || num_pairs < 0 || num_blocks <= 0) return PKV_ERR_SHAPE;
+  if (!counts) return PKV_ERR_NULL;
+  if ((num_tokens > 0 && !slot_mapping) || (num_pairs > 0 && !block_mapping)) return PKV_ERR_NULL;
+  if (!supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
+  const hipError_t e = pkv::launch_check_cache_ops(slot_mapping, num_tokens, (int64_t)num_blocks * block_size,
+                                                   block_mapping, num_pairs, num_blocks, counts, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 int pagedkv_stream_read(const void* src, size_t bytes, uint32_t* sink, int grid,
                         hipStream_t stream) {
   if (grid < 0) return PKV_ERR_SHAPE;
@@ -591,20 +637,3 @@ const char* pagedkv_status_string(int status) {
 }
 
 }  // extern "C"
-
-namespace pkv {
-
-// Epochs of decode launches: distinct for every launch of the process and
-// unlikely to match what a workspace header held before (a time-derived
-// start), never 0.
-uint32_t next_launch_epoch() {
-  static std::atomic<uint32_t> counter{(uint32_t)(
-      std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u)};
-  uint32_t e;
-  do {
-    e = counter.fetch_add(1, std::memory_order_relaxed);
-  } while (e == 0);
-  return e;
-}
-
-}  // namespace pkv

@@ -1,6 +1,6 @@
 // KV-pool maintenance kernels for CDNA4 (gfx950): the new-token scatter
 // (reshape_and_cache), the copy-on-write block copy (copy_blocks) and the
-// contract check of decode inputs. All are pure data movement in 16-byte
+// contract checks of decode and cache-operation inputs. All are pure data movement in 16-byte
 // units: one lane moves one 16-byte chunk, so a wave moves 1 KiB per access
 // and consecutive lanes touch consecutive addresses.
 
@@ -181,6 +181,71 @@ __global__ __launch_bounds__(256) void check_decode_inputs_kernel(
   if (threadIdx.x < 2) counts[threadIdx.x] = threadIdx.x == 0 ? s_blk[0] : s_len[0];
 }
 
+// Clears n counters (a kernel rather than a memset, so that a captured
+// graph holds no memset node).
+__global__ __launch_bounds__(64) void zero_counts_kernel(int32_t* counts, int n) {
+  if ((int)threadIdx.x < n) counts[threadIdx.x] = 0;
+}
+
+// Contract check of the cache operations' index arguments. Workgroups
+// [0, slot_groups) take 256 tokens of slot_mapping each, the rest 256 pairs of
+// block_mapping each; every workgroup compares its entries with the others
+// through LDS tiles of 256 and adds what it finds to
+//   counts[0]  slots >= num_slots (negative slots mean "no slot")
+//   counts[1]  slots in the pool equal to the slot of an earlier token
+//              (append_slot hands out each slot once: "LLM inference engine
+//              internals" section 2.3)
+//   counts[2]  pairs with a block id outside [0, num_blocks)
+//   counts[3]  pairs (ids in range) whose destination is some pair's source
+//              or an earlier pair's destination (blocks_to_copy destinations
+//              are fresh blocks: the same page, section 3.1)
+__global__ __launch_bounds__(256) void check_cache_ops_kernel(
+    const int64_t* __restrict__ slots, int num_tokens, int64_t num_slots, const int64_t* __restrict__ pairs,
+    int num_pairs, int num_blocks, int slot_groups, int32_t* __restrict__ counts) {
+  __shared__ int64_t tile[2 * 256];
+  const int t = threadIdx.x;
+  if ((int)blockIdx.x < slot_groups) {
+    const int i = blockIdx.x * 256 + t;
+    const int64_t me = i < num_tokens ? slots[i] : -1;
+    const bool in_pool = me >= 0 && me < num_slots;
+    int dup = 0;
+    const int end = min(num_tokens, (int)(blockIdx.x + 1) * 256);  // tokens before this group's last
+    for (int j0 = 0; j0 < end; j0 += 256) {
+      __syncthreads();
+      tile[t] = j0 + t < num_tokens ? slots[j0 + t] : -1;
+      __syncthreads();
+      if (in_pool && !dup) {
+        const int n = min(256, i - j0);  // earlier tokens only
+        for (int k = 0; k < n; ++k) dup |= tile[k] == me;
+      }
+    }
+    if (me >= num_slots) atomicAdd(counts + 0, 1);
+    if (dup) atomicAdd(counts + 1, 1);
+  } else {
+    const int i = ((int)blockIdx.x - slot_groups) * 256 + t;
+    int64_t src = -1, dst = -1;
+    if (i < num_pairs) {
+      src = pairs[2 * (int64_t)i];
+      dst = pairs[2 * (int64_t)i + 1];
+    }
+    const bool in_range = i < num_pairs && src >= 0 && src < num_blocks && dst >= 0 && dst < num_blocks;
+    int overlap = 0;
+    for (int j0 = 0; j0 < num_pairs; j0 += 256) {
+      __syncthreads();
+      tile[2 * t] = j0 + t < num_pairs ? pairs[2 * (int64_t)(j0 + t)] : -1;
+      tile[2 * t + 1] = j0 + t < num_pairs ? pairs[2 * (int64_t)(j0 + t) + 1] : -1;
+      __syncthreads();
+      if (in_range && !overlap) {
+        const int n = min(256, num_pairs - j0);
+        for (int k = 0; k < n; ++k)
+          overlap |= tile[2 * k] == dst || (j0 + k < i && tile[2 * k + 1] == dst);
+      }
+    }
+    if (i < num_pairs && !in_range) atomicAdd(counts + 2, 1);
+    if (overlap) atomicAdd(counts + 3, 1);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache,
@@ -262,6 +327,20 @@ hipError_t launch_check_decode_inputs(const int32_t* block_table, const int32_t*
                                       int max_seq_len, int32_t* counts, hipStream_t stream) {
   check_decode_inputs_kernel<<<dim3(1), dim3(256), 0, stream>>>(
       block_table, seq_lens, num_seqs, block_size, num_blocks, max_blocks, max_seq_len, counts);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_cache_ops(const int64_t* slot_mapping, int num_tokens, int64_t num_slots,
+                                  const int64_t* block_mapping, int num_pairs, int num_blocks,
+                                  int32_t* counts, hipStream_t stream) {
+  zero_counts_kernel<<<dim3(1), dim3(64), 0, stream>>>(counts, 4);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int slot_groups = (num_tokens + 255) / 256;
+  const int pair_groups = (num_pairs + 255) / 256;
+  if (slot_groups + pair_groups == 0) return hipSuccess;
+  check_cache_ops_kernel<<<dim3(slot_groups + pair_groups), dim3(256), 0, stream>>>(
+      slot_mapping, num_tokens, num_slots, block_mapping, num_pairs, num_blocks, slot_groups, counts);
   return hipGetLastError();
 }
 

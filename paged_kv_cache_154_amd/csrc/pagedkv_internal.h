@@ -15,12 +15,15 @@ struct DecodeParams {
   const void* v;
   const int32_t* block_table;
   const int32_t* seq_lens;
-  unsigned long long* work;  // item counter: (epoch << 32) | items taken
-  uint32_t epoch;            // set per launch: nonzero, distinct within the process
+  // control word of the launch: (workgroups finished << 32) | items taken
+  // from the counter; zero when the launch starts, and set back to zero by
+  // the last workgroup to finish
+  unsigned long long* work;
   float* ws_o;    // [S, q_len, H, NP, D] weighted-V partial sums (split only); the D
                   // values of one partial: the (0, 1) pairs of its quads, then the (2, 3) pairs
   float* ws_ml;   // [S, q_len, H, NP, 2] (running max in log2 units, sum of weights)
-  unsigned long long* arrive;  // [S, Hkv] (epoch << 32) | partitions done (split only)
+  uint32_t* arrive;  // [S, Hkv] partitions done (split only): zero when the launch
+                     // starts, set back to zero by the partition that merges
   const float* k_scale;  // [Hkv] e4m3 pools: value = code * scale (else unused)
   const float* v_scale;  // [Hkv]
   int num_seqs;
@@ -52,9 +55,6 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxPartition = 16384;
 // Sequences per launch of the partition kernel (its schedule lives in LDS).
 constexpr int kMaxSeqsPerLaunch = 2048;
-
-// A fresh epoch for one launch of the decode kernel (see DecodeParams::work).
-uint32_t next_launch_epoch();
 
 // kv_dtype: 0 fp32, 1 fp16, 2 bf16 (the query's type too), 3 e4m3 with a
 // query of type query_dtype (1 fp16 or 2 bf16).
@@ -94,5 +94,9 @@ hipError_t launch_check_decode_inputs(const int32_t* block_table,
                                       int block_size, int num_blocks,
                                       int max_blocks, int max_seq_len,
                                       int32_t* counts, hipStream_t stream);
+
+hipError_t launch_check_cache_ops(const int64_t* slot_mapping, int num_tokens, int64_t num_slots,
+                                  const int64_t* block_mapping, int num_pairs, int num_blocks,
+                                  int32_t* counts, hipStream_t stream);
 
 }  // namespace pkv

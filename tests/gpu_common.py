@@ -47,3 +47,46 @@ def max_err(gpu_out, ref, seqs=None):
 
 def bits(t):
     return t.view({2: torch.int16, 4: torch.int32}[t.element_size()])
+
+
+# The fp32-accumulation bar for fp32 outputs, beside the per-dtype bars
+# above: the kernels accumulate in fp32, and the observed error against the
+# fp64 oracle is ~1e-6 or less; leaving out a single token of a sequence of
+# 8192 tokens moves some output element by far more (test_oracle_sensitivity).
+FP32_BAR = 2e-5
+
+
+def assert_close(out, ref, kv_dtype, seqs=None, label=""):
+    """max-abs error within the bar of the KV (or query) dtype, and, for an
+    fp32 output, within FP32_BAR as well. Returns the error."""
+    err = max_err(out, ref, seqs)
+    n = "all" if seqs is None else len(seqs)
+    say(f"{label} out={out.dtype} max_abs_err={err:.3g} on {n} seqs")
+    assert err <= TOL[kv_dtype], (label, out.dtype, err)
+    if out.dtype == torch.float32:
+        assert err <= FP32_BAR, (label, err)
+    return err
+
+
+def poisoned_workspace(nbytes, ctl_bytes):
+    """A workspace whose control area (the first ctl_bytes, which must be zero
+    at first use) is zero and whose partials are 0xFF bytes (fp32 NaN)."""
+    ws = torch.full((max(int(nbytes), int(ctl_bytes), 256),), 0xFF, dtype=torch.uint8, device=DEV)
+    ws[:ctl_bytes].zero_()
+    return ws
+
+
+def repoison(ws, ctl_bytes, gen=None):
+    """Partials overwritten (0xFF, or random bytes with a generator); the
+    control area is left as the last call left it."""
+    if gen is None:
+        ws[ctl_bytes:].fill_(0xFF)
+    else:
+        ws[ctl_bytes:].copy_(torch.randint(0, 256, (ws.numel() - ctl_bytes,), generator=gen,
+                                           device=DEV, dtype=torch.uint8))
+
+
+def control_is_zero(ws, ctl_bytes):
+    """Every call must leave the workspace's control area zero."""
+    torch.cuda.synchronize()
+    return bool((ws[:ctl_bytes] == 0).all())

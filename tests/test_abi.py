@@ -191,6 +191,18 @@ def test_sixteen_bit_entry_points_refuse_e4m3_pools():
     assert _multi_query(kvdt=3, outdt=0) == UNSUP
 
 
+def _ws_expected(S, rows, Hkv, D, np_):
+    """The documented layout: the control area (a 256-byte header, and when
+    split one 32-bit arrival count per (sequence, KV head) padded to 256
+    bytes), then fp32 (max, sum) + head_dim partial sums per (sequence, query
+    row, partition), for at most 2048 sequences."""
+    s = min(S, 2048)
+    if np_ <= 1:
+        return 256
+    ctl = 256 + (4 * s * Hkv + 255) // 256 * 256
+    return ctl + s * rows * np_ * (D + 2) * 4
+
+
 def test_multi_query_workspace_sizing():
     L = _lib.lib()
     hdr = 256
@@ -199,13 +211,13 @@ def test_multi_query_workspace_sizing():
         S, H, Hkv, D, bs, maxlen, P = args
         assert (L.paged_attn_multi_query_workspace_size(S, 1, H, Hkv, D, bs, maxlen, P)
                 == L.paged_attn_workspace_size(*args))
-    # partials scale with the q_len * num_heads query rows; arrival words do not
+    # partials scale with the q_len * num_heads query rows; arrival counts do not
     assert (L.paged_attn_multi_query_workspace_size(256, 4, 32, 8, 128, 8, 10000, 512)
-            == hdr + 256 * 4 * 32 * 20 * (128 + 2) * 4 + 256 * 8 * 8)
+            == _ws_expected(256, 4 * 32, 8, 128, 20))
     assert L.paged_attn_multi_query_workspace_size(64, 2, 32, 8, 128, 16, 512, 512) == hdr
     assert L.paged_attn_multi_query_workspace_size(64, 33, 32, 8, 128, 16, 4039, 0) == 0
     assert (L.paged_attn_multi_query_workspace_size(64, 8, 32, 8, 128, 16, 4039, 0)
-            == hdr + 64 * 8 * 32 * 4 * 130 * 4 + 64 * 8 * 8)
+            == _ws_expected(64, 8 * 32, 8, 128, 4))
     assert L.paged_attn_multi_query_workspace_size(64, 0, 32, 8, 128, 16, 4039, 0) == 0
 
 
@@ -217,20 +229,37 @@ def test_partition_and_workspace_sizing():
     assert L.paged_attn_partition_tokens(384, 8, 16, 2560, 0) == 2560    # many, short: no split
     assert L.paged_attn_partition_tokens(64, 8, 8, 10000, 512) == 512
     assert L.paged_attn_partition_tokens(64, 8, 32, 100, 48) == SHAPE    # not a multiple of 32
-    # a 256-byte header (the item counter) and, when sequences are split, fp32
-    # (max, sum) + head_dim partial sums per (seq, head, partition) and one
-    # 8-byte arrival word per (seq, KV head), for at most 2048 sequences
-    # (larger batches run as several launches that reuse them)
     hdr = 256
     assert L.paged_attn_workspace_size(64, 32, 8, 128, 16, 512, 512) == hdr   # no split
     n = L.paged_attn_workspace_size(256, 32, 8, 128, 8, 10000, 512)
-    assert n == hdr + 256 * 32 * 20 * (128 + 2) * 4 + 256 * 8 * 8
-    assert L.paged_attn_workspace_size(4, 4, 4, 64, 16, 50, 16) == hdr + 4 * 4 * 4 * 66 * 4 + 4 * 4 * 8
+    assert n == hdr + 256 * 8 * 4 + 256 * 32 * 20 * (128 + 2) * 4
+    assert n == _ws_expected(256, 32, 8, 128, 20)
+    assert L.paged_attn_workspace_size(4, 4, 4, 64, 16, 50, 16) == hdr + 256 + 4 * 4 * 4 * 66 * 4
     assert L.paged_attn_workspace_size(384, 32, 8, 128, 16, 2560, 0) == hdr
-    assert L.paged_attn_workspace_size(64, 32, 8, 128, 16, 4039, 0) == hdr + 64 * 32 * 4 * 130 * 4 + 64 * 8 * 8
+    assert L.paged_attn_workspace_size(64, 32, 8, 128, 16, 4039, 0) == _ws_expected(64, 32, 8, 128, 4)
     assert (L.paged_attn_workspace_size(5000, 8, 8, 64, 16, 4096, 1024)
-            == hdr + 2048 * 8 * 4 * 66 * 4 + 2048 * 8 * 8)
+            == _ws_expected(5000, 8, 8, 64, 4))
     assert L.paged_attn_workspace_size(0, 32, 8, 128, 16, 4039, 0) == 0
+
+
+def test_control_area_sizes_match_the_layout():
+    """The binding's control-area sizes (the part of a workspace that must be
+    zero at first use) follow the documented formula and sit inside the
+    workspace the library asks for."""
+    for S, H, Hkv, D, bs, maxlen, P in [(64, 32, 8, 128, 16, 4039, 0), (256, 32, 8, 128, 8, 10000, 512),
+                                        (384, 32, 8, 128, 16, 2560, 0), (5000, 8, 8, 64, 16, 4096, 1024)]:
+        c = pkv.workspace_control_bytes(S, Hkv, D, bs, maxlen, P)
+        n = pkv.paged_attn_workspace_size(S, H, Hkv, D, bs, maxlen, P)
+        split = pkv.paged_attn_partition_tokens(S, Hkv, bs, maxlen, P) < maxlen
+        assert c == (256 + (4 * min(S, 2048) * Hkv + 255) // 256 * 256 if split else 256)
+        assert c <= n and c % 256 == 0
+    # shared-prefix: both passes' control areas first
+    L = _lib.lib()
+    G_, n_, H, Hkv, D, bs = 128, 3, 32, 8, 128, 16
+    c = pkv.shared_prefix_control_bytes(G_, n_, Hkv, D, bs, 2048, 512, 0)
+    assert c == (pkv.workspace_control_bytes(G_, Hkv, D, bs, 2048, 0)
+                 + pkv.workspace_control_bytes(G_ * n_, Hkv, D, bs, 512, 0))
+    assert c <= L.paged_attn_shared_prefix_workspace_size(G_, n_, H, Hkv, D, bs, 2048, 512, 0)
 
 
 @pytest.mark.parametrize("call,code", [
@@ -268,6 +297,12 @@ def test_partition_and_workspace_sizing():
     (lambda L: L.copy_blocks(ctypes.c_void_p(0x1008), FAKE, FAKE, 3, 10, 16, 8, 128, 2, None), SHAPE),
     (lambda L: L.pagedkv_check_decode_inputs(FAKE, FAKE, 4, 16, 10, 8, 128, None, None), NULL),
     (lambda L: L.pagedkv_check_decode_inputs(FAKE, FAKE, 4, 16, 10, 8, -1, FAKE, None), SHAPE),
+    (lambda L: L.pagedkv_check_cache_op_inputs(FAKE, 4, 16, 10, FAKE, 2, None, None), NULL),
+    (lambda L: L.pagedkv_check_cache_op_inputs(None, 4, 16, 10, FAKE, 2, FAKE, None), NULL),
+    (lambda L: L.pagedkv_check_cache_op_inputs(FAKE, 4, 16, 10, None, 2, FAKE, None), NULL),
+    (lambda L: L.pagedkv_check_cache_op_inputs(FAKE, -1, 16, 10, FAKE, 2, FAKE, None), SHAPE),
+    (lambda L: L.pagedkv_check_cache_op_inputs(FAKE, 4, 16, 0, FAKE, 2, FAKE, None), SHAPE),
+    (lambda L: L.pagedkv_check_cache_op_inputs(FAKE, 4, 12, 10, FAKE, 2, FAKE, None), UNSUP),
     (lambda L: L.pagedkv_stream_read(FAKE, 0, FAKE, 16, None), OK),          # nothing to read
     (lambda L: L.pagedkv_stream_read(None, 1024, FAKE, 16, None), NULL),
     (lambda L: L.pagedkv_stream_read(FAKE, 1000, FAKE, 16, None), SHAPE),   # not a multiple of 16

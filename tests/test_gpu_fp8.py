@@ -13,7 +13,7 @@ import torch
 from oracle import fp8_kv as F
 import paged_kv_cache_154_amd as pkv
 from paged_kv_cache_154_amd import workloads as W
-from gpu_common import DEV, TOL, max_err, say
+from gpu_common import DEV, assert_close, control_is_zero, poisoned_workspace, say
 
 pytestmark = pytest.mark.gpu
 
@@ -152,8 +152,7 @@ def test_fp8_decode_matches_oracle(case):
                                   wl.max_seq_len, P)
         torch.cuda.synchronize()
         assert torch.isfinite(out).all()
-        err = max_err(out, ref)
-        assert err <= TOL[qdt], (name, out_dt, err)
+        assert_close(out, ref, qdt, label=f"fp8 decode {name}")
 
 
 @pytest.mark.parametrize("Q,P", [(4, 0), (8, 64), (3, 16)])
@@ -171,7 +170,7 @@ def test_fp8_multi_query_matches_oracle(Q, P):
                                    torch.from_numpy(wl.seq_lens).to(DEV), wl.scale,
                                    wl.max_seq_len, P)
     torch.cuda.synchronize()
-    assert max_err(out, ref) <= TOL[torch.bfloat16]
+    assert_close(out, ref, torch.bfloat16, label=f"fp8 multi-query q_len={Q} P={P}")
 
 
 def test_fp8_llama3_8b_shaped_step():
@@ -195,15 +194,22 @@ def test_fp8_llama3_8b_shaped_step():
                               ks.to(DEV), vs.to(DEV))
     out32 = torch.empty(wl.query.shape, dtype=torch.float32, device=DEV)
     out16 = torch.empty(wl.query.shape, dtype=torch.bfloat16, device=DEV)
+    P = wl.partition_size
+    n = pkv.paged_attn_workspace_size(wl.num_seqs, wl.num_heads, Hkv, D, bs, wl.max_seq_len, P)
+    c = pkv.workspace_control_bytes(wl.num_seqs, Hkv, D, bs, wl.max_seq_len, P)
     for out in (out32, out16):
+        ws = poisoned_workspace(n, c)
         pkv.paged_attn_decode_fp8(out, wl.query.to(DEV), gk, gv, ks.to(DEV), vs.to(DEV),
                                   torch.from_numpy(wl.block_table).to(DEV),
                                   torch.from_numpy(wl.seq_lens).to(DEV), wl.scale,
-                                  wl.max_seq_len, wl.partition_size)
+                                  wl.max_seq_len, P, workspace=ws)
+        assert control_is_zero(ws, c)
     torch.cuda.synchronize()
 
+    # 16 sequences: the 4 shortest, the 4 longest and 8 more (the oracle's
+    # quantisation of every block of the batch would take minutes)
     order = np.argsort(wl.seq_lens)
-    seqs = sorted(set(order[:3].tolist() + order[-3:].tolist() + [17, 41]))
+    seqs = sorted(set(order[:4].tolist() + order[-4:].tolist() + [3, 11, 17, 25, 33, 41, 49, 57]))
     # the oracle's own pool of the sampled sequences' blocks (compact, remapped)
     blocks = sorted({int(b) for s_ in seqs
                      for b in wl.block_table[s_, :(int(wl.seq_lens[s_]) + bs - 1) // bs]})
@@ -226,6 +232,4 @@ def test_fp8_llama3_8b_shaped_step():
     ref = F.decode_fp8(wl.query, ok, ov, ks.numpy(), vs.numpy(), table, wl.seq_lens, wl.scale,
                        seqs=seqs)
     for out in (out32, out16):
-        err = max_err(out, ref, seqs)
-        say(f"  out={out.dtype} max_abs_err={err:.3g} on {len(seqs)} seqs")
-        assert err <= TOL[torch.bfloat16]
+        assert_close(out, ref, torch.bfloat16, seqs, label="fp8 Llama-3-8B step")
