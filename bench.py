@@ -1,35 +1,40 @@
 """Benchmark of the paged decode hot path on one MI355X.
 
-One step = one layer's decode step of the Llama-3-8B-shaped batch (64
-sequences, 32 query / 8 KV heads, head_dim 128, bf16, block_size 16, lengths
-uniform in [512, 4096], 20000-block pool): reshape_and_cache of the 64 new
-tokens, then paged_attn_decode over all cached tokens. Steps rotate over
-``--layers`` copies of the layer's pools (same shapes and tables), so that a
-step never finds its K/V in the 256 MB Infinity Cache or the L2 from the
-previous use of the same pool.
+One step = one layer's decode step of the Llama-2-70B-shaped batch (256
+sequences, 64 query / 8 KV heads, head_dim 128, fp16 KV, block_size 32,
+lengths lognormal with median 1024 clipped to [32, 8192], blocks placed at
+random in a pool of 1.2x the blocks needed): paged_attn_decode over all
+cached tokens. Steps rotate over ``--layers`` copies of the layer's pools
+(same shapes and tables), so that a step never finds its K/V in the 256 MB
+Infinity Cache or the L2 from the previous use of the same pool.
 
 Prints one JSON line. ``value`` is KV GB/s: the algorithmic KV bytes a step
 must read (every cached token's K and V rows, once) over the measured step
 time. The roofline entry is for the decode call (one kernel: the split
-sequences are merged by their last partition), timed with HIP events on the
-stream the library launches on.
+sequences are merged by their last partition), its duration the kernel's own
+start-to-end time from events its launch sets, on the stream the library
+launches on. The same measurement of the Llama-3-8B-shaped step (64
+sequences, 32 / 8 heads, bf16, block_size 16, lengths uniform in [512, 4096]:
+reshape_and_cache of the 64 new tokens, then decode) rides along under the
+key ``llama3_8b_bf16``; ``--workload llama3_8b_bf16`` makes it the headline.
 
 The line also carries the streaming-read rate the same GPU reaches (the
 library's stream-read kernel over a 4 GiB buffer, best of a few grid sizes)
 and the decode call's share of it, and p10/p50/p90 of the decode call.
 ``--secondary`` adds the measurements the pages give context for: a
-block-size sweep (8, 16, 32) of the same lengths and paged vs contiguous
-placement of the same blocks. ``--per-config`` adds every page-shaped
-workload (the Llama-3-8B and Llama-2-70B layers, the prefix-sharing batch
-and the mixed batch with split sequences): decode calls timed cold, with
-p10/p50/p90, and the scatter and block copy of each step.
+block-size sweep (8, 16, 32) of the Llama-3-8B lengths and paged vs
+contiguous placement of the same blocks. ``--per-config`` adds every
+page-shaped workload (the Llama-3-8B and Llama-2-70B layers, the
+prefix-sharing batch and the mixed batch with split sequences): decode calls
+timed cold, with p10/p50/p90, and the scatter and block copy of each step.
 ``--multi-query`` adds the verification pass of speculative decoding (q_len
-2, 4 and 8 new tokens per sequence, causal) on the same lengths, beside decode;
-``--q-len Q`` makes that pass, with its scatter of 64 x Q tokens, the timed
-step itself (the profile of it then covers that pass alone).
+2, 4 and 8 new tokens per sequence, causal) on the Llama-3-8B lengths, beside
+decode; ``--q-len Q`` makes that pass, with its scatter of 64 x Q tokens, the
+timed step itself (on the Llama-3-8B batch; the profile of it then covers
+that pass alone). ``--kv-fp8`` times the e4m3 step of the Llama-3-8B batch.
 
-    python bench.py [--steps K] [--warmup W] [--layers N] [--no-cpu-baseline] [--secondary]
-                    [--per-config] [--multi-query] [--q-len Q]
+    python bench.py [--steps K] [--warmup W] [--layers N] [--workload W] [--no-cpu-baseline]
+                    [--secondary] [--per-config] [--multi-query] [--q-len Q] [--kv-fp8]
 """
 
 import argparse
@@ -46,6 +51,19 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
 METRIC = "paged decode attention: KV GB/s and % of HBM peak; sequences/s per layer"
+
+# headline-able workloads: name -> (config number, description, lengths)
+WORKLOADS = {
+    "llama2_70b_fp16": (3, "Llama-2-70B-shaped single-layer decode",
+                        "lognormal, median 1024, sigma 1.0, clipped to [32, 8192], seed 1543"),
+    "llama3_8b_bf16": (2, "Llama-3-8B-shaped single-layer decode", "uniform [512, 4096], seed 1542"),
+    "prefix_share_bf16": (4, "parallel-sampling batch, 128 prompts x 3 samples sharing a "
+                             "2048-token prefix, plain decode of every sample",
+                          "2048 + uniform [0, 512], seed 1544"),
+    "mixed_splitk_bf16": (5, "mixed batch, 16 x 10000 + 240 x uniform [50, 2000] tokens, "
+                             "block_size 8, 512-token partitions",
+                          "16 x 10000 + 240 x uniform [50, 2000], shuffled, seed 1545"),
+}
 
 
 def kernel_source_hash():
@@ -395,7 +413,7 @@ def prefix_share_rows(pkv, W, dev, calls=100, warm=10):
     mp, ms = int(pl.max()), int(sl2.max())
     n = pkv.lib().paged_attn_shared_prefix_workspace_size(128, 3, wl.num_heads, wl.num_kv_heads,
                                                           wl.head_dim, wl.block_size, mp, ms, 0)
-    ws2 = torch.empty(n, dtype=torch.uint8, device=dev)
+    ws2 = torch.zeros(n, dtype=torch.uint8, device=dev)   # control areas zero at first use
     NB, bs, Hkv, D = kc.shape
     ks, vs = fp8_scales(kc), fp8_scales(vc)
     k8 = torch.empty(kc.shape, dtype=torch.uint8, device=dev)
@@ -488,31 +506,227 @@ def cpu_baseline_fp8(wl, ks, vs, n_seqs=8, budget_s=20.0):
             "seconds_per_step": round(t, 3)}
 
 
-def cpu_baseline(wl, budget_s=20.0):
-    """The CPU oracle on the same step (scatter + attention of every sequence),
-    wall clock, median over repeats within about budget_s seconds."""
-    import torch
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
+
+def _oracle_step(wl):
     import oracle
+    kc, vc = wl.key_cache, wl.value_cache
+    if wl.slot_mapping is not None:
+        kc, vc = oracle.reshape_and_cache(wl.new_key, wl.new_value, kc, vc, wl.slot_mapping)
+    if wl.q_len == 1:
+        oracle.decode(wl.query, kc, vc, wl.block_table, wl.seq_lens, wl.scale)
+    else:
+        oracle.multi_query(wl.query, kc, vc, wl.block_table, wl.seq_lens, wl.scale)
+
+
+def cpu_baseline(wl, budget_s=20.0):
+    """The CPU oracle on the same step (the scatter of the new tokens, when
+    the step has them, and attention of every sequence), wall clock, median
+    over up to 3 repeats within about budget_s seconds, on every host thread
+    torch and NumPy use."""
+    import torch
     times = []
     while len(times) < 3 and sum(times) < budget_s:
         t0 = time.perf_counter()
-        kc, vc = oracle.reshape_and_cache(wl.new_key, wl.new_value, wl.key_cache,
-                                          wl.value_cache, wl.slot_mapping)
-        if wl.q_len == 1:
-            oracle.decode(wl.query, kc, vc, wl.block_table, wl.seq_lens, wl.scale)
-        else:
-            oracle.multi_query(wl.query, kc, vc, wl.block_table, wl.seq_lens, wl.scale)
+        _oracle_step(wl)
         times.append(time.perf_counter() - t0)
         log(f"cpu oracle step {len(times)}: {times[-1]:.2f} s")
     t = statistics.median(times)
+    what = "decode" if wl.q_len == 1 else f"multi-query, q_len {wl.q_len}"
+    scat = "oracle scatter of the new tokens + " if wl.slot_mapping is not None else ""
     return {"value": round(wl.kv_bytes() / t / 1e9, 4), "unit": "GB/s",
             "cores": torch.get_num_threads(), "kind": "oracle",
             "sample": (f"the whole step of the same workload ({wl.num_seqs} sequences, "
-                       f"{wl.num_tokens} tokens: oracle scatter of the new tokens + fp64 "
-                       f"{'decode' if wl.q_len == 1 else f'multi-query, q_len {wl.q_len}'}), median of {len(times)} run(s), {t:.2f} s per step"),
+                       f"{wl.num_tokens} tokens: {scat}fp64 {what}), median of {len(times)} "
+                       f"run(s), {t:.2f} s per step"),
+            "cpu_model": cpu_model(),
             "seconds_per_step": round(t, 3),
             "seqs_per_s": round(wl.num_seqs / t, 3)}
+
+
+def cpu_baseline_one_thread(wl, budget_s=15.0):
+    """The same oracle step on one host thread (NumPy's BLAS and torch both
+    limited to one), wall clock, median over up to 3 repeats within about
+    budget_s seconds."""
+    import torch
+    from threadpoolctl import threadpool_limits
+    prev = torch.get_num_threads()
+    times = []
+    try:
+        torch.set_num_threads(1)
+        with threadpool_limits(limits=1):
+            while len(times) < 3 and sum(times) < budget_s:
+                t0 = time.perf_counter()
+                _oracle_step(wl)
+                times.append(time.perf_counter() - t0)
+                log(f"cpu oracle, 1 thread, {wl.name} step {len(times)}: {times[-1]:.2f} s")
+    finally:
+        torch.set_num_threads(prev)
+    t = statistics.median(times)
+    return {"workload": wl.name, "value": round(wl.kv_bytes() / t / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "seconds_per_step": round(t, 3), "runs": len(times),
+            "seqs_per_s": round(wl.num_seqs / t, 3)}
+
+
+def time_step(pkv, wl, dev, args, Q=1, fp8=False, P=None, layers_n=4):
+    """The timed steps of one workload and their instrumented repeats.
+
+    K steps with one event pair around them (events inside the steps would
+    add their own dispatch latency to every step); then the same K steps
+    with the attention call's own kernel start and end (events its launch
+    sets, paged_attn_timed) and events recorded around the call; then K
+    attention calls back to back. Returns the measurements (ms) and the
+    workload's facts."""
+    import torch
+    S, H, D = wl.num_seqs, wl.num_heads, wl.head_dim
+    NB, bs, Hkv, _ = wl.key_cache.shape
+    P = wl.partition_size if P is None else P
+    attn = pkv.paged_attn_decode if Q == 1 else pkv.paged_attn_multi_query
+    attn_name = "paged_attn_decode" if Q == 1 else f"paged_attn_multi_query (q_len {Q})"
+    q = wl.query.to(dev)
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    sl = torch.from_numpy(wl.seq_lens).to(dev)
+    has_new = wl.slot_mapping is not None
+    if has_new:
+        nk, nv = wl.new_key.to(dev), wl.new_value.to(dev)
+        slots = torch.from_numpy(wl.slot_mapping).to(dev)
+    kc0, vc0 = wl.key_cache.to(dev), wl.value_cache.to(dev)
+    if wl.block_mapping is not None:
+        # the copy-on-write of the fork (prefix-sharing batch), once, before
+        # the steps: the copies' contents are what the remapped tables read
+        pkv.copy_blocks(kc0, vc0, torch.from_numpy(wl.block_mapping).to(dev))
+    ks = vs = None
+    if fp8:
+        # setup, not timed: a scale per KV head (largest magnitude / 448, the
+        # caller's calibration) and every slot of the pools quantised
+        ks, vs = fp8_scales(kc0), fp8_scales(vc0)
+        k8 = torch.empty(kc0.shape, dtype=torch.uint8, device=dev)
+        v8 = torch.empty_like(k8)
+        pkv.reshape_and_cache_fp8(kc0.view(-1, Hkv, D), vc0.view(-1, Hkv, D), k8, v8,
+                                  torch.arange(NB * bs, dtype=torch.int64, device=dev), ks, vs)
+        del kc0, vc0
+        kc0, vc0 = k8, v8
+        attn_f8 = pkv.paged_attn_decode_fp8 if Q == 1 else pkv.paged_attn_multi_query_fp8
+        attn_name = attn_name.replace("paged_attn_decode", "paged_attn_decode_fp8").replace(
+            "paged_attn_multi_query", "paged_attn_multi_query_fp8")
+
+        def scatter(kc, vc):
+            pkv.reshape_and_cache_fp8(nk, nv, kc, vc, slots, ks, vs)
+
+        def attend(kc, vc, events=None):
+            attn_f8(out, q, kc, vc, ks, vs, bt, sl, wl.scale, wl.max_seq_len, P, ws, events=events)
+    else:
+        def scatter(kc, vc):
+            pkv.reshape_and_cache(nk, nv, kc, vc, slots)
+
+        def attend(kc, vc, events=None):
+            attn(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws, events=events)
+    layers = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(layers_n - 1)]
+    out = torch.empty(wl.query.shape, dtype=wl.dtype, device=dev)
+    ws = pkv.workspace_for(q, kc0, wl.max_seq_len, P)
+    part_tokens = pkv.paged_attn_partition_tokens(S, Hkv, bs, wl.max_seq_len, P)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        kc, vc = layers[i % len(layers)]
+        if has_new:
+            scatter(kc, vc)
+        attend(kc, vc)
+
+    log(f"{wl.name}: warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_stop) / args.steps
+    log(f"{wl.name}: {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f})")
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in kev:   # HIP creates an event on its first record
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        kc, vc = layers[i % len(layers)]
+        if has_new:
+            scatter(kc, vc)
+        ev[i][0].record(stream)
+        attend(kc, vc, kev[i])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    dec_ms = [a.elapsed_time(b) for a, b in ev]
+    ker_ms = [a.elapsed_time(b) for a, b in kev]
+    ker_avg = sum(ker_ms) / len(ker_ms)
+    log(f"{wl.name}: attention kernel avg {ker_avg * 1e3:.1f} us (median "
+        f"{statistics.median(ker_ms) * 1e3:.1f}); with events around the call "
+        f"{sum(dec_ms) / len(dec_ms) * 1e3:.1f} us")
+
+    for i in range(args.warmup):
+        kc, vc = layers[i % len(layers)]
+        attend(kc, vc)
+    b0 = torch.cuda.Event(enable_timing=True)
+    b1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    b0.record(stream)
+    for i in range(args.steps):
+        kc, vc = layers[i % len(layers)]
+        attend(kc, vc)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    dec_bb = b0.elapsed_time(b1) / args.steps
+    log(f"{wl.name}: attention back to back: {dec_bb * 1e3:.1f} us per call")
+    del layers, out, ws
+    torch.cuda.empty_cache()
+    kv = wl.kv_bytes() // (2 if fp8 else 1)      # e4m3: one byte per element
+    return {"ms_step": ms_step, "dec_ms": dec_ms, "ker_ms": ker_ms, "ker_avg": ker_avg,
+            "dec_bb": dec_bb, "kv": kv, "attn_name": attn_name, "part_tokens": part_tokens,
+            "layers": layers_n, "scales": (ks, vs), "new_tokens": S * Q if has_new else 0}
+
+
+def _pct3(xs):
+    q = statistics.quantiles(xs, n=10) if len(xs) >= 2 else xs * 9
+    return [round(q[0] * 1e3, 2), round(statistics.median(xs) * 1e3, 2), round(q[-1] * 1e3, 2)]
+
+
+def step_summary(wl, m):
+    """The per-workload figures of one time_step result."""
+    kv = m["kv"]
+    achieved = kv / (m["ker_avg"] * 1e-3) / 1e9
+    return {
+        "kv_GBps": round(kv / (m["ms_step"] * 1e-3) / 1e9, 2),
+        "ms_per_step": round(m["ms_step"], 5),
+        "pct_hbm_peak": round(100 * kv / (m["ms_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "seqs_per_s_per_layer": round(wl.num_seqs / (m["ms_step"] * 1e-3), 1),
+        "decode_us": round(sum(m["dec_ms"]) / len(m["dec_ms"]) * 1e3, 2),
+        "decode_us_p10_p50_p90": _pct3(m["dec_ms"]),
+        "decode_kernel_us": round(m["ker_avg"] * 1e3, 2),
+        "decode_kernel_us_p10_p50_p90": _pct3(m["ker_ms"]),
+        "decode_us_back_to_back": round(m["dec_bb"] * 1e3, 2),
+        "kv_GBps_back_to_back": round(kv / (m["dec_bb"] * 1e-3) / 1e9, 1),
+        "kernel_frac_of_hbm_peak": round(achieved / HBM_PEAK_GBS, 4),
+        "achieved_GBps": round(achieved, 2),
+    }
 
 
 def main():
@@ -521,10 +735,16 @@ def main():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--workload", choices=list(WORKLOADS), default=None,
+                    help="the headline workload (default: the Llama-2-70B-shaped layer; the "
+                         "Llama-3-8B one for --q-len > 1 and --kv-fp8); the prefix-sharing and "
+                         "mixed batches time their decode calls (for profiles)")
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-peak", action="store_true",
                     help="skip measuring the streaming-read rate")
+    ap.add_argument("--no-second-workload", action="store_true",
+                    help="time the headline workload only")
     ap.add_argument("--secondary", action="store_true",
                     help="add the block-size sweep and the placement comparison")
     ap.add_argument("--q-len", type=int, default=1,
@@ -567,198 +787,113 @@ def main():
         torch.cuda.synchronize()
         log("copied 1 GiB x 10")
         return
-    log("generating workload (Llama-3-8B-shaped layer)")
     Q = args.q_len
-    wl = W.llama3_8b(q_len=Q)
-    P = wl.partition_size if args.partition_size is None else args.partition_size
-    S, H, D = wl.num_seqs, wl.num_heads, wl.head_dim
-    attn = pkv.paged_attn_decode if Q == 1 else pkv.paged_attn_multi_query
-    attn_name = "paged_attn_decode" if Q == 1 else f"paged_attn_multi_query (q_len {Q})"
-    NB, bs, Hkv, _ = wl.key_cache.shape
-
-    q = wl.query.to(dev)
-    bt = torch.from_numpy(wl.block_table).to(dev)
-    sl = torch.from_numpy(wl.seq_lens).to(dev)
-    nk, nv = wl.new_key.to(dev), wl.new_value.to(dev)
-    slots = torch.from_numpy(wl.slot_mapping).to(dev)
-    kc0, vc0 = wl.key_cache.to(dev), wl.value_cache.to(dev)
     fp8 = args.kv_fp8
-    if fp8:
-        # setup, not timed: a scale per KV head (largest magnitude / 448, the
-        # caller's calibration) and every slot of the pools quantised
-        ks, vs = fp8_scales(kc0), fp8_scales(vc0)
-        k8 = torch.empty(kc0.shape, dtype=torch.uint8, device=dev)
-        v8 = torch.empty_like(k8)
-        D_ = wl.head_dim
-        pkv.reshape_and_cache_fp8(kc0.view(-1, Hkv, D_), vc0.view(-1, Hkv, D_), k8, v8,
-                                  torch.arange(NB * bs, dtype=torch.int64, device=dev), ks, vs)
-        del kc0, vc0
-        kc0, vc0 = k8, v8
-        attn_f8 = pkv.paged_attn_decode_fp8 if Q == 1 else pkv.paged_attn_multi_query_fp8
-        attn_name = attn_name.replace("paged_attn_decode", "paged_attn_decode_fp8").replace(
-            "paged_attn_multi_query", "paged_attn_multi_query_fp8")
-
-        def scatter(kc, vc):
-            pkv.reshape_and_cache_fp8(nk, nv, kc, vc, slots, ks, vs)
-
-        def attend(kc, vc, events=None):
-            attn_f8(out, q, kc, vc, ks, vs, bt, sl, wl.scale, wl.max_seq_len, P, ws, events=events)
+    name = args.workload or ("llama3_8b_bf16" if (Q > 1 or fp8) else "llama2_70b_fp16")
+    if name != "llama3_8b_bf16" and (Q > 1 or fp8):
+        ap.error("--q-len > 1 and --kv-fp8 run on the Llama-3-8B-shaped batch")
+    log(f"generating workload {name}")
+    wl = W.llama3_8b(q_len=Q) if name == "llama3_8b_bf16" else W.make(WORKLOADS[name][0])
+    m = time_step(pkv, wl, dev, args, Q=Q, fp8=fp8, P=args.partition_size, layers_n=args.layers)
+    S, H, D = wl.num_seqs, wl.num_heads, wl.head_dim
+    NB, bs, Hkv, _ = wl.key_cache.shape
+    summ = step_summary(wl, m)
+    kv = m["kv"]
+    achieved = summ["achieved_GBps"]
+    if name != "llama3_8b_bf16":
+        workload = f"{name}: {WORKLOADS[name][1]}"
+        lens = WORKLOADS[name][2]
+        step_desc = "paged_attn_decode"
+        if wl.block_mapping is not None:
+            step_desc += " (after the fork's copy_blocks, done once before the steps)"
+        profile = f"decode_{name}"
     else:
-        def scatter(kc, vc):
-            pkv.reshape_and_cache(nk, nv, kc, vc, slots)
-
-        def attend(kc, vc, events=None):
-            attn(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws, events=events)
-    layers = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(args.layers - 1)]
-    out = torch.empty(wl.query.shape, dtype=wl.dtype, device=dev)
-    ws = pkv.workspace_for(q, kc0, wl.max_seq_len, P)
-    part_tokens = pkv.paged_attn_partition_tokens(S, Hkv, bs, wl.max_seq_len, P)
-    stream = torch.cuda.current_stream(dev)
-
-    def step(i):
-        kc, vc = layers[i % len(layers)]
-        scatter(kc, vc)
-        attend(kc, vc)
-
-    log(f"warmup {args.warmup} steps")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # timed region: K whole steps with one event pair around them (events
-    # inside the steps would add their own dispatch latency to every step)
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t_stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = t_start.elapsed_time(t_stop) / args.steps
-    log(f"{args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f})")
-
-    # The same K steps again, instrumented: the decode kernel's own start and
-    # end, set by its launch (hipExtLaunchKernel events through
-    # paged_attn_timed), which give the roofline's duration, and events
-    # recorded on the stream around each decode call (which add their own
-    # dispatch latency).
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for a, b in kev:   # HIP creates an event on its first record
-        a.record(stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        kc, vc = layers[i % len(layers)]
-        scatter(kc, vc)
-        ev[i][0].record(stream)
-        attend(kc, vc, kev[i])
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    dec_ms = [a.elapsed_time(b) for a, b in ev]
-    dec_avg = sum(dec_ms) / len(dec_ms)
-    dec_q = statistics.quantiles(dec_ms, n=10) if len(dec_ms) >= 2 else dec_ms * 9
-    ker_ms = [a.elapsed_time(b) for a, b in kev]
-    ker_avg = sum(ker_ms) / len(ker_ms)
-    ker_q = statistics.quantiles(ker_ms, n=10) if len(ker_ms) >= 2 else ker_ms * 9
-    log(f"decode kernel avg {ker_avg * 1e3:.1f} us (median {statistics.median(ker_ms) * 1e3:.1f}); "
-        f"with events around the call {dec_avg * 1e3:.1f} us")
-
-    # The same decode calls back to back (no scatter between them, one event
-    # pair around all): the per-call event pairs above add their own marker
-    # and dispatch latency to each call; this is closer to the kernel time.
-    for i in range(args.warmup):
-        kc, vc = layers[i % len(layers)]
-        attend(kc, vc)
-    b0 = torch.cuda.Event(enable_timing=True)
-    b1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    b0.record(stream)
-    for i in range(args.steps):
-        kc, vc = layers[i % len(layers)]
-        attend(kc, vc)
-    b1.record(stream)
-    torch.cuda.synchronize()
-    dec_bb = b0.elapsed_time(b1) / args.steps
-    log(f"decode back to back: {dec_bb * 1e3:.1f} us per call")
-
-    kv = wl.kv_bytes() // (2 if fp8 else 1)      # e4m3: one byte per element
-    value = kv / (ms_step * 1e-3) / 1e9
-    achieved = kv / (ker_avg * 1e-3) / 1e9
+        workload = (("llama3_8b_e4m3" if fp8 else "llama3_8b_bf16")
+                    + ("" if Q == 1 else f"_q{Q}") + ": Llama-3-8B-shaped single-layer "
+                    + ("decode" if Q == 1 else f"verification of {Q} new tokens per sequence")
+                    + (", e4m3 KV cache (a scale per KV head)" if fp8 else ""))
+        lens = "uniform [512, 4096], seed 1542"
+        step_desc = f"reshape_and_cache({m['new_tokens']} new tokens) + {m['attn_name']}"
+        profile = (("decode" if Q == 1 else f"multi_query_q{Q}")
+                   + ("_llama3_8b_e4m3" if fp8 else "_llama3_8b_bf16"))
+    dtype = {torch.float16: "fp16", torch.bfloat16: "bf16", torch.float32: "fp32"}[wl.dtype]
     res = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": summ["kv_GBps"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": summ["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 KV, bf16 query" if fp8 else "bf16",
+        "dtype": f"e4m3 KV, {dtype} query" if fp8 else dtype,
         "data": "synthetic",
         "config": {
-            "workload": (("llama3_8b_e4m3" if fp8 else "llama3_8b_bf16")
-                         + ("" if Q == 1 else f"_q{Q}") + ": Llama-3-8B-shaped single-layer "
-                         + ("decode" if Q == 1 else f"verification of {Q} new tokens per sequence")
-                         + (", e4m3 KV cache (a scale per KV head)" if fp8 else "")),
+            "workload": workload,
             "num_seqs": S, "num_heads": H, "num_kv_heads": Hkv, "head_dim": D,
-            "block_size": bs, "num_blocks": NB, "seq_lens": "uniform [512, 4096], seed 1542",
+            "block_size": bs, "num_blocks": NB, "seq_lens": lens,
             "tokens": wl.num_tokens, "kv_bytes_per_step": kv,
-            "partition_tokens": part_tokens, "layers_rotated": len(layers),
-            "step": f"reshape_and_cache({S * Q} new tokens) + {attn_name}",
+            "partition_tokens": m["part_tokens"], "layers_rotated": m["layers"],
+            "step": step_desc,
         },
-        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "seqs_per_s_per_layer": round(S / (ms_step * 1e-3), 1),
-        "decode_us": round(dec_avg * 1e3, 2),
-        "decode_us_p10_p50_p90": [round(dec_q[0] * 1e3, 2), round(statistics.median(dec_ms) * 1e3, 2),
-                                  round(dec_q[-1] * 1e3, 2)],
-        "decode_kernel_us": round(ker_avg * 1e3, 2),
-        "decode_kernel_us_p10_p50_p90": [round(ker_q[0] * 1e3, 2), round(statistics.median(ker_ms) * 1e3, 2),
-                                         round(ker_q[-1] * 1e3, 2)],
-        "decode_us_back_to_back": round(dec_bb * 1e3, 2),
-        "kv_GBps_back_to_back": round(kv / (dec_bb * 1e-3) / 1e9, 1),
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(("decode" if Q == 1 else f"multi_query_q{Q}")
-                                        + ("_llama3_8b_e4m3" if fp8 else "_llama3_8b_bf16")),
-            "kernel": f"{attn_name} (decode_partition_kernel)",
-            "duration": "mean of the kernel's own start-to-end time (events set by its launch, "
-                        "hipExtLaunchKernel) over K more steps like the timed ones",
-        },
-        "cpu_baseline": None,
     }
+    res.update({k: v for k, v in summ.items()
+                if k not in ("kv_GBps", "ms_per_step", "kernel_frac_of_hbm_peak", "achieved_GBps")})
+    res["roofline"] = {
+        "bound": "hbm",
+        "achieved": achieved,
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": measured_traffic(profile),
+        "kernel": f"{m['attn_name']} (decode_partition_kernel)",
+        "duration": "mean of the kernel's own start-to-end time (events set by its launch, "
+                    "hipExtLaunchKernel) over K more steps like the timed ones",
+    }
+    res["cpu_baseline"] = None
+    ks, vs = m["scales"]
+    second = None
+    if name == "llama2_70b_fp16" and not args.no_second_workload:
+        log("generating workload llama3_8b_bf16 (second line item)")
+        second = W.llama3_8b()
+        m2 = time_step(pkv, second, dev, args, layers_n=args.layers)
+        s2 = step_summary(second, m2)
+        res["llama3_8b_bf16"] = {
+            "workload": "llama3_8b_bf16: Llama-3-8B-shaped single-layer decode (64 sequences, "
+                        "32 / 8 heads, head_dim 128, bf16, block_size 16, lengths uniform "
+                        "[512, 4096])",
+            "step": f"reshape_and_cache({m2['new_tokens']} new tokens) + paged_attn_decode",
+            "kv_bytes_per_step": m2["kv"], "partition_tokens": m2["part_tokens"], **s2,
+            "roofline": {"bound": "hbm", "achieved": s2["achieved_GBps"], "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": s2["kernel_frac_of_hbm_peak"],
+                         "traffic": measured_traffic("decode_llama3_8b_bf16")},
+        }
     if not args.no_stream_peak:
         log("measuring the streaming-read rate")
         peak = stream_read_peak(dev)
         res["measured_stream_read_GBps"] = round(peak, 1)
         res["roofline"]["frac_of_measured_stream_read"] = round(achieved / peak, 4)
-    if args.secondary or args.multi_query or args.swap or args.prefix_share:
-        del layers
+    if args.secondary or args.multi_query or args.swap or args.prefix_share or args.per_config:
         torch.cuda.empty_cache()
+    base = second if second is not None else (wl if name == "llama3_8b_bf16" else None)
     if args.swap:
         res["swap"] = swap_rows(pkv, W.llama3_8b(), dev)
     if args.prefix_share:
         res["prefix_share"] = prefix_share_rows(pkv, W, dev)
     if args.secondary:
-        res["secondary"] = secondary(pkv, W, wl, dev)
+        res["secondary"] = secondary(pkv, W, base if base is not None else W.llama3_8b(), dev)
     if args.multi_query:
-        res["multi_query"] = multi_query_rows(pkv, W, wl, dev)
+        res["multi_query"] = multi_query_rows(pkv, W, base if base is not None else W.llama3_8b(), dev)
     if args.per_config:
         res["per_config"] = per_config(pkv, W, dev)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the same step")
         res["cpu_baseline"] = cpu_baseline_fp8(wl, ks, vs) if fp8 else cpu_baseline(wl)
+        one = second if second is not None else (wl if (name == "llama3_8b_bf16" and not fp8) else None)
+        if one is not None:
+            res["cpu_baseline"]["one_thread"] = cpu_baseline_one_thread(one)
     print(json.dumps(res), flush=True)
 
 
