@@ -480,6 +480,35 @@ int paged_attn_timed(void* out, const void* query, const void* key_cache, const 
                      int query_dtype, int out_dtype, int partition_size, void* workspace,
                      size_t workspace_bytes, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
+/*
+ * paged_attn_decode_noalloc - paged_attn_decode without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * caller still passes every input and output; the workspace is a static
+ * device array of PKV_NOALLOC_SCRATCH_BYTES (64 MiB) inside the library, one
+ * per GPU, held until the process ends. Nothing is allocated by the call.
+ * Its first call on a device looks up the array's address
+ * (hipGetSymbolAddress) and clears it with a kernel on `stream`; every call
+ * leaves its control area zero again, as for paged_attn_decode.
+ * Arguments, layout, results and status codes are those of
+ * paged_attn_decode, plus PKV_ERR_WORKSPACE (nothing launched) when the call
+ * needs more workspace than the array holds (paged_attn_workspace_size(...) >
+ * PKV_NOALLOC_SCRATCH_BYTES: e.g. 256 sequences of up to 10 000 tokens at 32
+ * query heads split into 512-token partitions; the library's own partition
+ * choice keeps the page-shaped batches within it) and PKV_ERR_HIP when the
+ * runtime refuses the address lookup. Every call on one GPU shares that
+ * GPU's array: calls that may overlap on one GPU (different streams, other
+ * threads) race and must be serialised by the caller; calls in order on one
+ * stream, and replays of a graph that captured a call, are fine.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int paged_attn_decode_noalloc(void* out, const void* query, const void* key_cache,
+                              const void* value_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, int num_seqs, int num_heads,
+                              int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                              int max_blocks_per_seq, int max_seq_len, float scale, int kv_dtype,
+                              int out_dtype, int partition_size, hipStream_t stream);
+
 /* pagedkv_status_string - a static, NUL-terminated name for a status code. */
 const char* pagedkv_status_string(int status);
 

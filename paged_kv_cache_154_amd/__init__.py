@@ -243,6 +243,34 @@ def paged_attn_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.T
                       events=events)
 
 
+def paged_attn_decode_noalloc(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                              value_cache: torch.Tensor, block_table: torch.Tensor,
+                              seq_lens: torch.Tensor, scale: float, max_seq_len: int,
+                              partition_size: int = 0, stream=None) -> torch.Tensor:
+    """paged_attn_decode with the library's static per-GPU scratch as the
+    workspace: nothing is allocated, by the binding or the library (for code
+    under graph capture and loops that must not allocate). Calls that may
+    overlap on one GPU race on the shared scratch; a call that needs more
+    than its 64 MiB raises PagedKVError (PKV_ERR_WORKSPACE)."""
+    _require(query.dim() == 3 and out.shape == query.shape, "query/out must be [S, H, D]")
+    _require(key_cache.dim() == 4 and value_cache.shape == key_cache.shape,
+             "pools must be [num_blocks, block_size, num_kv_heads, head_dim]")
+    _require(block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32,
+             "block_table and seq_lens must be int32")
+    _require(query.dtype == key_cache.dtype == value_cache.dtype, "query and pools share a dtype")
+    S, H, D = query.shape
+    NB, bs, Hkv, D2 = key_cache.shape
+    _require(D2 == D, "head_dim of query and pools differ")
+    _require(block_table.dim() == 2 and block_table.shape[0] == S and seq_lens.shape == (S,),
+             "block_table must be [S, max_blocks] and seq_lens [S]")
+    st = lib().paged_attn_decode_noalloc(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_table),
+        _ptr(seq_lens), S, H, Hkv, D, bs, NB, block_table.shape[1], int(max_seq_len), float(scale),
+        dtype_code(query.dtype), dtype_code(out.dtype), int(partition_size), _stream(query, stream))
+    check(st, "paged_attn_decode_noalloc")
+    return out
+
+
 def paged_attn_multi_query(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
                            value_cache: torch.Tensor, block_table: torch.Tensor,
                            seq_lens: torch.Tensor, scale: float, max_seq_len: int,

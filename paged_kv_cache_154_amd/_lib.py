@@ -21,6 +21,9 @@ SIGNATURES = {
                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                    _c_int, _c_float, _c_int, _c_int, _c_int, _c_ptr, _c_size,
                                    _c_ptr]),
+    "paged_attn_decode_noalloc": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                           _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                           _c_int, _c_float, _c_int, _c_int, _c_int, _c_ptr]),
     "paged_attn_multi_query": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                         _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                         _c_int, _c_int, _c_float, _c_int, _c_int, _c_int, _c_ptr,

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libpagedkv.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["api.cpp", "decode.hip", "cache_ops.hip", "stream_read.hip", "shared_prefix.hip"]
+SOURCES = ["api.cpp", "decode.hip", "cache_ops.hip", "stream_read.hip", "shared_prefix.hip", "noalloc.hip"]
 
 # Packed fp32 instructions are turned off for all device code.
 HIP_FLAGS = [

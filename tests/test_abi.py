@@ -328,3 +328,22 @@ def test_binding_rejects_bad_tensors_before_the_library():
     with pytest.raises(ValueError):
         pkv.reshape_and_cache(torch.zeros(3, 4, 64), torch.zeros(3, 4, 64), kc, kc,
                               torch.zeros(3, dtype=torch.int32))
+
+
+def test_noalloc_refuses_a_call_beyond_its_scratch():
+    """paged_attn_decode_noalloc's host checks: 256 sequences of 10 000
+    tokens at 32 query heads in 512-token partitions need ~85 MB of partials,
+    more than the 64 MiB static scratch: refused, nothing launched (the
+    pointers are never used); invalid arguments give decode's own status."""
+    SCRATCH = 64 << 20
+    need = pkv.paged_attn_workspace_size(256, 32, 8, 128, 8, 10000, 512)
+    assert need > SCRATCH
+    fake = ctypes.c_void_p(0x10000)
+    st = _lib.lib().paged_attn_decode_noalloc(fake, fake, fake, fake, fake, fake, 256, 32, 8, 128, 8,
+                                              100000, 1250, 10000, ctypes.c_float(0.088), pkv.PKV_BF16,
+                                              pkv.PKV_F32, 512, None)
+    assert st == WS
+    st = _lib.lib().paged_attn_decode_noalloc(fake, fake, fake, fake, fake, fake, 4, 32, 8, 96, 16,
+                                              100, 10, 100, ctypes.c_float(0.1), pkv.PKV_BF16,
+                                              pkv.PKV_F32, 0, None)
+    assert st == UNSUP   # head_dim 96
