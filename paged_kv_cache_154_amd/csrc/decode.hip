@@ -319,6 +319,8 @@ struct TileEngine {
   static constexpr int KT_BYTES = kKLds ? 16 * KTS : 0;  // one wave's K tile
   static_assert(!P4 || (kF8 && D == 128), "the 4x4x1 P.V form takes e4m3 rows of 128 elements");
   static constexpr int NACC = P4 ? 4 : VPL;  // O^T accumulator tiles
+  // bf16 pools: P.V on the bf16 MFMA with the weights cut into exact parts
+  static constexpr bool kPVbf16 = std::is_same<Tag, BF16Tag>::value;
 
   int col;  // MFMA column: query row within the KV head's rows
   int grp;  // lane group 0..3
@@ -437,7 +439,7 @@ struct TileEngine {
   // wholly past the end changes nothing). kt is the wave's LDS tile
   // (KT_BYTES); causal applies the column's own limit `lim` as well
   // (several new tokens).
-  template <bool causal>
+  template <bool causal, bool k_ops = false>
   __device__ void consume(Tile& g, int cs, int t_last, float scale_log2, unsigned char* kt) {
     uint4 (&kr)[NKL] = g.kr;
     if constexpr (kF8) {
@@ -447,7 +449,7 @@ struct TileEngine {
         Tr::widen(raw, kr[2 * u], kr[2 * u + 1]);
       }
     }
-    if constexpr (kKLds) {
+    if constexpr (kKLds && !k_ops) {
       // through the wave's LDS tile (rows padded by 16 bytes: both the row
       // writes and the column reads below hit every bank once) into the
       // MFMA layout: lane (col, grp) takes chunk 4i + grp of token cs + col
@@ -515,6 +517,39 @@ struct TileEngine {
         acc[2] = __builtin_amdgcn_mfma_f32_4x4x1f32(v23.x, w, acc[2], 0, 0, 0);
         acc[3] = __builtin_amdgcn_mfma_f32_4x4x1f32(v23.y, w, acc[3], 0, 0, 0);
       }
+    } else if constexpr (kPVbf16) {
+      // O^T += V^T P^T on the bf16 MFMA, exactly: each weight is cut into
+      // three bf16 parts by truncation (hi = the top 16 bits of its fp32
+      // pattern, mid the same of the remainder, lo the rest, which has at
+      // most 8 significant bits), so hi + mid + lo is the weight itself; the
+      // products with the bf16 V elements are exact and the MFMA sums them in
+      // fp32. A lane group's 32 k slots carry its 4 tokens twice: against
+      // (hi, mid) in one 16x16x32 MFMA and (lo, 0) in a second, so a head-dim
+      // block of a 16-token tile takes two MFMAs (the fp32 16x16x4 form took
+      // four of twice the cycles each).
+      uint32_t hp[4], mp[4], lp[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t u = __float_as_uint(s[r]);
+        hp[r] = u & 0xffff0000u;
+        const float r1 = s[r] - __uint_as_float(hp[r]);
+        mp[r] = __float_as_uint(r1) & 0xffff0000u;
+        lp[r] = __float_as_uint(r1 - __uint_as_float(mp[r]));
+      }
+      // upper halves of a and b -> (a.hi | b.hi << 16)
+      auto hi2 = [](uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); };
+      const uint4 bhm = make_uint4(hi2(hp[0], hp[1]), hi2(hp[2], hp[3]), hi2(mp[0], mp[1]), hi2(mp[2], mp[3]));
+      const uint4 bl0 = make_uint4(hi2(lp[0], lp[1]), hi2(lp[2], lp[3]), 0u, 0u);
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        // element j of tokens (0, 1) and (2, 3), as bf16 pairs
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t x01 = __builtin_amdgcn_perm(g.vr[1][j >> 1], g.vr[0][j >> 1], sel);
+        const uint32_t x23 = __builtin_amdgcn_perm(g.vr[3][j >> 1], g.vr[2][j >> 1], sel);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(x01, x23, x01, x23));
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bhm), acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bl0), acc[j], 0, 0, 0);
+      }
     } else {
       // O^T += V^T P^T, 4 tokens per MFMA
 #pragma unroll
@@ -550,6 +585,57 @@ struct TileEngine {
     issue<nt>(g, kbase, vbase, cs, t_last, slot_bytes, row_off);
     __builtin_amdgcn_sched_barrier(0);  // every load of the tile in flight first
     consume<causal>(g, cs, t_last, scale_log2, kt);
+  }
+
+  // ---- tiles shared by the waves of a workgroup (more than 16 query rows
+  // per KV head: several column groups read every tile) ----------------------
+  // A tile's K and V rows go from HBM straight into LDS (global_load_lds, no
+  // registers held while in flight), once, and every column group reads its
+  // operands from there. A slot holds 16 rows of RB bytes for K and as much
+  // for V; the 16-byte chunks of row t sit at position chunk ^ swz(t), so that
+  // the 16 lanes of a column read (16 rows, one chunk each) and of a V read
+  // (one row, 16 chunks) touch 16 different bank groups.
+  static constexpr int CH = RB / 16;        // 16-byte chunks per row
+  static constexpr int TPI = 64 / CH;       // rows per load instruction (64 lanes x 16 bytes)
+  static constexpr bool kShared = (CH == 8 || CH == 16) && !P4;
+  static constexpr int SLOT_BYTES = 16 * RB;
+  __device__ static inline int swz(int t) { return (t / (16 / CH)) & (CH - 1); }
+
+  // Loads of the tile at cs (cs <= t_last; rows past t_last read t_last's)
+  // into the slot pair (sk, sv): instruction a takes rows a TPI .. a TPI +
+  // TPI - 1, lane l the chunk (l mod CH) ^ swz(row) of row a TPI + l / CH,
+  // written to LDS at the lane's own 16 bytes. Completion: vmcnt.
+  template <bool nt, class RowOff>
+  __device__ void issue_shared(unsigned char* sk, unsigned char* sv, const unsigned char* kbase,
+                               const unsigned char* vbase, int cs, int t_last, RowOff row_off) {
+    static_assert(kShared, "shared tiles take rows of 128 or 256 bytes");
+    const int lane = col + 16 * grp;
+    const int c = lane % CH;
+#pragma unroll
+    for (int a = 0; a < 16 / TPI; ++a) {
+      const int tt = a * TPI + lane / CH;
+      const uint64_t off = row_off(min(cs + tt, t_last)) + 16 * (c ^ swz(tt));
+      __builtin_amdgcn_global_load_lds(kbase + off, (__attribute__((address_space(3))) void*)(sk + a * 1024), 16,
+                                       0, nt ? 2 : 0);
+      __builtin_amdgcn_global_load_lds(vbase + off, (__attribute__((address_space(3))) void*)(sv + a * 1024), 16,
+                                       0, nt ? 2 : 0);
+    }
+  }
+
+  // The operands of the tile in the slot pair (sk, sv), in the layout issue
+  // leaves in registers: key chunk 4u + grp of row col (raw codes for e4m3),
+  // and the V bytes [col VPL E, + VPL E) of rows 4 grp + r.
+  __device__ void fetch_shared(Tile& g, const unsigned char* sk, const unsigned char* sv) {
+#pragma unroll
+    for (int u = 0; u < NKR; ++u)
+      g.kr[u] = *reinterpret_cast<const uint4*>(sk + col * RB + 16 * ((4 * u + grp) ^ swz(col)));
+    constexpr int VB = VPL * E;  // V bytes per lane per row
+    const int b = col * VB;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tt = 4 * grp + r;
+      load_words<false, VW>(g.vr[r], sv + tt * RB + 16 * ((b / 16) ^ swz(tt)) + (b % 16));
+    }
   }
 
   // The wave's unnormalised O rows to LDS: head h's row at o0 + h * ost.
@@ -835,6 +921,16 @@ __host__ __device__ inline int lds_total_bytes(int D, int R, int span, int BS, i
   return lds_main_bytes(D, R, span, BS, kt_bytes) + 2 * kWaves * 16 * 4 + 16 + plan_bytes(S);
 }
 
+// LDS of one wave's share of the tile area for R query rows per KV head: its
+// K reorder tile, or, with several column groups, a shared tile slot pair.
+template <class Eng>
+__host__ __device__ inline int wave_tile_bytes(int R) {
+  if constexpr (Eng::kShared) {
+    if (col_tiles(R) > 1) return Eng::KT_BYTES > 2 * Eng::SLOT_BYTES ? Eng::KT_BYTES : 2 * Eng::SLOT_BYTES;
+  }
+  return Eng::KT_BYTES;
+}
+
 // One work item: KV head kvh of partition `part` of sequence `seq`, by the
 // whole workgroup. Waves take its 16-token tiles round-robin and merge
 // (m, l, O) through LDS; a sequence in one partition is normalised and
@@ -842,7 +938,7 @@ __host__ __device__ inline int lds_total_bytes(int D, int R, int span, int BS, i
 // the workspace and arrives at the (sequence, KV head) word; the last to
 // arrive merges every partition's partials and writes out. With `draw`,
 // thread 0 takes a ticket from the counter for the workgroup's next item.
-template <class Tag, int D, int BS, bool P4>
+template <class Tag, int D, int BS, bool P4, bool SH>
 __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char* smem, int lds_main,
                                             int seq, int L, int kvh, int part, int tid, int wave,
                                             bool draw, int& ticket) {
@@ -954,11 +1050,44 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   };
   using Yes = std::true_type;
   using No = std::false_type;
-  const bool cached = shared || nct > 1;
-  if (p.q_len == 1 || !p.causal) {
-    if (cached) tiles(No{}, No{}); else tiles(Yes{}, No{});
+  // several column groups: rounds of kWaves tiles, each loaded once into the
+  // tile slots in LDS (wave w loads tile w of the round) and read from there
+  // by one wave of every group; barriers bracket the loads of a round.
+  auto shared_tiles = [&](auto nt, auto causal) {
+    if constexpr (SH && Eng::kShared) {
+      unsigned char* slots = smem + bt_lds_bytes(p.partition < p.max_seq_len ? p.partition : p.max_seq_len, BS);
+      const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
+      for (int r0 = 0; r0 < ntiles; r0 += kWaves) {
+        __syncthreads();  // every wave is done with the previous round's slots
+        if (r0 + wave < ntiles)
+          eng.template issue_shared<decltype(nt)::value>(slots + wave * 2 * Eng::SLOT_BYTES,
+                                                         slots + wave * 2 * Eng::SLOT_BYTES + Eng::SLOT_BYTES, kbase,
+                                                         vbase, t_begin + (r0 + wave) * kTile, t_end - 1, row_off);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        for (int k = wi; k < kWaves && r0 + k < ntiles; k += wpg) {
+          typename Eng::Tile g;
+          eng.fetch_shared(g, slots + k * 2 * Eng::SLOT_BYTES, slots + k * 2 * Eng::SLOT_BYTES + Eng::SLOT_BYTES);
+          eng.template consume<decltype(causal)::value, true>(g, t_begin + (r0 + k) * kTile, t_end - 1,
+                                                              scale_log2, nullptr);
+        }
+      }
+    }
+  };
+  const bool causal_rows = p.q_len > 1 && p.causal;
+  if (SH && Eng::kShared && nct > 1) {
+    if (shared) {
+      if (causal_rows) shared_tiles(No{}, Yes{}); else shared_tiles(No{}, No{});
+    } else {
+      if (causal_rows) shared_tiles(Yes{}, Yes{}); else shared_tiles(Yes{}, No{});
+    }
   } else {
-    if (cached) tiles(No{}, Yes{}); else tiles(Yes{}, Yes{});
+    const bool cached = shared || nct > 1;
+    if (!causal_rows) {
+      if (cached) tiles(No{}, No{}); else tiles(Yes{}, No{});
+    } else {
+      if (cached) tiles(No{}, Yes{}); else tiles(Yes{}, Yes{});
+    }
   }
 
   // ---- merge the waves ---------------------------------------------------
@@ -1140,7 +1269,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
 // (then static rounds or counter tickets, as above), or, with `dynamic`,
 // every item from the counter. `parity` alternates the two next-item slots
 // across passes.
-template <class Tag, int D, int BS, bool P4>
+template <class Tag, int D, int BS, bool P4, bool SH>
 __device__ __forceinline__ void run_items(const DecodeParams& p, const Plan& pl, unsigned char* smem, int lds_main,
                                           int* s_next, int wave, bool dynamic, int& parity) {
   const int entries = pl.n_full + pl.S;
@@ -1173,7 +1302,8 @@ __device__ __forceinline__ void run_items(const DecodeParams& p, const Plan& pl,
     // hoisted out of this loop and held in registers across the tiles.
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    decode_item<Tag, D, BS, P4>(p, smem, lds_main, seq, uniform(pl.len[seq]), kvh, part, tid, wave, draw, ticket);
+    decode_item<Tag, D, BS, P4, SH>(p, smem, lds_main, seq, uniform(pl.len[seq]), kvh, part, tid, wave, draw,
+                                    ticket);
     if (threadIdx.x == 0) {
       const int64_t nx = !draw ? (int64_t)nxt_static : (int64_t)ws + ticket;
       s_next[parity] = (nx >= 0 && nx < total) ? (int)nx : total;
@@ -1194,7 +1324,8 @@ void decode_partition_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int wave = uniform(threadIdx.x >> 6);
   const int span = p.partition < p.max_seq_len ? p.partition : p.max_seq_len;
-  const int lds_main = lds_main_bytes(D, p.q_len * p.group, span, BS, TileEngine<Tag, D, BS, P4>::KT_BYTES);
+  const int lds_main = lds_main_bytes(D, p.q_len * p.group, span, BS,
+                                      wave_tile_bytes<TileEngine<Tag, D, BS, P4>>(p.q_len * p.group));
   // Two slots for the next item, used alternately: an item may pass no
   // barrier (a zero-length sequence), and a slot is rewritten only after the
   // barrier that follows every wave's read of it. The third int is the
@@ -1203,18 +1334,18 @@ void decode_partition_kernel(DecodeParams p) {
   Plan pl = plan_at(reinterpret_cast<unsigned char*>(s_next + 4), p.num_seqs);
   build_plan(p, pl, reinterpret_cast<uint64_t*>(smem));
   int parity = 0;
-  run_items<Tag, D, BS, P4>(p, pl, smem, lds_main, s_next, wave, false, parity);
+  run_items<Tag, D, BS, P4, true>(p, pl, smem, lds_main, s_next, wave, false, parity);
   if (threadIdx.x == 0) finish_launch(p.work);  // after the workgroup's last ticket
 }
 
 // LDS of a two-pass launch: the larger main area of the two passes, then the
 // (m, l) slots and next-item slots, then both work lists.
-__host__ __device__ inline int pair_lds_main(int D, int BS, int kt_bytes, const DecodeParams& a,
-                                             const DecodeParams& b) {
+template <class EngA, class EngB>
+__host__ __device__ inline int pair_lds_main(int D, int BS, const DecodeParams& a, const DecodeParams& b) {
   const int la = lds_main_bytes(D, a.q_len * a.group, a.partition < a.max_seq_len ? a.partition : a.max_seq_len,
-                                BS, kt_bytes);
+                                BS, EngA::KT_BYTES);
   const int lb = lds_main_bytes(D, b.q_len * b.group, b.partition < b.max_seq_len ? b.partition : b.max_seq_len,
-                                BS, kt_bytes);
+                                BS, EngB::KT_BYTES);
   return la > lb ? la : lb;
 }
 
@@ -1231,7 +1362,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesP
 void decode_pair_kernel(DecodeParams p0, DecodeParams p1) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int wave = uniform(threadIdx.x >> 6);
-  const int lds_main = pair_lds_main(D, BS, TileEngine<Tag, D, BS>::KT_BYTES, p0, p1);
+  const int lds_main = pair_lds_main<TileEngine<Tag, D, BS>, TileEngine<Tag, D, BS, P4B>>(D, BS, p0, p1);
   int* s_next = reinterpret_cast<int*>(smem + lds_main + 2 * kWaves * 16 * 4);
   unsigned char* plans = reinterpret_cast<unsigned char*>(s_next + 4);
   Plan pl0 = plan_at(plans, p0.num_seqs);
@@ -1239,8 +1370,10 @@ void decode_pair_kernel(DecodeParams p0, DecodeParams p1) {
   build_plan(p0, pl0, reinterpret_cast<uint64_t*>(smem));
   build_plan(p1, pl1, reinterpret_cast<uint64_t*>(smem));
   int parity = 0;
-  run_items<Tag, D, BS, false>(p0, pl0, smem, lds_main, s_next, wave, false, parity);
-  run_items<Tag, D, BS, P4B>(p1, pl1, smem, lds_main, s_next, wave, true, parity);
+  // (the shared tile slots are left to the single-pass kernel: two passes'
+  // worth of tile loops in one kernel would spill registers)
+  run_items<Tag, D, BS, false, false>(p0, pl0, smem, lds_main, s_next, wave, false, parity);
+  run_items<Tag, D, BS, P4B, false>(p1, pl1, smem, lds_main, s_next, wave, true, parity);
   if (threadIdx.x == 0) {  // after the workgroup's last ticket of each pass
     finish_launch(p0.work);
     finish_launch(p1.work);
@@ -1289,7 +1422,7 @@ hipError_t launch_p(const DecodeParams& p, hipStream_t stream, hipEvent_t start,
   // so that two workgroups fit per CU, when the rest of it leaves room.
   int chunk = kMaxSeqsPerLaunch;
   {
-    const int fixed = lds_total_bytes(D, p.q_len * p.group, span, BS, Eng::KT_BYTES, 0);
+    const int fixed = lds_total_bytes(D, p.q_len * p.group, span, BS, wave_tile_bytes<Eng>(p.q_len * p.group), 0);
     const int room = (kLdsPerWorkgroup - fixed - 32) / 10;
     if (room < chunk) chunk = room > 256 ? room : 256;
   }
@@ -1302,7 +1435,7 @@ hipError_t launch_p(const DecodeParams& p, hipStream_t stream, hipEvent_t start,
     c.block_table = p.block_table + (size_t)s0 * p.max_blocks;
     c.seq_lens = p.seq_lens + s0;
     const size_t lds =
-        (size_t)lds_total_bytes(D, c.q_len * c.group, span, BS, Eng::KT_BYTES, c.num_seqs);
+        (size_t)lds_total_bytes(D, c.q_len * c.group, span, BS, wave_tile_bytes<Eng>(c.q_len * c.group), c.num_seqs);
     const int64_t max_items = (int64_t)c.num_seqs * c.num_kv_heads * c.num_partitions;
     int64_t grid = resident_workgroups(kfn, lds);
     if (grid > max_items) grid = max_items;
@@ -1336,8 +1469,8 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream, hipEvent_t start,
 template <class Tag, int D, int BS, bool P4B>
 hipError_t launch_pair_p(DecodeParams a, DecodeParams b, hipStream_t stream) {
   if (a.num_seqs > kMaxSeqsPerLaunch || b.num_seqs > kMaxSeqsPerLaunch) return hipErrorNotSupported;
-  const int kt = TileEngine<Tag, D, BS>::KT_BYTES;
-  const size_t lds = (size_t)pair_lds_main(D, BS, kt, a, b) + 2 * kWaves * 16 * 4 + 16 + plan_bytes(a.num_seqs) +
+  const size_t lds = (size_t)pair_lds_main<TileEngine<Tag, D, BS>, TileEngine<Tag, D, BS, P4B>>(D, BS, a, b) +
+                     2 * kWaves * 16 * 4 + 16 + plan_bytes(a.num_seqs) +
                      plan_bytes(b.num_seqs);
   if (lds > (size_t)kLdsPerWorkgroup) return hipErrorNotSupported;
   const void* kfn = reinterpret_cast<const void*>(&decode_pair_kernel<Tag, D, BS, P4B>);
