@@ -28,11 +28,13 @@
 //        tokens) as the B operand (the other columns are 0).
 //        The result S[token][head] leaves each lane one head's scores for 4
 //        tokens, so a head's softmax state lives in one lane column;
-//      - P.V on v_mfma_f32_16x16x4_f32 with A = V^T (each lane holds head_dim
-//        / 16 contiguous elements of one token's V row, widened to fp32) and
-//        B = P^T in fp32: probabilities never drop below fp32, and the output
-//        tile O^T[d][head] keeps a head in the same lane column as its
-//        softmax state, so the online rescale is lane-local.
+//      - P.V with A = V^T (each lane holds head_dim / 16 contiguous elements
+//        of 4 tokens' V rows) and B = P^T: on v_mfma_f32_16x16x32_bf16 for
+//        bf16 and e4m3 pools, each weight cut exactly into three bf16 parts
+//        (hi + mid + lo = the fp32 weight), on v_mfma_f32_16x16x4_f32 with
+//        fp32 weights otherwise: the probabilities keep fp32 precision, and
+//        the output tile O^T[d][head] keeps a head in the same lane column
+//        as its softmax state, so the online rescale is lane-local.
 //  * Tokens past seq_len in the last tile are never read: their address is
 //    clamped to the last valid token (finite data) and their score is set to
 //    -inf before the exponent, so their weight is exactly 0.
@@ -154,22 +156,12 @@ struct KV<BF16Tag> {
   }
 };
 
-// e4m3 code `b` (0..3) of the word w, as fp32 (every e4m3 value is exact).
-__device__ inline float f8_at(uint32_t w, int b) {
-  switch (b) {
-    case 0: return __builtin_amdgcn_cvt_f32_fp8(w, 0);
-    case 1: return __builtin_amdgcn_cvt_f32_fp8(w, 1);
-    case 2: return __builtin_amdgcn_cvt_f32_fp8(w, 2);
-    default: return __builtin_amdgcn_cvt_f32_fp8(w, 3);
-  }
-}
-
 typedef float f32x2v __attribute__((ext_vector_type(2)));
 
 // The e4m3 K/V traits over a 16-bit query type Q16 (KV<BF16Tag> or
 // KV<F16Tag>): the key codes are widened to Q16 in registers (exactly: e4m3
 // has 3 mantissa bits and a range inside both) for the 16-bit MFMA, values
-// to fp32 for the fp32 MFMA.
+// to bf16 (exactly) for the bf16 P.V MFMA.
 template <class Q16, bool kBF>
 struct KVe4m3 {
   static constexpr int kBytes = 1;
@@ -195,7 +187,6 @@ struct KVe4m3 {
     widen4(raw.z, c1.x, c1.y);
     widen4(raw.w, c1.z, c1.w);
   }
-  __device__ static inline float elem(const uint32_t* w, int j) { return f8_at(w[j >> 2], j & 3); }
   __device__ static inline void store(void* out, size_t i, float x) { Q16::store(out, i, x); }
   __device__ static inline void store4(void* out, size_t i, float4 x) { Q16::store4(out, i, x); }
 };
@@ -290,15 +281,7 @@ __device__ inline float lse_of(float M, float den) { return den > 0.0f ? M + __l
 // Per-lane state of one wave working through the tiles of one (sequence, KV
 // head): the query operand, the softmax state of head `col` and its O^T
 // accumulators.
-//
-// P4 (e4m3 rows of 128 elements, at most 4 query rows per KV head): P.V runs
-// on the 4x4x1 fp32 MFMA, 16 blocks of 4 x 4, so that only the 4 columns of
-// the query rows are computed instead of the 16 of the 16x16x4 one. V is
-// loaded per token pair: lanes 0-31 take the first token, 32-63 the second,
-// 4 codes (4 head-dim elements) per lane; lane 4b + h then accumulates head
-// h over head-dim 16 (b % 8) + 4 i + c in acc[c][i], and the halves b and
-// b + 8 (the pair's two tokens) are summed when O goes to LDS.
-template <class Tag, int D, int BS, bool P4 = false>
+template <class Tag, int D, int BS>
 struct TileEngine {
   using Tr = KV<Tag>;
   static constexpr int E = Tr::kBytes;
@@ -317,10 +300,10 @@ struct TileEngine {
   static constexpr int KCL = RB / 256;     // 16-byte chunks per lane per token (K rows whole)
   static constexpr int KTS = RB + 16;      // LDS row stride of the K tile
   static constexpr int KT_BYTES = kKLds ? 16 * KTS : 0;  // one wave's K tile
-  static_assert(!P4 || (kF8 && D == 128), "the 4x4x1 P.V form takes e4m3 rows of 128 elements");
-  static constexpr int NACC = P4 ? 4 : VPL;  // O^T accumulator tiles
-  // bf16 pools: P.V on the bf16 MFMA with the weights cut into exact parts
-  static constexpr bool kPVbf16 = std::is_same<Tag, BF16Tag>::value;
+  static constexpr int NACC = VPL;  // O^T accumulator tiles
+  // bf16 and e4m3 pools: P.V on the bf16 MFMA with the weights cut into exact
+  // parts (e4m3 values are bf16 values)
+  static constexpr bool kPVbf16 = std::is_same<Tag, BF16Tag>::value || kF8;
 
   int col;  // MFMA column: query row within the KV head's rows
   int grp;  // lane group 0..3
@@ -328,7 +311,7 @@ struct TileEngine {
   uint4 qv[NKL];
   float m;     // running max of head `col` (log2 units)
   float lsum;  // this lane's share of the running sum of weights
-  f32x4 acc[NACC];  // acc[j][i] = O[head col][VPL * (4 * grp + i) + j] (P4: as above)
+  f32x4 acc[NACC];  // acc[j][i] = O[head col][VPL * (4 * grp + i) + j]
 
   __device__ void init(int lane) {
     col = lane & 15;
@@ -358,8 +341,7 @@ struct TileEngine {
   // The registers of one tile's K and V, as loaded.
   struct Tile {
     uint4 kr[NKL];
-    uint32_t vr[P4 ? 1 : 4][P4 ? 1 : VW];
-    uint32_t vq[P4 ? 8 : 1];  // P4: codes of token cs + 2 q + (lane >> 5), 4 per lane
+    uint32_t vr[4][VW];
   };
 
   // Loads of the tile of tokens cs .. cs+15 (cs a multiple of 16, cs <=
@@ -401,32 +383,7 @@ struct TileEngine {
         for (int i = 0; i < NKL; ++i) kr[i] = *reinterpret_cast<const uint4*>(kp + 64 * i);
       }
     }
-    if constexpr (P4) {
-      const int lane = col + 16 * grp;
-      const int h2 = lane >> 5;
-      const unsigned char* vp = vbase + 4 * (lane & 31);
-      if constexpr (BS % 16 == 0) {  // the whole tile in one block
-        const unsigned char* vt = vp + row_off(cs);
-        const uint32_t rt = (uint32_t)(t_last - cs);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint32_t r = (uint32_t)(2 * q + h2);
-          g.vq[q] = NTL<nt>::ld(reinterpret_cast<const uint32_t*>(vt + (r < rt ? r : rt) * slot_bytes));
-        }
-      } else {  // 4-aligned groups of tokens (never across a block)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int ta = min(cs + 4 * a, t_last);
-          const unsigned char* vt = vp + row_off(ta);
-          const uint32_t ra = (uint32_t)(t_last - ta);
-#pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            const uint32_t r = (uint32_t)(2 * b + h2);
-            g.vq[2 * a + b] = NTL<nt>::ld(reinterpret_cast<const uint32_t*>(vt + (r < ra ? r : ra) * slot_bytes));
-          }
-        }
-      }
-    } else {
+    {
       const unsigned char* vp = vbase + off4 + col * (VPL * E);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -484,10 +441,8 @@ struct TileEngine {
       const float m_new = fmaxf(m, cmax);
       const float alpha = fast_exp2(m - m_new);
       lsum *= alpha;
-      // P4: lane 4b + h holds sums of head h, whose alpha is lane h's
-      const float a_acc = P4 ? __shfl(alpha, (col + 16 * grp) & 3) : alpha;
 #pragma unroll
-      for (int j = 0; j < NACC; ++j) acc[j] *= a_acc;
+      for (int j = 0; j < NACC; ++j) acc[j] *= alpha;
       m = m_new;
     }
 #pragma unroll
@@ -496,28 +451,7 @@ struct TileEngine {
       lsum += s[r];
     }
 
-    if constexpr (P4) {
-      // token pair q: the weights of tokens cs + 2q and cs + 2q + 1 sit in
-      // lanes 16 (q / 2) + h (head h), registers 2 (q % 2) and 2 (q % 2) + 1;
-      // each half of the wave takes its token's, then one 4x4x1 MFMA per
-      // code of the lane's V word
-      const int lane = col + 16 * grp;
-      const bool second = lane >= 32;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int src = 16 * (q >> 1) + (lane & 3);
-        const float w0 = __shfl(s[2 * (q & 1)], src);
-        const float w1 = __shfl(s[2 * (q & 1) + 1], src);
-        const float w = second ? w1 : w0;
-        // the word's 4 codes widened two at a time
-        const f32x2v v01 = __builtin_amdgcn_cvt_pk_f32_fp8(g.vq[q], false);
-        const f32x2v v23 = __builtin_amdgcn_cvt_pk_f32_fp8(g.vq[q], true);
-        acc[0] = __builtin_amdgcn_mfma_f32_4x4x1f32(v01.x, w, acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_4x4x1f32(v01.y, w, acc[1], 0, 0, 0);
-        acc[2] = __builtin_amdgcn_mfma_f32_4x4x1f32(v23.x, w, acc[2], 0, 0, 0);
-        acc[3] = __builtin_amdgcn_mfma_f32_4x4x1f32(v23.y, w, acc[3], 0, 0, 0);
-      }
-    } else if constexpr (kPVbf16) {
+    if constexpr (kPVbf16) {
       // O^T += V^T P^T on the bf16 MFMA, exactly: each weight is cut into
       // three bf16 parts by truncation (hi = the top 16 bits of its fp32
       // pattern, mid the same of the remainder, lo the rest, which has at
@@ -540,39 +474,42 @@ struct TileEngine {
       auto hi2 = [](uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); };
       const uint4 bhm = make_uint4(hi2(hp[0], hp[1]), hi2(hp[2], hp[3]), hi2(mp[0], mp[1]), hi2(mp[2], mp[3]));
       const uint4 bl0 = make_uint4(hi2(lp[0], lp[1]), hi2(lp[2], lp[3]), 0u, 0u);
-#pragma unroll
-      for (int j = 0; j < VPL; ++j) {
-        // element j of tokens (0, 1) and (2, 3), as bf16 pairs
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t x01 = __builtin_amdgcn_perm(g.vr[1][j >> 1], g.vr[0][j >> 1], sel);
-        const uint32_t x23 = __builtin_amdgcn_perm(g.vr[3][j >> 1], g.vr[2][j >> 1], sel);
+      auto pv = [&](int j, uint32_t x01, uint32_t x23) {
         const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(x01, x23, x01, x23));
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bhm), acc[j], 0, 0, 0);
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bl0), acc[j], 0, 0, 0);
+      };
+      if constexpr (kF8) {
+        // e4m3 V: bytes j and j + 1 of tokens (0, 1) gathered into one word
+        // and widened to bf16 exactly (e4m3 values are bf16 values), two
+        // elements per conversion
+#pragma unroll
+        for (int j = 0; j < VPL; j += 2) {
+          const uint32_t b0 = j & 3;
+          const uint32_t sel = b0 | ((4u + b0) << 8) | ((b0 + 1u) << 16) | ((5u + b0) << 24);
+          const uint32_t t01 = __builtin_amdgcn_perm(g.vr[1][j >> 2], g.vr[0][j >> 2], sel);
+          const uint32_t t23 = __builtin_amdgcn_perm(g.vr[3][j >> 2], g.vr[2][j >> 2], sel);
+          pv(j, __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(t01, 1.0f, false)),
+             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(t23, 1.0f, false)));
+          pv(j + 1, __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(t01, 1.0f, true)),
+             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(t23, 1.0f, true)));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          // element j of tokens (0, 1) and (2, 3), as bf16 pairs
+          const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+          pv(j, __builtin_amdgcn_perm(g.vr[1][j >> 1], g.vr[0][j >> 1], sel),
+             __builtin_amdgcn_perm(g.vr[3][j >> 1], g.vr[2][j >> 1], sel));
+        }
       }
     } else {
       // O^T += V^T P^T, 4 tokens per MFMA
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if constexpr (kF8) {  // the row's codes widened two at a time
-          float e[VPL];
 #pragma unroll
-          for (int u = 0; u < VPL / 4; ++u) {
-            const f32x2v a = __builtin_amdgcn_cvt_pk_f32_fp8(g.vr[r][u], false);
-            const f32x2v b = __builtin_amdgcn_cvt_pk_f32_fp8(g.vr[r][u], true);
-            e[4 * u] = a.x;
-            e[4 * u + 1] = a.y;
-            e[4 * u + 2] = b.x;
-            e[4 * u + 3] = b.y;
-          }
-#pragma unroll
-          for (int j = 0; j < VPL; ++j)
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(e[j], s[r], acc[j], 0, 0, 0);
-        } else {
-#pragma unroll
-          for (int j = 0; j < VPL; ++j)
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(Tr::elem(g.vr[r], j), s[r], acc[j], 0, 0, 0);
-        }
+        for (int j = 0; j < VPL; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(Tr::elem(g.vr[r], j), s[r], acc[j], 0, 0, 0);
       }
     }
   }
@@ -597,7 +534,7 @@ struct TileEngine {
   // (one row, 16 chunks) touch 16 different bank groups.
   static constexpr int CH = RB / 16;        // 16-byte chunks per row
   static constexpr int TPI = 64 / CH;       // rows per load instruction (64 lanes x 16 bytes)
-  static constexpr bool kShared = (CH == 8 || CH == 16) && !P4;
+  static constexpr bool kShared = CH == 8 || CH == 16;
   static constexpr int SLOT_BYTES = 16 * RB;
   __device__ static inline int swz(int t) { return (t / (16 / CH)) & (CH - 1); }
 
@@ -639,23 +576,9 @@ struct TileEngine {
   }
 
   // The wave's unnormalised O rows to LDS: head h's row at o0 + h * ost.
-  // Called by every lane; writes the rows of this lane's column when `valid`
-  // (P4: the rows h < rows).
-  __device__ void write_o(float* o0, int ost, bool valid, int rows) {
-    if constexpr (P4) {
-      const int lane = col + 16 * grp;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[c][i] += __shfl_xor(acc[c][i], 32);
-      const int h = lane & 3;
-      if (lane < 32 && h < rows) {
-        float* orow = o0 + (size_t)h * ost + 16 * (lane >> 2);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<float4*>(orow + 4 * i) = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
-      }
-    } else if (valid) {
+  // Called by every lane; writes the rows of this lane's column when `valid`.
+  __device__ void write_o(float* o0, int ost, bool valid) {
+    if (valid) {
       float* orow = o0 + (size_t)col * ost;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -938,12 +861,12 @@ __host__ __device__ inline int wave_tile_bytes(int R) {
 // the workspace and arrives at the (sequence, KV head) word; the last to
 // arrive merges every partition's partials and writes out. With `draw`,
 // thread 0 takes a ticket from the counter for the workgroup's next item.
-template <class Tag, int D, int BS, bool P4, bool SH>
+template <class Tag, int D, int BS, bool SH>
 __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char* smem, int lds_main,
                                             int seq, int L, int kvh, int part, int tid, int wave,
                                             bool draw, int& ticket) {
   const int lane = tid & 63;
-  using Eng = TileEngine<Tag, D, BS, P4>;
+  using Eng = TileEngine<Tag, D, BS>;
   constexpr int RB = Eng::RB;
   constexpr int DQ = D / 4;  // quads (4 consecutive head-dim elements) per row
   const int G = p.group;
@@ -1119,7 +1042,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
     s_m[wave * 16 + eng.col] = eng.m;
     s_l[wave * 16 + eng.col] = lsum;
   }
-  eng.write_o(s_o + (size_t)(wave * RW) * OST, OST, valid, RW);
+  eng.write_o(s_o + (size_t)(wave * RW) * OST, OST, valid);
   __syncthreads();
 
   // One quad of one row per thread and pass: the group's waves combined with
@@ -1269,7 +1192,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
 // (then static rounds or counter tickets, as above), or, with `dynamic`,
 // every item from the counter. `parity` alternates the two next-item slots
 // across passes.
-template <class Tag, int D, int BS, bool P4, bool SH>
+template <class Tag, int D, int BS, bool SH>
 __device__ __forceinline__ void run_items(const DecodeParams& p, const Plan& pl, unsigned char* smem, int lds_main,
                                           int* s_next, int wave, bool dynamic, int& parity) {
   const int entries = pl.n_full + pl.S;
@@ -1302,7 +1225,7 @@ __device__ __forceinline__ void run_items(const DecodeParams& p, const Plan& pl,
     // hoisted out of this loop and held in registers across the tiles.
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    decode_item<Tag, D, BS, P4, SH>(p, smem, lds_main, seq, uniform(pl.len[seq]), kvh, part, tid, wave, draw,
+    decode_item<Tag, D, BS, SH>(p, smem, lds_main, seq, uniform(pl.len[seq]), kvh, part, tid, wave, draw,
                                     ticket);
     if (threadIdx.x == 0) {
       const int64_t nx = !draw ? (int64_t)nxt_static : (int64_t)ws + ticket;
@@ -1318,14 +1241,14 @@ __device__ __forceinline__ void run_items(const DecodeParams& p, const Plan& pl,
 // workgroup whose next item is a counter one draws a ticket while it merges
 // its current item; every ticket advances the counter, so every workgroup
 // ends. The last workgroup to end sets the control word back to zero.
-template <class Tag, int D, int BS, bool P4>
+template <class Tag, int D, int BS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEU<Tag, D>::value)))
 void decode_partition_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int wave = uniform(threadIdx.x >> 6);
   const int span = p.partition < p.max_seq_len ? p.partition : p.max_seq_len;
   const int lds_main = lds_main_bytes(D, p.q_len * p.group, span, BS,
-                                      wave_tile_bytes<TileEngine<Tag, D, BS, P4>>(p.q_len * p.group));
+                                      wave_tile_bytes<TileEngine<Tag, D, BS>>(p.q_len * p.group));
   // Two slots for the next item, used alternately: an item may pass no
   // barrier (a zero-length sequence), and a slot is rewritten only after the
   // barrier that follows every wave's read of it. The third int is the
@@ -1334,7 +1257,7 @@ void decode_partition_kernel(DecodeParams p) {
   Plan pl = plan_at(reinterpret_cast<unsigned char*>(s_next + 4), p.num_seqs);
   build_plan(p, pl, reinterpret_cast<uint64_t*>(smem));
   int parity = 0;
-  run_items<Tag, D, BS, P4, true>(p, pl, smem, lds_main, s_next, wave, false, parity);
+  run_items<Tag, D, BS, true>(p, pl, smem, lds_main, s_next, wave, false, parity);
   if (threadIdx.x == 0) finish_launch(p.work);  // after the workgroup's last ticket
 }
 
@@ -1355,14 +1278,13 @@ __host__ __device__ inline int pair_lds_main(int D, int BS, const DecodeParams& 
 // the second pass's items from that pass's own counter, so the first pass's
 // ramp-down is filled with the second pass's (short) items instead of
 // ending the launch. Each pass has its own control word, work list and
-// split-K workspace. P4B: the second pass takes the 4x4x1 P.V instance
-// (e4m3 rows of 128 elements, at most 4 query rows per KV head).
-template <class Tag, int D, int BS, bool P4B>
+// split-K workspace.
+template <class Tag, int D, int BS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEU<Tag, D>::value)))
 void decode_pair_kernel(DecodeParams p0, DecodeParams p1) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int wave = uniform(threadIdx.x >> 6);
-  const int lds_main = pair_lds_main<TileEngine<Tag, D, BS>, TileEngine<Tag, D, BS, P4B>>(D, BS, p0, p1);
+  const int lds_main = pair_lds_main<TileEngine<Tag, D, BS>, TileEngine<Tag, D, BS>>(D, BS, p0, p1);
   int* s_next = reinterpret_cast<int*>(smem + lds_main + 2 * kWaves * 16 * 4);
   unsigned char* plans = reinterpret_cast<unsigned char*>(s_next + 4);
   Plan pl0 = plan_at(plans, p0.num_seqs);
@@ -1372,8 +1294,8 @@ void decode_pair_kernel(DecodeParams p0, DecodeParams p1) {
   int parity = 0;
   // (the shared tile slots are left to the single-pass kernel: two passes'
   // worth of tile loops in one kernel would spill registers)
-  run_items<Tag, D, BS, false, false>(p0, pl0, smem, lds_main, s_next, wave, false, parity);
-  run_items<Tag, D, BS, P4B, false>(p1, pl1, smem, lds_main, s_next, wave, true, parity);
+  run_items<Tag, D, BS, false>(p0, pl0, smem, lds_main, s_next, wave, false, parity);
+  run_items<Tag, D, BS, false>(p1, pl1, smem, lds_main, s_next, wave, true, parity);
   if (threadIdx.x == 0) {  // after the workgroup's last ticket of each pass
     finish_launch(p0.work);
     finish_launch(p1.work);
@@ -1408,11 +1330,11 @@ int resident_workgroups(const void* kernel, size_t lds) {
   return n;
 }
 
-template <class Tag, int D, int BS, bool P4>
-hipError_t launch_p(const DecodeParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  using Eng = TileEngine<Tag, D, BS, P4>;
+template <class Tag, int D, int BS>
+hipError_t launch_t(const DecodeParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  using Eng = TileEngine<Tag, D, BS>;
   const int span = p.partition < p.max_seq_len ? p.partition : p.max_seq_len;
-  const void* kfn = reinterpret_cast<const void*>(&decode_partition_kernel<Tag, D, BS, P4>);
+  const void* kfn = reinterpret_cast<const void*>(&decode_partition_kernel<Tag, D, BS>);
   const size_t q_row = (size_t)p.q_len * p.num_heads * D;  // elements per sequence
   const size_t q_elem = (size_t)KV<Tag>::kQBytes;  // the output, unless fp32, has the query's type
   const size_t out_elem = p.out_f32 ? 4 : q_elem;
@@ -1443,54 +1365,34 @@ hipError_t launch_p(const DecodeParams& p, hipStream_t stream, hipEvent_t start,
     hipEvent_t ev0 = s0 == 0 ? start : nullptr;                 // the first launch's start
     hipEvent_t ev1 = s0 + c.num_seqs >= p.num_seqs ? stop : nullptr;  // the last one's end
     if (ev0 || ev1)
-      hipExtLaunchKernelGGL(decode_partition_kernel<Tag, D, BS, P4>, dim3((unsigned)grid), dim3(kThreads),
+      hipExtLaunchKernelGGL(decode_partition_kernel<Tag, D, BS>, dim3((unsigned)grid), dim3(kThreads),
                             (uint32_t)lds, stream, ev0, ev1, 0u, c);
     else
-      decode_partition_kernel<Tag, D, BS, P4><<<dim3((unsigned)grid), dim3(kThreads), lds, stream>>>(c);
+      decode_partition_kernel<Tag, D, BS><<<dim3((unsigned)grid), dim3(kThreads), lds, stream>>>(c);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
-// e4m3 rows of 128 elements with at most 4 query rows per KV head take the
-// 4x4x1 P.V form; everything else the 16x16x4 one.
-template <class Tag, int D, int BS>
-hipError_t launch_t(const DecodeParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  if constexpr (KV<Tag>::kF8 && D == 128) {
-    if (p.q_len * p.group <= 4) return launch_p<Tag, D, BS, true>(p, stream, start, stop);
-  }
-  return launch_p<Tag, D, BS, false>(p, stream, start, stop);
-}
-
 // Two passes in one launch when both fit one launch's work list and LDS
 // budget; hipErrorNotSupported otherwise (the caller then runs them one
 // after the other).
-template <class Tag, int D, int BS, bool P4B>
-hipError_t launch_pair_p(DecodeParams a, DecodeParams b, hipStream_t stream) {
+template <class Tag, int D, int BS>
+hipError_t launch_pair_t(DecodeParams a, DecodeParams b, hipStream_t stream) {
   if (a.num_seqs > kMaxSeqsPerLaunch || b.num_seqs > kMaxSeqsPerLaunch) return hipErrorNotSupported;
-  const size_t lds = (size_t)pair_lds_main<TileEngine<Tag, D, BS>, TileEngine<Tag, D, BS, P4B>>(D, BS, a, b) +
+  const size_t lds = (size_t)pair_lds_main<TileEngine<Tag, D, BS>, TileEngine<Tag, D, BS>>(D, BS, a, b) +
                      2 * kWaves * 16 * 4 + 16 + plan_bytes(a.num_seqs) +
                      plan_bytes(b.num_seqs);
   if (lds > (size_t)kLdsPerWorkgroup) return hipErrorNotSupported;
-  const void* kfn = reinterpret_cast<const void*>(&decode_pair_kernel<Tag, D, BS, P4B>);
+  const void* kfn = reinterpret_cast<const void*>(&decode_pair_kernel<Tag, D, BS>);
   const int64_t max_items = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions +
                             (int64_t)b.num_seqs * b.num_kv_heads * b.num_partitions;
   int64_t grid = resident_workgroups(kfn, lds);
   if (grid > max_items) grid = max_items;
   if (grid >= 8) grid = grid / 8 * 8;
-  decode_pair_kernel<Tag, D, BS, P4B><<<dim3((unsigned)grid), dim3(kThreads), lds, stream>>>(a, b);
+  decode_pair_kernel<Tag, D, BS><<<dim3((unsigned)grid), dim3(kThreads), lds, stream>>>(a, b);
   return hipGetLastError();
-}
-
-// The first pass always takes the 16x16x4 P.V instance; the second the
-// 4x4x1 one where the single-pass launch would.
-template <class Tag, int D, int BS>
-hipError_t launch_pair_t(const DecodeParams& a, const DecodeParams& b, hipStream_t stream) {
-  if constexpr (KV<Tag>::kF8 && D == 128) {
-    if (b.q_len * b.group <= 4) return launch_pair_p<Tag, D, BS, true>(a, b, stream);
-  }
-  return launch_pair_p<Tag, D, BS, false>(a, b, stream);
 }
 
 template <class Tag, int D>

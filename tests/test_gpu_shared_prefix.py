@@ -159,8 +159,8 @@ def test_shared_prefix_beyond_one_launch_runs_the_passes_in_turn():
     assert_close(out, ref, torch.bfloat16, seqs, label="shared prefix, two launches")
 
 
-# the second pass's 4x4x1 P.V form (head_dim 128, <= 4 rows per KV head)
-# and the 16x16x4 one (8 rows per KV head; head_dim 64)
+# head_dim 128 with 2, 4 and 8 query rows per KV head in the second pass,
+# and head_dim 64
 @pytest.mark.parametrize("qdt,G,D", [(torch.bfloat16, 4, 128), (torch.float16, 2, 128),
                                      (torch.float16, 8, 128), (torch.bfloat16, 4, 64)])
 def test_shared_prefix_fp8_matches_oracle(qdt, G, D):
