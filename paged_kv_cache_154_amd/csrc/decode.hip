@@ -295,11 +295,14 @@ struct TileEngine {
   static constexpr int VW = VPL * E / 4;  // 32-bit words per lane per token of V
   static_assert(RB % 64 == 0, "row must split into 4 lane groups of 16-byte chunks");
   // Rows of >= 256 bytes load K like V (whole rows) and reorder it through
-  // LDS; shorter rows load it in the operand layout.
+  // LDS; rows of 128 bytes (e4m3 at head_dim 128, 16-bit types at 64) are
+  // read whole too, 8 rows per instruction, and reordered the same way;
+  // shorter rows load it in the operand layout.
   static constexpr bool kKLds = RB >= 256;
+  static constexpr bool kKLds128 = RB == 128;
   static constexpr int KCL = RB / 256;     // 16-byte chunks per lane per token (K rows whole)
   static constexpr int KTS = RB + 16;      // LDS row stride of the K tile
-  static constexpr int KT_BYTES = kKLds ? 16 * KTS : 0;  // one wave's K tile
+  static constexpr int KT_BYTES = (kKLds || kKLds128) ? 16 * KTS : 0;  // one wave's K tile
   static constexpr int NACC = VPL;  // O^T accumulator tiles
   // bf16 and e4m3 pools: P.V on the bf16 MFMA with the weights cut into exact
   // parts (e4m3 values are bf16 values)
@@ -369,6 +372,16 @@ struct TileEngine {
           kr[r * KCL + u] = make_uint4(a.x, a.y, a.z, a.w);
         }
       }
+    } else if constexpr (kKLds128) {
+      // 8 lanes read a token's 128-byte row: instruction a takes rows 8 a ..
+      // 8 a + 7 of the tile (raw codes for e4m3)
+      const int lane = col + 16 * grp;
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const unsigned char* kp = kbase + row_off(min(cs + 8 * a + (lane >> 3), t_last)) + 16 * (lane & 7);
+        const u32x4 v = NTL<nt>::ld(reinterpret_cast<const u32x4*>(kp));
+        kr[a] = make_uint4(v.x, v.y, v.z, v.w);
+      }
     } else {
       const unsigned char* kp = kbase + row_off(min(cs + col, t_last)) + 16 * grp;
       if constexpr (kF8) {
@@ -399,6 +412,18 @@ struct TileEngine {
   template <bool causal, bool k_ops = false>
   __device__ void consume(Tile& g, int cs, int t_last, float scale_log2, unsigned char* kt) {
     uint4 (&kr)[NKL] = g.kr;
+    if constexpr (kKLds128 && !k_ops) {
+      // whole rows through the wave's LDS tile (rows padded by 16 bytes) into
+      // the operand layout: lane (col, grp) takes chunk 4u + grp of token cs
+      // + col (raw codes for e4m3, widened below)
+      const int lane = col + 16 * grp;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        *reinterpret_cast<uint4*>(kt + (8 * a + (lane >> 3)) * KTS + 16 * (lane & 7)) = kr[a];
+#pragma unroll
+      for (int u = 0; u < NKR; ++u)
+        kr[u] = *reinterpret_cast<const uint4*>(kt + col * KTS + 16 * (4 * u + grp));
+    }
     if constexpr (kF8) {
 #pragma unroll
       for (int u = NKR - 1; u >= 0; --u) {  // from the top: slot u is read before it is written
