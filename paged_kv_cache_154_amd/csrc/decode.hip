@@ -302,7 +302,8 @@ struct TileEngine {
   static constexpr bool kKLds128 = RB == 128;
   static constexpr int KCL = RB / 256;     // 16-byte chunks per lane per token (K rows whole)
   static constexpr int KTS = RB + 16;      // LDS row stride of the K tile
-  static constexpr int KT_BYTES = (kKLds || kKLds128) ? 16 * KTS : 0;  // one wave's K tile
+  // one wave's K tile (and, for 128-byte rows, its V tile after it)
+  static constexpr int KT_BYTES = kKLds ? 16 * KTS : (kKLds128 ? 2 * 16 * KTS : 0);
   static constexpr int NACC = VPL;  // O^T accumulator tiles
   // bf16 and e4m3 pools: P.V on the bf16 MFMA with the weights cut into exact
   // parts (e4m3 values are bf16 values)
@@ -396,7 +397,20 @@ struct TileEngine {
         for (int i = 0; i < NKL; ++i) kr[i] = *reinterpret_cast<const uint4*>(kp + 64 * i);
       }
     }
-    {
+    if constexpr (kKLds128) {
+      // V rows whole as well, 8 per instruction, into the words vr holds
+      // (reordered in consume)
+      const int lane = col + 16 * grp;
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const unsigned char* vp = vbase + row_off(min(cs + 8 * a + (lane >> 3), t_last)) + 16 * (lane & 7);
+        const u32x4 v = NTL<nt>::ld(reinterpret_cast<const u32x4*>(vp));
+        g.vr[2 * a][0] = v.x;
+        g.vr[2 * a][1] = v.y;
+        g.vr[2 * a + 1][0] = v.z;
+        g.vr[2 * a + 1][1] = v.w;
+      }
+    } else {
       const unsigned char* vp = vbase + off4 + col * (VPL * E);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -423,6 +437,19 @@ struct TileEngine {
 #pragma unroll
       for (int u = 0; u < NKR; ++u)
         kr[u] = *reinterpret_cast<const uint4*>(kt + col * KTS + 16 * (4 * u + grp));
+      // V the same way: lane (col, grp) takes bytes [8 col, 8 col + 8) of
+      // tokens cs + 4 grp + r
+      unsigned char* vt = kt + 16 * KTS;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        *reinterpret_cast<uint4*>(vt + (8 * a + (lane >> 3)) * KTS + 16 * (lane & 7)) =
+            make_uint4(g.vr[2 * a][0], g.vr[2 * a][1], g.vr[2 * a + 1][0], g.vr[2 * a + 1][1]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint2 w = *reinterpret_cast<const uint2*>(vt + (4 * grp + r) * KTS + 8 * col);
+        g.vr[r][0] = w.x;
+        g.vr[r][1] = w.y;
+      }
     }
     if constexpr (kF8) {
 #pragma unroll
