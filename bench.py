@@ -634,7 +634,8 @@ def time_step(pkv, wl, dev, args, Q=1, fp8=False, P=None, layers_n=4):
     layers = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(layers_n - 1)]
     out = torch.empty(wl.query.shape, dtype=wl.dtype, device=dev)
     ws = pkv.workspace_for(q, kc0, wl.max_seq_len, P)
-    part_tokens = pkv.paged_attn_partition_tokens(S, Hkv, bs, wl.max_seq_len, P)
+    part_tokens = pkv.paged_attn_partition_tokens(S, Hkv, bs, wl.max_seq_len, P, q_len=Q, num_heads=H,
+                                                  kv_dtype=pkv.PKV_E4M3 if fp8 else pkv.dtype_code(wl.dtype))
     stream = torch.cuda.current_stream(dev)
 
     def step(i):

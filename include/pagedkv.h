@@ -301,15 +301,20 @@ size_t paged_attn_shared_prefix_workspace_size(int num_groups, int group_size, i
                                                int partition_size);
 
 /*
- * paged_attn_partition_tokens - the partition length paged_attn_decode uses
- * for these arguments (resolving partition_size = 0), or a negative
- * pkv_status for invalid arguments. A value >= max_seq_len means no split.
- * The choice for 0: no split when there are at least 2048 (sequence, KV
- * head) pairs and max_seq_len <= 4096; else 1024 while that makes at most
- * 4096 (sequence, KV head, partition) units; else 2048.
+ * paged_attn_partition_tokens - the partition length the attention entry
+ * points use for these arguments (resolving partition_size = 0) over a pool
+ * of kv_dtype with q_len new tokens per sequence (1 for decode), or a
+ * negative pkv_status for invalid arguments. A value >= max_seq_len means no
+ * split. The choice for 0 starts from a base B: 1024 tokens, doubled for
+ * PKV_E4M3 pools and doubled again when q_len * num_heads / num_kv_heads >
+ * 16: no split when there are at least 2048 (sequence, KV head) pairs and
+ * max_seq_len <= 4096; else B while that makes at most 4096 (sequence, KV
+ * head, partition) units; else 2 B. The workspace sizes are those of the
+ * shortest choice (16-bit pools), which serve every dtype.
  */
-int paged_attn_partition_tokens(int num_seqs, int num_kv_heads, int block_size,
-                                int max_seq_len, int partition_size);
+int paged_attn_partition_tokens(int num_seqs, int q_len, int num_heads, int num_kv_heads,
+                                int block_size, int max_seq_len, int partition_size,
+                                int kv_dtype);
 
 /*
  * paged_attn_workspace_size - bytes of workspace paged_attn_decode needs for

@@ -94,9 +94,15 @@ def _require(cond: bool, msg: str) -> None:
 
 
 def paged_attn_partition_tokens(num_seqs: int, num_kv_heads: int, block_size: int,
-                                max_seq_len: int, partition_size: int = 0) -> int:
-    r = lib().paged_attn_partition_tokens(num_seqs, num_kv_heads, block_size, max_seq_len,
-                                          partition_size)
+                                max_seq_len: int, partition_size: int = 0, q_len: int = 1,
+                                num_heads: int | None = None, kv_dtype: int = PKV_BF16) -> int:
+    """The partition length the attention calls use (partition_size 0: the
+    library's choice for a pool of kv_dtype and q_len new tokens per
+    sequence); num_heads defaults to num_kv_heads (only the query rows per KV
+    head, q_len * num_heads / num_kv_heads, matter)."""
+    H = num_kv_heads if num_heads is None else num_heads
+    r = lib().paged_attn_partition_tokens(num_seqs, q_len, H, num_kv_heads, block_size, max_seq_len,
+                                          partition_size, kv_dtype)
     if r < 0:
         raise PagedKVError(r, "paged_attn_partition_tokens")
     return r
@@ -139,7 +145,10 @@ def workspace_control_bytes(num_seqs: int, num_kv_heads: int, head_dim: int, blo
                             max_seq_len: int, partition_size: int = 0) -> int:
     """Bytes at the start of a decode / multi-query workspace that must be
     zero at its first use (the control area; include/pagedkv.h): 256, plus
-    the arrival counts padded to 256 bytes when sequences are split."""
+    the arrival counts padded to 256 bytes when sequences are split (taken
+    for the shortest partition choice, that of 16-bit pools at one query
+    row per head, so the size serves every call the workspace is sized
+    for)."""
     P = paged_attn_partition_tokens(num_seqs, num_kv_heads, block_size, max_seq_len,
                                     partition_size)
     if P >= max_seq_len:

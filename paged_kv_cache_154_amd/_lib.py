@@ -52,7 +52,7 @@ SIGNATURES = {
                                             + [_c_ptr, _c_size, _c_ptr]),
     "paged_attn_shared_prefix_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int,
                                                           _c_int, _c_int, _c_int, _c_int]),
-    "paged_attn_partition_tokens": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "paged_attn_partition_tokens": (_c_int, [_c_int] * 8),
     "paged_attn_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                             _c_int]),
     "reshape_and_cache": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int,

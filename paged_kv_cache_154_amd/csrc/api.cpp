@@ -54,28 +54,38 @@ constexpr int kMaxQueryRows = 16 * pkv::kWaves;
 
 // Partition length chosen when partition_size is 0. A workgroup (8 waves)
 // handles one (sequence, KV head, partition); 512 fit on the GPU at once (256
-// CUs, 2 each). Measured on MI355X: with >= 2048 (sequence, KV head) pairs and
-// sequences of at most 4096 tokens, not splitting is best; otherwise 1024-token
+// CUs, 2 each). A base of B tokens: 1024 for 16-bit and fp32 pools, twice
+// that for e4m3 pools (half the bytes per token) and twice again with more
+// than 16 query rows per KV head (every tile costs each column group its
+// work). Measured on MI355X: with >= 2048 (sequence, KV head) pairs and
+// sequences of at most 4096 tokens, not splitting is best; otherwise B-token
 // partitions while that gives at most 4096 (sequence, KV head, partition)
-// units, else 2048 (fewer partials to write and merge).
-int auto_partition(int num_seqs, int num_kv_heads, int block_size, int max_seq_len) {
+// units, else 2 B (fewer partials to write and merge).
+int auto_partition(int num_seqs, int num_kv_heads, int block_size, int max_seq_len, int kv_elem_bytes,
+                   int rows) {
   const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
   const int unit = block_size > pkv::kTile ? block_size : pkv::kTile;
+  int base = 1024;
+  if (kv_elem_bytes == 1) base *= 2;
+  if (rows > 16) base *= 2;
   if (pairs >= 2048 && max_seq_len <= 4096) {
     const int P = (max_seq_len + unit - 1) / unit * unit;
     return P > 0 ? P : unit;
   }
-  if (pairs * ((max_seq_len + 1023) / 1024) <= 4096) return 1024;
-  return 2048;
+  if (pairs * ((max_seq_len + base - 1) / base) <= 4096) return base;
+  return 2 * base;
 }
 
 // Partition length for these arguments (> 0), or a negative status.
+// kv_elem_bytes and rows (query rows per KV head) only steer the choice for
+// partition_size 0; the workspace sizes take 2 bytes, the shortest choice.
 int resolve_partition(int num_seqs, int num_kv_heads, int block_size, int max_seq_len,
-                      int partition_size) {
+                      int partition_size, int kv_elem_bytes, int rows) {
   if (partition_size < 0) return PKV_ERR_SHAPE;
   if (!supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
-  const int P = partition_size == 0 ? auto_partition(num_seqs, num_kv_heads, block_size, max_seq_len)
-                                    : partition_size;
+  const int P = partition_size == 0
+                    ? auto_partition(num_seqs, num_kv_heads, block_size, max_seq_len, kv_elem_bytes, rows)
+                    : partition_size;
   if (P % pkv::kTile != 0 || P % block_size != 0) return PKV_ERR_SHAPE;
   if (P >= max_seq_len) {
     // one partition per sequence: its block-table slice must fit in LDS
@@ -134,10 +144,14 @@ size_t workspace_bytes_for(int num_seqs, int num_heads, int num_kv_heads, int he
 
 extern "C" {
 
-int paged_attn_partition_tokens(int num_seqs, int num_kv_heads, int block_size, int max_seq_len,
-                                int partition_size) {
-  if (num_seqs < 0 || num_kv_heads <= 0 || max_seq_len < 0) return PKV_ERR_SHAPE;
-  return resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
+int paged_attn_partition_tokens(int num_seqs, int q_len, int num_heads, int num_kv_heads, int block_size,
+                                int max_seq_len, int partition_size, int kv_dtype) {
+  if (num_seqs < 0 || q_len < 1 || num_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0 ||
+      num_heads % num_kv_heads != 0)
+    return PKV_ERR_SHAPE;
+  if (elem_bytes(kv_dtype) == 0) return PKV_ERR_UNSUPPORTED;
+  return resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size,
+                           elem_bytes(kv_dtype), q_len * (num_heads / num_kv_heads));
 }
 
 }  // extern "C"
@@ -177,7 +191,8 @@ int attention(void* out, const void* query, const void* key_cache, const void* v
   if ((int64_t)max_blocks_per_seq * block_size < max_seq_len) return PKV_ERR_SHAPE;
   if ((int64_t)num_blocks * block_size > (int64_t)INT32_MAX) return PKV_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return PKV_ERR_SHAPE;
-  const int P = resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
+  const int P = resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size,
+                                  elem_bytes(kv_dtype), q_len * group);
   if (P < 0) return P;
   const Cutting cut = cutting_for(max_seq_len, block_size, P);
   const int np = cut.np;
@@ -249,7 +264,10 @@ WorkspaceParts workspace_parts(int num_seqs, int q_len, int num_heads, int num_k
       q_len * (num_heads / num_kv_heads) > kMaxQueryRows)
     return w;
   if (!supported_head_dim(head_dim)) return w;
-  const int P = resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size);
+  // the shortest partition any pool dtype gets (2-byte elements): the most
+  // partials, so the size serves every dtype
+  const int P = resolve_partition(num_seqs, num_kv_heads, block_size, max_seq_len, partition_size, 2,
+                                  q_len * (num_heads / num_kv_heads));
   if (P < 0) return w;
   const int np = cutting_for(max_seq_len, block_size, P).np;
   w.ctl = control_bytes_for(num_seqs, num_kv_heads, np);

@@ -216,19 +216,30 @@ def test_multi_query_workspace_sizing():
             == _ws_expected(256, 4 * 32, 8, 128, 20))
     assert L.paged_attn_multi_query_workspace_size(64, 2, 32, 8, 128, 16, 512, 512) == hdr
     assert L.paged_attn_multi_query_workspace_size(64, 33, 32, 8, 128, 16, 4039, 0) == 0
+    # 8 x 4 = 32 query rows per KV head: 2048-token partitions
     assert (L.paged_attn_multi_query_workspace_size(64, 8, 32, 8, 128, 16, 4039, 0)
-            == _ws_expected(64, 8 * 32, 8, 128, 4))
+            == _ws_expected(64, 8 * 32, 8, 128, 2))
     assert L.paged_attn_multi_query_workspace_size(64, 0, 32, 8, 128, 16, 4039, 0) == 0
 
 
 def test_partition_and_workspace_sizing():
     L = _lib.lib()
     # partition_size 0: the library's choice
-    assert L.paged_attn_partition_tokens(64, 8, 16, 4039, 0) == 1024     # few (seq, KV head) pairs
-    assert L.paged_attn_partition_tokens(256, 8, 32, 8192, 0) == 2048    # many, long
-    assert L.paged_attn_partition_tokens(384, 8, 16, 2560, 0) == 2560    # many, short: no split
-    assert L.paged_attn_partition_tokens(64, 8, 8, 10000, 512) == 512
-    assert L.paged_attn_partition_tokens(64, 8, 32, 100, 48) == SHAPE    # not a multiple of 32
+    # (num_seqs, q_len, num_heads, num_kv_heads, block_size, max_seq_len, partition, kv_dtype)
+    pt = L.paged_attn_partition_tokens
+    assert pt(64, 1, 32, 8, 16, 4039, 0, 2) == 1024     # few (seq, KV head) pairs
+    assert pt(256, 1, 64, 8, 32, 8192, 0, 1) == 2048    # many, long
+    assert pt(384, 1, 32, 8, 16, 2560, 0, 2) == 2560    # many, short: no split
+    assert pt(64, 1, 32, 8, 8, 10000, 512, 2) == 512    # the caller's partition
+    assert pt(64, 1, 32, 8, 32, 100, 48, 2) == SHAPE    # not a multiple of 32
+    # e4m3 pools: twice the tokens per partition; more than 16 query rows per
+    # KV head: twice again
+    assert pt(64, 1, 32, 8, 16, 4039, 0, 3) == 2048
+    assert pt(256, 1, 64, 8, 32, 8192, 0, 3) == 4096
+    assert pt(64, 8, 32, 8, 16, 4039, 0, 2) == 2048     # q_len 8 x 4 heads = 32 rows
+    assert pt(64, 4, 32, 8, 16, 4039, 0, 2) == 1024     # 16 rows
+    assert pt(64, 1, 32, 8, 16, 4039, 0, 9) == UNSUP
+    assert pt(64, 1, 30, 8, 16, 4039, 0, 2) == SHAPE    # heads not a multiple of KV heads
     hdr = 256
     assert L.paged_attn_workspace_size(64, 32, 8, 128, 16, 512, 512) == hdr   # no split
     n = L.paged_attn_workspace_size(256, 32, 8, 128, 8, 10000, 512)
