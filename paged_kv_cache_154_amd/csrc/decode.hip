@@ -674,8 +674,8 @@ __device__ inline Cut cut_of(int L, int P) {
 }
 
 // The work list of one launch (at most kMaxSeqsPerLaunch sequences), built
-// by every workgroup in its own LDS from seq_lens when it starts. Entries are
-// (sequence, partition):
+// by every workgroup in its own LDS from seq_lens. Entries are (sequence,
+// partition):
 //   * first the full partitions n-1 .. 1 of every split sequence, in batch
 //     order: sequence s owns entries [full[s], full[s+1]) (an exclusive scan
 //     of n_s - 1);
@@ -685,7 +685,10 @@ __device__ inline Cut cut_of(int L, int P) {
 // Item w is entry w / num_kv_heads with KV head w % num_kv_heads. Long items
 // first and short ones last even out the end of the launch; the stable order
 // keeps sequences that sit next to each other in the batch (such as samples
-// of one prompt sharing its blocks) next to each other in time.
+// of one prompt sharing its blocks) next to each other in time. A
+// workgroup whose first item is a full partition of one of the first 64
+// sequences finds it with a scan of those 64 lengths in each wave (see
+// first_entry) and builds the list after that item.
 constexpr int kClasses = 4;
 constexpr int kClassBits = 12;  // packed per-class counts: kMaxSeqsPerLaunch < 2^12
 static_assert(kMaxSeqsPerLaunch < (1 << kClassBits), "class counts must fit their field");
@@ -830,6 +833,47 @@ __device__ inline void plan_entry(const Plan& pl, int e, int& seq, int& part) {
   }
 }
 
+// Entry e of the work list when it is a full partition of one of the first
+// 64 sequences, or, in a launch that splits no sequence, one of the first 64
+// sequences in the longest class (the list's order, without the list): each
+// wave loads those lengths, one per lane, and an inclusive scan of their
+// n_s - 1 gives full[s + 1]; the sequence is the first lane whose count
+// exceeds e. False (and nothing set) when entry e lies further on. len: the
+// sequence's length.
+__device__ inline bool first_entry(const DecodeParams& p, int e, int& seq, int& part, int& len) {
+  const int lane = threadIdx.x & 63;
+  const int n = p.num_seqs < 64 ? p.num_seqs : 64;
+  const int L = lane < n ? clamp_len(p.seq_lens[lane], p.max_seq_len) : 0;
+  int incl = L > 0 ? cut_of(L, p.partition).n - 1 : 0;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  const unsigned long long past = __ballot(incl > e);
+  if (past != 0ull) {
+    const int s = __ffsll((long long)past) - 1;
+    seq = s;
+    part = uniform(__shfl(incl, s)) - e;  // full[s + 1] - e: highest partition first
+    len = uniform(__shfl(L, s));
+    return true;
+  }
+  if (p.num_partitions != 1) return false;
+  // No sequence is split: the list is the partitions 0 by class, and the
+  // longest-class sequences among the first 64 are its first entries, in
+  // batch order. Entry e is the one with e such sequences before it.
+  const bool longest = L > 0 && length_class(cut_of(L, p.partition).r, p.partition) == 0;
+  const unsigned long long m = __ballot(longest);
+  const int before = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  const unsigned long long hit = __ballot(longest && before == e);
+  if (hit == 0ull) return false;
+  const int s = __ffsll((long long)hit) - 1;
+  seq = s;
+  part = 0;
+  len = uniform(__shfl(L, s));
+  return true;
+}
+
 // ---------------------------------------------------------------------------
 // Schedule of one launch over a persistent grid of `grid` workgroups (a
 // multiple of 8). Items below a split point are dealt statically in rounds of
@@ -879,12 +923,15 @@ __device__ inline void finish_launch(unsigned long long* word) {
   if ((uint32_t)(old >> 32) == gridDim.x - 1) atomicExch(word, 0ull);
 }
 
+// Control ints of a workgroup in LDS (next-item slots, merge flag, pending item).
+constexpr int kCtlInts = 8;
+
 // Partitions a merge reads per round trip.
 constexpr int kMergeBatch = 8;
 
 // LDS of the partition kernel: the partition's block-table slice and the
 // waves' K tiles, reused for the waves' O rows (and at the start for the
-// plan's scan); then the waves' (m, l); then the next item; then the plan.
+// plan's scan); then the waves' (m, l); then the control ints; then the plan.
 __host__ __device__ inline int bt_lds_bytes(int span, int BS) { return ((span / BS + 1) * 4 + 15) & ~15; }
 // R: query rows per KV head (q_len * G); a wave keeps at most 16 of them.
 __host__ __device__ inline int lds_main_bytes(int D, int R, int span, int BS, int kt_bytes) {
@@ -893,7 +940,7 @@ __host__ __device__ inline int lds_main_bytes(int D, int R, int span, int BS, in
   return ((o_bytes > tile_bytes ? o_bytes : tile_bytes) + 15) & ~15;
 }
 __host__ __device__ inline int lds_total_bytes(int D, int R, int span, int BS, int kt_bytes, int S) {
-  return lds_main_bytes(D, R, span, BS, kt_bytes) + 2 * kWaves * 16 * 4 + 16 + plan_bytes(S);
+  return lds_main_bytes(D, R, span, BS, kt_bytes) + 2 * kWaves * 16 * 4 + 4 * kCtlInts + plan_bytes(S);
 }
 
 // LDS of one wave's share of the tile area for R query rows per KV head: its
@@ -913,6 +960,89 @@ __host__ __device__ inline int wave_tile_bytes(int R) {
 // the workspace and arrives at the (sequence, KV head) word; the last to
 // arrive merges every partition's partials and writes out. With `draw`,
 // thread 0 takes a ticket from the counter for the workgroup's next item.
+// Merge of the split (seq, kvh): run by the workgroup whose arrival
+// completed the count. The partials are read with agent-scope atomic loads
+// (sc1: from the level every XCD shares, never a stale line of this XCD's
+// L2) and combined in partition order: M = max m_q, then the sums of
+// 2^(m_q - M) l_q and 2^(m_q - M) O_q, the running max moved between batches
+// of loads.
+template <class Tag, int D>
+__device__ __forceinline__ void merge_partials(const DecodeParams& p, int seq, int kvh, int nparts, int tid) {
+  constexpr int DQ = D / 4;
+  const int G = p.group;
+  const int R = p.q_len * G;
+  const int head0 = kvh * G;
+  const int g_inv = (2048 + G - 1) / G;  // token of row c: (c * g_inv) >> 11, as in decode_item
+  float v_scale = 1.0f;
+  if constexpr (KV<Tag>::kF8) v_scale = p.v_scale[kvh];
+  for (int qi = tid; qi < R * DQ; qi += kThreads) {
+    const int r = qi / DQ;
+    const int qd = qi - r * DQ;
+    const int d = 4 * qd;
+    const int j = (r * g_inv) >> 11;
+    const size_t row = ((size_t)seq * p.q_len + j) * p.num_heads + head0 + (r - j * G);
+    const unsigned long long* ml =
+        reinterpret_cast<const unsigned long long*>(p.ws_ml + 2 * row * p.num_partitions);
+    const unsigned long long* o =
+        reinterpret_cast<const unsigned long long*>(p.ws_o + row * p.num_partitions * D + 2 * qd);
+    // kMergeBatch partitions per round trip: every load of a batch (the
+    // (m, l) pair and the quad of each partition) is issued before any is
+    // used
+    float M = kNoMax, den = 0.0f;
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q0 = 0; q0 < nparts; q0 += kMergeBatch) {
+      unsigned long long mlq[kMergeBatch], oa[kMergeBatch], ob[kMergeBatch];
+      // one base per batch: the loads below take constant offsets from it
+      const unsigned long long* mlb = ml + q0;
+      const unsigned long long* ob0 = o + (size_t)q0 * (D / 2);
+#pragma unroll
+      for (int jj = 0; jj < kMergeBatch; ++jj) {
+        mlq[jj] = pack2(kNoMax, 0.0f);
+        oa[jj] = ob[jj] = 0ull;
+        if (q0 + jj < nparts) {
+          mlq[jj] = __hip_atomic_load(&mlb[jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          oa[jj] = __hip_atomic_load(&ob0[jj * (D / 2)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ob[jj] = __hip_atomic_load(&ob0[jj * (D / 2) + DQ], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      float cm = lo_of(mlq[0]);
+#pragma unroll
+      for (int jj = 1; jj < kMergeBatch; ++jj) cm = fmaxf(cm, lo_of(mlq[jj]));
+      const float M_new = fmaxf(M, cm);
+      const float alpha = fast_exp2(M - M_new);  // 0 for the first batch
+      den *= alpha;
+      num.x *= alpha;
+      num.y *= alpha;
+      num.z *= alpha;
+      num.w *= alpha;
+      M = M_new;
+#pragma unroll
+      for (int jj = 0; jj < kMergeBatch; ++jj) {
+        const float wq = fast_exp2(lo_of(mlq[jj]) - M);
+        den += wq * hi_of(mlq[jj]);
+        num.x += wq * lo_of(oa[jj]);
+        num.y += wq * hi_of(oa[jj]);
+        num.z += wq * lo_of(ob[jj]);
+        num.w += wq * hi_of(ob[jj]);
+      }
+    }
+    // num / den per element (times the V scale of an e4m3 pool), as for an
+    // unsplit row; 0 for a row that saw no position
+    float4 out = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (den > 0.0f) {
+      out = make_float4(num.x / den, num.y / den, num.z / den, num.w / den);
+      if constexpr (KV<Tag>::kF8) {
+        out.x *= v_scale;
+        out.y *= v_scale;
+        out.z *= v_scale;
+        out.w *= v_scale;
+      }
+    }
+    store_out4<Tag>(p, row * D + d, out);
+    if (p.lse && d == 0) p.lse[row] = lse_of(M, den);
+  }
+}
+
 template <class Tag, int D, int BS, bool SH>
 __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char* smem, int lds_main,
                                             int seq, int L, int kvh, int part, int tid, int wave,
@@ -985,6 +1115,14 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   const int bnext = next[0];
   eng.lim = valid && p.causal ? L - p.q_len + token_of(myrow) : L - 1;
   eng.reset();
+  // A split item of this workgroup that has not yet arrived (the pending
+  // item, recorded in ctl[4..6] at the end of that item): its partial stores
+  // were issued then; waiting for them here costs nothing beyond the start's
+  // own round trip, which is in flight with them.
+  int* ctl = reinterpret_cast<int*>(smem + lds_main + 2 * kWaves * 16 * 4);
+  const int pseq0 = uniform(ctl[4]);
+  const int pkvh0 = uniform(ctl[5]);
+  if (pseq0 >= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (tid < nlb) s_bt[tid] = ((unsigned)e0 < (unsigned)p.num_blocks) ? e0 : 0;  // never leave the pool
   for (int i = tid + kThreads; i < nlb; i += kThreads) {
     const int b = row[i];
@@ -996,6 +1134,12 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   // with non-temporal loads. Only the speed depends on this guess.
   const bool shared = (seq > 0 && bprev == b0) || (seq + 1 < p.num_seqs && bnext == b0);
   __syncthreads();
+  // every thread's stores of the pending item are acknowledged: it arrives
+  // now, and the count comes back while the tiles stream
+  uint32_t pdone = 0;
+  if (pseq0 >= 0 && tid == 0)
+    pdone = __hip_atomic_fetch_add(p.arrive + (size_t)pseq0 * p.num_kv_heads + pkvh0, 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
 
   unsigned char* kt = smem + bt_lds_bytes(p.partition < p.max_seq_len ? p.partition : p.max_seq_len, BS) +
                      wave * Eng::KT_BYTES;
@@ -1073,6 +1217,19 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   // items taken one after the other (the KV heads of the same tokens) start
   // close together in time.
   if (draw && tid == 0) ticket = take_ticket(p.work);
+  // the pending item's count: the partition that completes it merges. The
+  // record is read here, before the barrier below, so that thread 0 may
+  // rewrite it at the end of this item.
+  const int pseq = uniform(ctl[4]);
+  const int pkvh = uniform(ctl[5]);
+  const int pn = uniform(ctl[6]);
+  if (pseq >= 0 && tid == 0) {
+    const bool last = pdone == (uint32_t)(pn - 1);
+    if (last)  // every other partition has arrived: ready for the next launch
+      __hip_atomic_store(p.arrive + (size_t)pseq * p.num_kv_heads + pkvh, 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    ctl[2] = last;
+  }
   // num / den per element (times the V scale of an e4m3 pool); 0 for a row
   // that saw no position
   auto finish = [&](float4 num, float den) -> float4 {
@@ -1148,95 +1305,56 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (nparts <= 1) return;
+  // the pending item's merge, when its arrival completed the count
+  if (pseq >= 0 && ctl[2]) merge_partials<Tag, D>(p, pseq, pkvh, pn, tid);
+  // This item's partials are in flight: it becomes the pending item and
+  // arrives at the start of the workgroup's next item (or at the end of the
+  // pass). Every wave read the old record before the last barrier.
+  if (tid == 0) {
+    ctl[4] = nparts > 1 ? seq : -1;
+    ctl[5] = kvh;
+    ctl[6] = nparts;
+  }
+}
 
-  // ---- the last partition of (seq, kvh) to finish merges them all ---------
-  // Publication of the partials across XCDs (each XCD has its own L2): the
-  // partials are agent-scope atomic stores, which gfx950 issues with the sc1
-  // bit, written through to the level all XCDs share (LLVM AMDGPUUsage,
-  // memory model for GFX942 and later: "store atomic monotonic agent" is a
-  // global_store with sc1); every thread's s_waitcnt vmcnt(0) waits until its
-  // stores are acknowledged by that level; after the workgroup barrier,
-  // thread 0 arrives with an agent-scope atomic add on the (seq, kvh) word
-  // (performed at the same level); the partition that sees the count reach
-  // nparts - 1 reads the partials with agent-scope atomic loads (sc1: served
-  // from the shared level, never from a stale line of its own L2). So every
-  // partial is complete where the merger reads it before the merger can see
-  // the count. (The language-level alternative, an agent-scope release
-  // fence before the arrival and an acquire fence in the merger, adds an
-  // L2-wide write-back and invalidate per partition: measured 151.7 vs 102.9
-  // us on the Llama-3-8B-shaped batch, 576 vs 293 us on the mixed batch at
-  // 512-token partitions.) The merge combines the partitions in index
-  // order: M = max m_q, then sums of 2^(m_q - M) l_q and 2^(m_q - M) O_q
-  // (with the running max moved between batches of loads). The merging
-  // partition sets the word back to zero for the next launch: every other
-  // partition's add precedes it (atomics on one location, the count seen
-  // complete).
+// Arrival of the workgroup's pending item at the end of a pass (see
+// decode_item), and its merge when that completes the count.
+//
+// Publication of the partials across XCDs (each XCD has its own L2): the
+// partials are agent-scope atomic stores, which gfx950 issues with the sc1
+// bit, written through to the level all XCDs share (LLVM AMDGPUUsage,
+// memory model for GFX942 and later: "store atomic monotonic agent" is a
+// global_store with sc1); every thread's s_waitcnt vmcnt(0) waits until its
+// stores are acknowledged by that level; after a workgroup barrier, thread
+// 0 arrives with an agent-scope atomic add on the (seq, kvh) word (performed
+// at the same level); the partition that sees the count reach nparts - 1
+// reads the partials with agent-scope atomic loads (sc1: served from the
+// shared level). So every partial is complete where the merger reads it
+// before the merger can see the count. (The language-level alternative, an
+// agent-scope release fence before the arrival and an acquire fence in the
+// merger, adds an L2-wide write-back and invalidate per partition: measured
+// 151.7 vs 102.9 us on the Llama-3-8B-shaped batch, 576 vs 293 us on the
+// mixed batch at 512-token partitions.) The merging partition sets the word
+// back to zero for the next launch: every other partition's add precedes
+// it (atomics on one location, the count seen complete).
+template <class Tag, int D>
+__device__ __forceinline__ void arrive_pending(const DecodeParams& p, int* ctl) {
+  const int pseq = uniform(ctl[4]);
+  if (pseq < 0) return;
+  const int pkvh = uniform(ctl[5]);
+  const int pn = uniform(ctl[6]);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  int* s_last = reinterpret_cast<int*>(smem + lds_main + 2 * kWaves * 16 * 4) + 2;
-  if (tid == 0) {
-    uint32_t* word = p.arrive + (size_t)seq * p.num_kv_heads + kvh;
+  if (threadIdx.x == 0) {
+    uint32_t* word = p.arrive + (size_t)pseq * p.num_kv_heads + pkvh;
     const uint32_t done = __hip_atomic_fetch_add(word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = done == (uint32_t)(nparts - 1);
+    const bool last = done == (uint32_t)(pn - 1);
     if (last) __hip_atomic_store(word, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_last = last;
+    ctl[2] = last;
+    ctl[4] = -1;
   }
   __syncthreads();
-  if (!*s_last) return;
-  for (int qi = tid; qi < R * DQ; qi += kThreads) {
-    const int r = qi / DQ;
-    const int qd = qi - r * DQ;
-    const int d = 4 * qd;
-    const size_t row = row_of(r);
-    const unsigned long long* ml =
-        reinterpret_cast<const unsigned long long*>(p.ws_ml + 2 * row * p.num_partitions);
-    const unsigned long long* o =
-        reinterpret_cast<const unsigned long long*>(p.ws_o + row * p.num_partitions * D + 2 * qd);
-    // kMergeBatch partitions per round trip: every load of a batch (the
-    // (m, l) pair and the quad of each partition) is issued before any is
-    // used; the running max moves between batches
-    float M = kNoMax, den = 0.0f;
-    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int q0 = 0; q0 < nparts; q0 += kMergeBatch) {
-      unsigned long long mlq[kMergeBatch], oa[kMergeBatch], ob[kMergeBatch];
-      // one base per batch: the loads below take constant offsets from it
-      const unsigned long long* mlb = ml + q0;
-      const unsigned long long* ob0 = o + (size_t)q0 * (D / 2);
-#pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) {
-        mlq[j] = pack2(kNoMax, 0.0f);
-        oa[j] = ob[j] = 0ull;
-        if (q0 + j < nparts) {
-          mlq[j] = __hip_atomic_load(&mlb[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          oa[j] = __hip_atomic_load(&ob0[j * (D / 2)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          ob[j] = __hip_atomic_load(&ob0[j * (D / 2) + DQ], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-      float cm = lo_of(mlq[0]);
-#pragma unroll
-      for (int j = 1; j < kMergeBatch; ++j) cm = fmaxf(cm, lo_of(mlq[j]));
-      const float M_new = fmaxf(M, cm);
-      const float alpha = fast_exp2(M - M_new);  // 0 for the first batch
-      den *= alpha;
-      num.x *= alpha;
-      num.y *= alpha;
-      num.z *= alpha;
-      num.w *= alpha;
-      M = M_new;
-#pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) {
-        const float wq = fast_exp2(lo_of(mlq[j]) - M);
-        den += wq * hi_of(mlq[j]);
-        num.x += wq * lo_of(oa[j]);
-        num.y += wq * hi_of(oa[j]);
-        num.z += wq * lo_of(ob[j]);
-        num.w += wq * hi_of(ob[j]);
-      }
-    }
-    store_out4<Tag>(p, row * D + d, finish(num, den));
-    if (p.lse && d == 0) p.lse[row] = lse_of(M, den);
-  }
+  if (ctl[2]) merge_partials<Tag, D>(p, pseq, pkvh, pn, (int)threadIdx.x);
 }
 
 // The items of one pass (a launch's work list `pl` over the parameters p),
@@ -1246,26 +1364,32 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
 // across passes.
 template <class Tag, int D, int BS, bool SH>
 __device__ __forceinline__ void run_items(const DecodeParams& p, const Plan& pl, unsigned char* smem, int lds_main,
-                                          int* s_next, int wave, bool dynamic, int& parity) {
+                                          int* s_next, int wave, bool dynamic, bool first_done, int& parity) {
+  const int hkv = p.num_kv_heads;
   const int entries = pl.n_full + pl.S;
-  const int total = entries * p.num_kv_heads;
+  const int total = entries * hkv;
   const int grid = (int)gridDim.x;
   const int ws = dynamic ? 0 : static_end(total, grid, 8 * pl.n_long >= 7 * entries);
   const int b = (int)blockIdx.x;
   int w = b;
-  if (dynamic) {
+  int round = 0;  // static round of the current item
+  if (first_done) {  // this workgroup's item of round 0 is done: round 1 next
+    round = 1;
+    w = 2 * grid - 1 - b;
+  }
+  if (dynamic || (first_done && w >= ws)) {
     if (threadIdx.x == 0) {
       const int t = take_ticket(p.work);
-      s_next[parity] = (t >= 0 && t < total) ? t : total;
+      const int64_t nx = (int64_t)(dynamic ? 0 : ws) + t;
+      s_next[parity] = (nx >= 0 && nx < total) ? (int)nx : total;
     }
     __syncthreads();
     w = uniform(s_next[parity]);
     parity ^= 1;
   }
-  int round = 0;  // static round of the current item
   for (; (unsigned)w < (unsigned)total; parity ^= 1) {
-    const int e = w / p.num_kv_heads;
-    const int kvh = w - e * p.num_kv_heads;
+    const int e = w / hkv;
+    const int kvh = w - e * hkv;
     int seq, part;
     plan_entry(pl, e, seq, part);
     ++round;
@@ -1286,6 +1410,7 @@ __device__ __forceinline__ void run_items(const DecodeParams& p, const Plan& pl,
     __syncthreads();
     w = uniform(s_next[parity]);
   }
+  arrive_pending<Tag, D>(p, s_next);
 }
 
 // Persistent: a grid of as many workgroups as fit on the GPU at once (a
@@ -1301,15 +1426,32 @@ void decode_partition_kernel(DecodeParams p) {
   const int span = p.partition < p.max_seq_len ? p.partition : p.max_seq_len;
   const int lds_main = lds_main_bytes(D, p.q_len * p.group, span, BS,
                                       wave_tile_bytes<TileEngine<Tag, D, BS>>(p.q_len * p.group));
-  // Two slots for the next item, used alternately: an item may pass no
-  // barrier (a zero-length sequence), and a slot is rewritten only after the
-  // barrier that follows every wave's read of it. The third int is the
-  // merge flag of decode_item, the fourth is free.
+  // Control ints: two slots for the next item, used alternately (an item
+  // may pass no barrier (a zero-length sequence), and a slot is rewritten
+  // only after the barrier that follows every wave's read of it); the merge
+  // flag; the pending item (sequence or -1, KV head, partitions).
   int* s_next = reinterpret_cast<int*>(smem + lds_main + 2 * kWaves * 16 * 4);
-  Plan pl = plan_at(reinterpret_cast<unsigned char*>(s_next + 4), p.num_seqs);
+  // (written by every wave for itself: the first item reads it before any
+  // barrier)
+  if ((threadIdx.x & 63) == 0) s_next[4] = -1;
+  // A first item that first_entry finds needs only the first 64 lengths,
+  // not the work list: it starts streaming right away, and the list is
+  // built after it (while the other workgroup on the CU streams).
+  int seq0, part0, len0;
+  const int e0 = (int)blockIdx.x / p.num_kv_heads;
+  const bool first = first_entry(p, e0, seq0, part0, len0);
+  if (first) {
+    const int kvh = (int)blockIdx.x - e0 * p.num_kv_heads;
+    int ticket = 0;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    decode_item<Tag, D, BS, true>(p, smem, lds_main, seq0, len0, kvh, part0, tid, wave, false, ticket);
+    __syncthreads();  // the list's scan reuses the item's LDS
+  }
+  Plan pl = plan_at(reinterpret_cast<unsigned char*>(s_next + kCtlInts), p.num_seqs);
   build_plan(p, pl, reinterpret_cast<uint64_t*>(smem));
   int parity = 0;
-  run_items<Tag, D, BS, true>(p, pl, smem, lds_main, s_next, wave, false, parity);
+  run_items<Tag, D, BS, true>(p, pl, smem, lds_main, s_next, wave, false, first, parity);
   if (threadIdx.x == 0) finish_launch(p.work);  // after the workgroup's last ticket
 }
 
@@ -1338,7 +1480,8 @@ void decode_pair_kernel(DecodeParams p0, DecodeParams p1) {
   const int wave = uniform(threadIdx.x >> 6);
   const int lds_main = pair_lds_main<TileEngine<Tag, D, BS>, TileEngine<Tag, D, BS>>(D, BS, p0, p1);
   int* s_next = reinterpret_cast<int*>(smem + lds_main + 2 * kWaves * 16 * 4);
-  unsigned char* plans = reinterpret_cast<unsigned char*>(s_next + 4);
+  if (threadIdx.x == 0) s_next[4] = -1;  // no pending item (seen after the plans' barriers)
+  unsigned char* plans = reinterpret_cast<unsigned char*>(s_next + kCtlInts);
   Plan pl0 = plan_at(plans, p0.num_seqs);
   Plan pl1 = plan_at(plans + plan_bytes(p0.num_seqs), p1.num_seqs);
   build_plan(p0, pl0, reinterpret_cast<uint64_t*>(smem));
@@ -1346,8 +1489,8 @@ void decode_pair_kernel(DecodeParams p0, DecodeParams p1) {
   int parity = 0;
   // (the shared tile slots are left to the single-pass kernel: two passes'
   // worth of tile loops in one kernel would spill registers)
-  run_items<Tag, D, BS, false>(p0, pl0, smem, lds_main, s_next, wave, false, parity);
-  run_items<Tag, D, BS, false>(p1, pl1, smem, lds_main, s_next, wave, true, parity);
+  run_items<Tag, D, BS, false>(p0, pl0, smem, lds_main, s_next, wave, false, false, parity);
+  run_items<Tag, D, BS, false>(p1, pl1, smem, lds_main, s_next, wave, true, false, parity);
   if (threadIdx.x == 0) {  // after the workgroup's last ticket of each pass
     finish_launch(p0.work);
     finish_launch(p1.work);
@@ -1434,7 +1577,7 @@ template <class Tag, int D, int BS>
 hipError_t launch_pair_t(DecodeParams a, DecodeParams b, hipStream_t stream) {
   if (a.num_seqs > kMaxSeqsPerLaunch || b.num_seqs > kMaxSeqsPerLaunch) return hipErrorNotSupported;
   const size_t lds = (size_t)pair_lds_main<TileEngine<Tag, D, BS>, TileEngine<Tag, D, BS>>(D, BS, a, b) +
-                     2 * kWaves * 16 * 4 + 16 + plan_bytes(a.num_seqs) +
+                     2 * kWaves * 16 * 4 + 4 * kCtlInts + plan_bytes(a.num_seqs) +
                      plan_bytes(b.num_seqs);
   if (lds > (size_t)kLdsPerWorkgroup) return hipErrorNotSupported;
   const void* kfn = reinterpret_cast<const void*>(&decode_pair_kernel<Tag, D, BS>);

@@ -444,6 +444,33 @@ def test_more_sequences_than_one_launch():
         assert torch.equal(out[4095], torch.zeros_like(out[4095]))
 
 
+FIRST_ITEM_CASES = [
+    # id, lengths, partition: the first items of some workgroups are found
+    # from the first 64 lengths alone, the others from the work list
+    ("few_splits_in_first_64", [int(x) for x in np.r_[np.full(60, 200), [700, 1500, 30, 2100],
+                                                        np.arange(36) * 61 + 900]], 512),
+    ("unsplit_mixed_classes", [int(x) for x in (np.arange(80) * 37) % 1000 + 1], 1008),
+    ("unsplit_with_empty", [0, 5, 1000, 999, 0] + [1000] * 70, 1008),
+]
+
+
+@pytest.mark.parametrize("case", FIRST_ITEM_CASES, ids=[c[0] for c in FIRST_ITEM_CASES])
+def test_first_items_with_and_without_the_work_list(case):
+    name, lens, P = case
+    wl = W.custom(zlib.crc32(name.encode()) % 10000 + 300, seq_lens=lens, num_heads=32, num_kv_heads=8,
+                  head_dim=128, block_size=16, dtype=torch.bfloat16, partition_size=P)
+    ref, _, _ = oracle_step(wl)
+    d = to_dev(wl)
+    n, c = ws_sizes(wl, P)
+    ws = poisoned_workspace(n, c)
+    for call in range(2):
+        say(f"{name} call {call}")
+        repoison(ws, c)
+        out = gpu_step(wl, d, out_dtype=torch.float32, workspace=ws)
+        assert control_is_zero(ws, c)
+        assert_close(out, ref, wl.dtype, label=name)
+
+
 def test_schedule_order_does_not_change_results():
     """Reversing the batch changes every sequence's place in the schedule
     (and which workgroup runs it) but not its output bits."""
