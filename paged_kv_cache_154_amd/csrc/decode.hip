@@ -302,8 +302,13 @@ struct TileEngine {
   static constexpr bool kKLds128 = RB == 128;
   static constexpr int KCL = RB / 256;     // 16-byte chunks per lane per token (K rows whole)
   static constexpr int KTS = RB + 16;      // LDS row stride of the K tile
-  // one wave's K tile (and, for 128-byte rows, its V tile after it)
-  static constexpr int KT_BYTES = kKLds ? 16 * KTS : (kKLds128 ? 2 * 16 * KTS : 0);
+  // e4m3 rows of 128 bytes: each wave's tiles go from HBM straight into two
+  // LDS tile buffers of its own (the shared-tile layout below), the next
+  // tile streaming into one while the other is consumed
+  static constexpr bool kPipe = kF8 && RB == 128;
+  // one wave's K tile (and, for 128-byte rows, its V tile after it); with
+  // kPipe its two tile buffers (K then V rows, 16 RB bytes each)
+  static constexpr int KT_BYTES = kPipe ? 4 * 16 * RB : (kKLds ? 16 * KTS : (kKLds128 ? 2 * 16 * KTS : 0));
   static constexpr int NACC = VPL;  // O^T accumulator tiles
   // bf16 and e4m3 pools: P.V on the bf16 MFMA with the weights cut into exact
   // parts (e4m3 values are bf16 values)
@@ -1163,9 +1168,33 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   }
   // the loop is compiled four ways (load kind x causal limit), chosen per item
   auto tiles = [&](auto nt, auto causal) {
-    for (int cs = t_begin + wi * kTile; cs < t_end; cs += wpg * kTile)
-      eng.template step<decltype(nt)::value, decltype(causal)::value>(kbase, vbase, cs, t_end - 1, slot_bytes,
-                                                                      scale_log2, row_off, kt);
+    constexpr bool NT = decltype(nt)::value;
+    constexpr bool CAUSAL = decltype(causal)::value;
+    if constexpr (Eng::kPipe) {
+      // The wave's tiles through its two LDS buffers: tile k is read into
+      // registers as soon as its rows have landed, then the loads of tile k+1
+      // (issue_shared: global_load_lds, no registers held) are issued into
+      // the other buffer, and tile k's math runs while they stream.
+      constexpr int TB = 2 * Eng::SLOT_BYTES;  // one buffer: K rows, then V rows
+      const int stride = wpg * kTile;
+      int cs = t_begin + wi * kTile;
+      if (cs < t_end) eng.template issue_shared<NT>(kt, kt + Eng::SLOT_BYTES, kbase, vbase, cs, t_end - 1, row_off);
+      for (int b = 0; cs < t_end; cs += stride, b ^= 1) {
+        unsigned char* cur = kt + b * TB;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile k's rows are in LDS
+        typename Eng::Tile g;
+        eng.fetch_shared(g, cur, cur + Eng::SLOT_BYTES);
+        if (cs + stride < t_end) {
+          unsigned char* nx = kt + (b ^ 1) * TB;
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // every read of the buffers so far is done
+          eng.template issue_shared<NT>(nx, nx + Eng::SLOT_BYTES, kbase, vbase, cs + stride, t_end - 1, row_off);
+        }
+        eng.template consume<CAUSAL, true>(g, cs, t_end - 1, scale_log2, nullptr);
+      }
+    } else {
+      for (int cs = t_begin + wi * kTile; cs < t_end; cs += wpg * kTile)
+        eng.template step<NT, CAUSAL>(kbase, vbase, cs, t_end - 1, slot_bytes, scale_log2, row_off, kt);
+    }
   };
   using Yes = std::true_type;
   using No = std::false_type;
