@@ -13,7 +13,9 @@
  *     dense and row-major; no strides. The caller allocates and owns all of
  *     it, including the workspace. The library allocates nothing, and the
  *     only host state it keeps is a cache of how many workgroups of each
- *     kernel fit on a device (a property of the device). Per-call state lives
+ *     kernel fit on a device (a property of the device) and, once
+ *     paged_attn_decode_noalloc has run on a device, the address of that
+ *     entry point's static device scratch there. Per-call state lives
  *     in the caller's workspace (see paged_attn_decode): calls with separate
  *     workspaces are independent and may run concurrently; calls in order on
  *     one stream may share one. A call may be captured into a HIP graph and
