@@ -368,7 +368,8 @@ def per_config(pkv, W, dev, calls=200, warm=20):
             p10, p50, p90 = _pcts(_us(ev))
             gbs = wl.kv_bytes() / p50 / 1e3
             part = pkv.paged_attn_partition_tokens(S, wl.num_kv_heads, wl.block_size,
-                                                   wl.max_seq_len, P)
+                                                   wl.max_seq_len, P, num_heads=wl.num_heads,
+                                                   kv_dtype=pkv.dtype_code(wl.dtype))
             row["decode"][f"partition_size={P}"] = {
                 "partition_tokens": part, "cold_us_p10_p50_p90": [p10, p50, p90],
                 "warm_mean_us": round(w0.elapsed_time(w1) * 1e3 / warm, 2),

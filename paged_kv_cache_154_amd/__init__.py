@@ -146,11 +146,11 @@ def workspace_control_bytes(num_seqs: int, num_kv_heads: int, head_dim: int, blo
     """Bytes at the start of a decode / multi-query workspace that must be
     zero at its first use (the control area; include/pagedkv.h): 256, plus
     the arrival counts padded to 256 bytes when sequences are split (taken
-    for the shortest partition choice, that of 16-bit pools at one query
-    row per head, so the size serves every call the workspace is sized
+    for the shortest partition choice, that of 16-bit pools at 9 to 16 query
+    rows per KV head, so the size serves every call the workspace is sized
     for)."""
     P = paged_attn_partition_tokens(num_seqs, num_kv_heads, block_size, max_seq_len,
-                                    partition_size)
+                                    partition_size, q_len=16)
     if P >= max_seq_len:
         return 256
     return 256 + (4 * min(num_seqs, 2048) * num_kv_heads + 255) // 256 * 256

@@ -54,10 +54,11 @@ constexpr int kMaxQueryRows = 16 * pkv::kWaves;
 
 // Partition length chosen when partition_size is 0. A workgroup (8 waves)
 // handles one (sequence, KV head, partition); 512 fit on the GPU at once (256
-// CUs, 2 each). A base of B tokens: 1024 for 16-bit and fp32 pools, twice
-// that for e4m3 pools (half the bytes per token) and twice again with more
-// than 16 query rows per KV head (every tile costs each column group its
-// work). Measured on MI355X: with >= 2048 (sequence, KV head) pairs and
+// CUs, 2 each). A base of B tokens: for 16-bit and fp32 pools 1280 (1024
+// with 9 to 16 query rows per KV head), for e4m3 pools (half the bytes per
+// token) 2048; with more than 16 query rows per KV head (every tile costs
+// each column group its work) 2048 and 4096.
+// Measured on MI355X: with >= 2048 (sequence, KV head) pairs and
 // sequences of at most 4096 tokens, not splitting is best; otherwise B-token
 // partitions while that gives at most 4096 (sequence, KV head, partition)
 // units, else 2 B (fewer partials to write and merge).
@@ -65,9 +66,8 @@ int auto_partition(int num_seqs, int num_kv_heads, int block_size, int max_seq_l
                    int rows) {
   const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
   const int unit = block_size > pkv::kTile ? block_size : pkv::kTile;
-  int base = 1024;
-  if (kv_elem_bytes == 1) base *= 2;
-  if (rows > 16) base *= 2;
+  int base = kv_elem_bytes == 1 ? 2048 : (rows > 8 ? 1024 : 1280);
+  if (rows > 16) base = kv_elem_bytes == 1 ? 4096 : 2048;
   if (pairs >= 2048 && max_seq_len <= 4096) {
     const int P = (max_seq_len + unit - 1) / unit * unit;
     return P > 0 ? P : unit;

@@ -227,17 +227,18 @@ def test_partition_and_workspace_sizing():
     # partition_size 0: the library's choice
     # (num_seqs, q_len, num_heads, num_kv_heads, block_size, max_seq_len, partition, kv_dtype)
     pt = L.paged_attn_partition_tokens
-    assert pt(64, 1, 32, 8, 16, 4039, 0, 2) == 1024     # few (seq, KV head) pairs
-    assert pt(256, 1, 64, 8, 32, 8192, 0, 1) == 2048    # many, long
+    assert pt(64, 1, 32, 8, 16, 4039, 0, 2) == 1280     # few (seq, KV head) pairs
+    assert pt(256, 1, 64, 8, 32, 8192, 0, 1) == 2560    # many, long
     assert pt(384, 1, 32, 8, 16, 2560, 0, 2) == 2560    # many, short: no split
     assert pt(64, 1, 32, 8, 8, 10000, 512, 2) == 512    # the caller's partition
     assert pt(64, 1, 32, 8, 32, 100, 48, 2) == SHAPE    # not a multiple of 32
-    # e4m3 pools: twice the tokens per partition; more than 16 query rows per
-    # KV head: twice again
+    # e4m3 pools: 2048-token base; 9-16 query rows per KV head: 1024 (16-bit);
+    # more than 16: 2048 (16-bit) and 4096 (e4m3)
     assert pt(64, 1, 32, 8, 16, 4039, 0, 3) == 2048
     assert pt(256, 1, 64, 8, 32, 8192, 0, 3) == 4096
     assert pt(64, 8, 32, 8, 16, 4039, 0, 2) == 2048     # q_len 8 x 4 heads = 32 rows
     assert pt(64, 4, 32, 8, 16, 4039, 0, 2) == 1024     # 16 rows
+    assert pt(64, 2, 32, 8, 16, 4039, 0, 2) == 1280     # 8 rows
     assert pt(64, 1, 32, 8, 16, 4039, 0, 9) == UNSUP
     assert pt(64, 1, 30, 8, 16, 4039, 0, 2) == SHAPE    # heads not a multiple of KV heads
     hdr = 256
@@ -253,6 +254,16 @@ def test_partition_and_workspace_sizing():
     assert L.paged_attn_workspace_size(0, 32, 8, 128, 16, 4039, 0) == 0
 
 
+def test_control_area_covers_every_row_count():
+    """At 1200 tokens decode (4 query rows per KV head, 1280-token base) is
+    not split but q_len 4 (16 rows, 1024-token base) is: the control area the
+    binding zeroes is the split one, which serves both."""
+    L = _lib.lib()
+    assert L.paged_attn_workspace_size(64, 32, 8, 128, 16, 1200, 0) == 256
+    assert L.paged_attn_multi_query_workspace_size(64, 4, 32, 8, 128, 16, 1200, 0) > 256 + 2048
+    assert pkv.workspace_control_bytes(64, 8, 128, 16, 1200, 0) == 256 + 4 * 64 * 8
+
+
 def test_control_area_sizes_match_the_layout():
     """The binding's control-area sizes (the part of a workspace that must be
     zero at first use) follow the documented formula and sit inside the
@@ -261,7 +272,7 @@ def test_control_area_sizes_match_the_layout():
                                         (384, 32, 8, 128, 16, 2560, 0), (5000, 8, 8, 64, 16, 4096, 1024)]:
         c = pkv.workspace_control_bytes(S, Hkv, D, bs, maxlen, P)
         n = pkv.paged_attn_workspace_size(S, H, Hkv, D, bs, maxlen, P)
-        split = pkv.paged_attn_partition_tokens(S, Hkv, bs, maxlen, P) < maxlen
+        split = pkv.paged_attn_partition_tokens(S, Hkv, bs, maxlen, P, q_len=16) < maxlen
         assert c == (256 + (4 * min(S, 2048) * Hkv + 255) // 256 * 256 if split else 256)
         assert c <= n and c % 256 == 0
     # shared-prefix: both passes' control areas first
