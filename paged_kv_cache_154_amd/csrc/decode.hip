@@ -70,6 +70,7 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 struct F32Tag { static constexpr int kBytes = 4; };
 struct F16Tag { static constexpr int kBytes = 2; };
@@ -482,9 +483,16 @@ struct TileEngine {
 #pragma unroll
     for (int i = 0; i < NKL; ++i) a = Tr::qk(kr[i], qv[i], a);
     float s[4];
-    const int last = causal ? min(t_last, lim) : t_last;
+    // e4m3 pools (issue-bound): no mask when the whole tile is inside the
+    // sequence
+    if (kF8 && !causal && cs + kTile - 1 <= t_last) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[r] = (cs + 4 * grp + r) <= last ? a[r] * scale_log2 : -INFINITY;
+      for (int r = 0; r < 4; ++r) s[r] = a[r] * scale_log2;
+    } else {
+      const int last = causal ? min(t_last, lim) : t_last;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[r] = (cs + 4 * grp + r) <= last ? a[r] * scale_log2 : -INFINITY;
+    }
 
     // Online softmax with a lazy running max: the max (and the rescale of
     // lsum and O) moves only when some lane's tile max exceeds it by more than
@@ -514,10 +522,13 @@ struct TileEngine {
       // pattern, mid the same of the remainder, lo the rest, which has at
       // most 8 significant bits), so hi + mid + lo is the weight itself; the
       // products with the bf16 V elements are exact and the MFMA sums them in
-      // fp32. A lane group's 32 k slots carry its 4 tokens twice: against
-      // (hi, mid) in one 16x16x32 MFMA and (lo, 0) in a second, so a head-dim
-      // block of a 16-token tile takes two MFMAs (the fp32 16x16x4 form took
-      // four of twice the cycles each).
+      // fp32. bf16 pools: a lane group's 32 k slots of the 16x16x32 MFMA
+      // carry its 4 tokens twice, against (hi, mid) in one MFMA and (lo, 0)
+      // in a second. e4m3 pools (issue-bound): its 16 k slots of the 16x16x16
+      // MFMA are its 4 tokens, three MFMAs against hi, mid and lo, on the V
+      // pairs as they are widened, without the copies that writing the
+      // tokens twice takes. (The fp32 16x16x4 form took four MFMAs of twice
+      // the cycles per head-dim block.)
       uint32_t hp[4], mp[4], lp[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -529,12 +540,22 @@ struct TileEngine {
       }
       // upper halves of a and b -> (a.hi | b.hi << 16)
       auto hi2 = [](uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); };
-      const uint4 bhm = make_uint4(hi2(hp[0], hp[1]), hi2(hp[2], hp[3]), hi2(mp[0], mp[1]), hi2(mp[2], mp[3]));
-      const uint4 bl0 = make_uint4(hi2(lp[0], lp[1]), hi2(lp[2], lp[3]), 0u, 0u);
+      const uint2 h01 = make_uint2(hi2(hp[0], hp[1]), hi2(hp[2], hp[3]));
+      const uint2 m01 = make_uint2(hi2(mp[0], mp[1]), hi2(mp[2], mp[3]));
+      const uint2 l01 = make_uint2(hi2(lp[0], lp[1]), hi2(lp[2], lp[3]));
       auto pv = [&](int j, uint32_t x01, uint32_t x23) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(x01, x23, x01, x23));
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bhm), acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bl0), acc[j], 0, 0, 0);
+        if constexpr (kF8) {
+          const s16x4 av = __builtin_bit_cast(s16x4, make_uint2(x01, x23));
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4, h01), acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4, m01), acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4, l01), acc[j], 0, 0, 0);
+        } else {
+          const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(x01, x23, x01, x23));
+          const uint4 bhm = make_uint4(h01.x, h01.y, m01.x, m01.y);
+          const uint4 bl0 = make_uint4(l01.x, l01.y, 0u, 0u);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bhm), acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bl0), acc[j], 0, 0, 0);
+        }
       };
       if constexpr (kF8) {
         // e4m3 V: bytes j and j + 1 of tokens (0, 1) gathered into one word
