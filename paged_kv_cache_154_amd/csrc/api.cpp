@@ -56,8 +56,8 @@ constexpr int kMaxQueryRows = 16 * pkv::kWaves;
 // handles one (sequence, KV head, partition); 512 fit on the GPU at once (256
 // CUs, 2 each). A base of B tokens: for 16-bit and fp32 pools 1280 (1024
 // with 9 to 16 query rows per KV head), for e4m3 pools (half the bytes per
-// token) 2048; with more than 16 query rows per KV head (every tile costs
-// each column group its work) 2048 and 4096.
+// token) 2048; with more than 16 query rows per KV head (column groups
+// sharing each tile through LDS) 1280 for every pool.
 // Measured on MI355X: with >= 2048 (sequence, KV head) pairs and
 // sequences of at most 4096 tokens, not splitting is best; otherwise B-token
 // partitions while that gives at most 4096 (sequence, KV head, partition)
@@ -67,7 +67,7 @@ int auto_partition(int num_seqs, int num_kv_heads, int block_size, int max_seq_l
   const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
   const int unit = block_size > pkv::kTile ? block_size : pkv::kTile;
   int base = kv_elem_bytes == 1 ? 2048 : (rows > 8 ? 1024 : 1280);
-  if (rows > 16) base = kv_elem_bytes == 1 ? 4096 : 2048;
+  if (rows > 16) base = 1280;
   if (pairs >= 2048 && max_seq_len <= 4096) {
     const int P = (max_seq_len + unit - 1) / unit * unit;
     return P > 0 ? P : unit;

@@ -216,9 +216,9 @@ def test_multi_query_workspace_sizing():
             == _ws_expected(256, 4 * 32, 8, 128, 20))
     assert L.paged_attn_multi_query_workspace_size(64, 2, 32, 8, 128, 16, 512, 512) == hdr
     assert L.paged_attn_multi_query_workspace_size(64, 33, 32, 8, 128, 16, 4039, 0) == 0
-    # 8 x 4 = 32 query rows per KV head: 2048-token partitions
+    # 8 x 4 = 32 query rows per KV head: 1280-token partitions
     assert (L.paged_attn_multi_query_workspace_size(64, 8, 32, 8, 128, 16, 4039, 0)
-            == _ws_expected(64, 8 * 32, 8, 128, 2))
+            == _ws_expected(64, 8 * 32, 8, 128, 4))
     assert L.paged_attn_multi_query_workspace_size(64, 0, 32, 8, 128, 16, 4039, 0) == 0
 
 
@@ -233,10 +233,12 @@ def test_partition_and_workspace_sizing():
     assert pt(64, 1, 32, 8, 8, 10000, 512, 2) == 512    # the caller's partition
     assert pt(64, 1, 32, 8, 32, 100, 48, 2) == SHAPE    # not a multiple of 32
     # e4m3 pools: 2048-token base; 9-16 query rows per KV head: 1024 (16-bit);
-    # more than 16: 2048 (16-bit) and 4096 (e4m3)
+    # more than 16: 1280 for every pool
     assert pt(64, 1, 32, 8, 16, 4039, 0, 3) == 2048
     assert pt(256, 1, 64, 8, 32, 8192, 0, 3) == 4096
-    assert pt(64, 8, 32, 8, 16, 4039, 0, 2) == 2048     # q_len 8 x 4 heads = 32 rows
+    assert pt(64, 8, 32, 8, 16, 4039, 0, 2) == 1280     # q_len 8 x 4 heads = 32 rows
+    assert pt(64, 8, 32, 8, 16, 4039, 0, 3) == 1280     # the same over e4m3 pools
+    assert pt(64, 16, 32, 8, 16, 4039, 0, 2) == 1280    # 64 rows
     assert pt(64, 4, 32, 8, 16, 4039, 0, 2) == 1024     # 16 rows
     assert pt(64, 2, 32, 8, 16, 4039, 0, 2) == 1280     # 8 rows
     assert pt(64, 1, 32, 8, 16, 4039, 0, 9) == UNSUP
