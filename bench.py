@@ -583,11 +583,13 @@ def time_step(pkv, wl, dev, args, Q=1, fp8=False, P=None, layers_n=4):
     """The timed steps of one workload and their instrumented repeats.
 
     K steps with one event pair around them (events inside the steps would
-    add their own dispatch latency to every step); then the same K steps
-    with the attention call's own kernel start and end (events its launch
-    sets, paged_attn_timed) and events recorded around the call; then K
-    attention calls back to back. Returns the measurements (ms) and the
-    workload's facts."""
+    add their own dispatch latency to every step); then N = max(K, 100)
+    more steps with the attention call's own kernel start and end (events
+    its launch sets, paged_attn_timed) and events recorded around the call;
+    then N attention calls back to back. N is at least 100 because the
+    first few dozen calls after the GPU has been idle run up to 5% slower
+    than the steady state the kernel's roofline is about. Returns the
+    measurements (ms) and the workload's facts."""
     import torch
     S, H, D = wl.num_seqs, wl.num_heads, wl.head_dim
     NB, bs, Hkv, _ = wl.key_cache.shape
@@ -661,15 +663,16 @@ def time_step(pkv, wl, dev, args, Q=1, fp8=False, P=None, layers_n=4):
     ms_step = t_start.elapsed_time(t_stop) / args.steps
     log(f"{wl.name}: {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f})")
 
+    n_inst = max(args.steps, 100)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+          for _ in range(n_inst)]
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+           for _ in range(n_inst)]
     for a, b in kev:   # HIP creates an event on its first record
         a.record(stream)
         b.record(stream)
     torch.cuda.synchronize()
-    for i in range(args.steps):
+    for i in range(n_inst):
         kc, vc = layers[i % len(layers)]
         if has_new:
             scatter(kc, vc)
@@ -691,12 +694,12 @@ def time_step(pkv, wl, dev, args, Q=1, fp8=False, P=None, layers_n=4):
     b1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     b0.record(stream)
-    for i in range(args.steps):
+    for i in range(n_inst):
         kc, vc = layers[i % len(layers)]
         attend(kc, vc)
     b1.record(stream)
     torch.cuda.synchronize()
-    dec_bb = b0.elapsed_time(b1) / args.steps
+    dec_bb = b0.elapsed_time(b1) / n_inst
     log(f"{wl.name}: attention back to back: {dec_bb * 1e3:.1f} us per call")
     del layers, out, ws
     torch.cuda.empty_cache()
@@ -852,7 +855,7 @@ def main():
         "traffic": measured_traffic(profile),
         "kernel": f"{m['attn_name']} (decode_partition_kernel)",
         "duration": "mean of the kernel's own start-to-end time (events set by its launch, "
-                    "hipExtLaunchKernel) over K more steps like the timed ones",
+                    "hipExtLaunchKernel) over max(K, 100) more steps like the timed ones",
     }
     res["cpu_baseline"] = None
     ks, vs = m["scales"]
