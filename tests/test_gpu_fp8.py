@@ -155,9 +155,10 @@ def test_fp8_decode_matches_oracle(case):
         assert_close(out, ref, qdt, label=f"fp8 decode {name}")
 
 
-@pytest.mark.parametrize("Q,P", [(4, 0), (8, 64), (3, 16)])
+@pytest.mark.parametrize("Q,P", [(4, 0), (8, 64), (3, 16), (8, 0)])
 def test_fp8_multi_query_matches_oracle(Q, P):
-    lens = [Q, Q + 1, 63, 64, 65, 300, 1100]
+    # 2900 tokens: split by the library's own partition at every q_len here
+    lens = [Q, Q + 1, 63, 64, 65, 300, 1100, 2900]
     wl = W.custom(600 + Q, seq_lens=lens, num_heads=32, num_kv_heads=8, head_dim=128,
                   block_size=16, dtype=torch.bfloat16, partition_size=P, new_token=True, q_len=Q)
     gk, gv, ok, ov, ks, vs = quantise_pools(wl)
