@@ -39,6 +39,7 @@ that pass alone). ``--kv-fp8`` times the e4m3 step of the Llama-3-8B batch.
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import statistics
@@ -67,11 +68,16 @@ WORKLOADS = {
 
 
 def kernel_source_hash():
-    """sha256 of the decode kernel sources (as in the traffic profile)."""
+    """sha256 of the decode kernel sources (as in the traffic profile), with
+    their comments and blank lines left out: the measured traffic belongs to
+    the code, which a change of comments leaves as it was."""
     h = hashlib.sha256()
     for f in ("decode.hip", "pagedkv_internal.h"):
         with open(os.path.join(ROOT, "paged_kv_cache_154_amd", "csrc", f)) as fh:
-            h.update(fh.read().encode())
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip()).encode())
     return h.hexdigest()
 
 

@@ -20,7 +20,10 @@
 //    unless the blocks look shared (see decode_item): on MI355X that reads
 //    ~6.6 TB/s where 16 rows x 64 bytes per instruction, the layout the MFMA
 //    operand wants, reads ~5.7 (and worse when non-temporal). K is therefore
-//    reordered through a per-wave LDS tile into the operand layout. Then
+//    reordered through a per-wave LDS tile into the operand layout (e4m3
+//    rows of 128 bytes instead stream from HBM into two LDS tile buffers per
+//    wave, the next tile in flight while the current one is worked on; see
+//    TileEngine). Then
 //      - Q.K^T on v_mfma_f32_16x16x32_{f16,bf16} (fp32 pools:
 //        v_mfma_f32_16x16x4_f32) with the key tile as the A operand (16
 //        tokens x 32 head-dim elements, straight from the pool) and the G
@@ -30,7 +33,8 @@
 //        tokens, so a head's softmax state lives in one lane column;
 //      - P.V with A = V^T (each lane holds head_dim / 16 contiguous elements
 //        of 4 tokens' V rows) and B = P^T: on v_mfma_f32_16x16x32_bf16 for
-//        bf16 and e4m3 pools, each weight cut exactly into three bf16 parts
+//        bf16 pools and v_mfma_f32_16x16x16_bf16 for e4m3 pools (codes
+//        widened to bf16), each weight cut exactly into three bf16 parts
 //        (hi + mid + lo = the fp32 weight), on v_mfma_f32_16x16x4_f32 with
 //        fp32 weights otherwise: the probabilities keep fp32 precision, and
 //        the output tile O^T[d][head] keeps a head in the same lane column
