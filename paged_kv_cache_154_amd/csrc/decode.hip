@@ -641,6 +641,106 @@ struct TileEngine {
     }
   }
 
+  // The loads of one half of the tile at cs (K rows from kbase or V rows from
+  // vbase, as issue_shared) into the slot s. Completion: vmcnt.
+  template <bool nt, class RowOff>
+  __device__ void issue_half(unsigned char* s, const unsigned char* base, int cs, int t_last, RowOff row_off) {
+    static_assert(kShared, "shared tiles take rows of 128 or 256 bytes");
+    const int lane = col + 16 * grp;
+    const int c = lane % CH;
+#pragma unroll
+    for (int a = 0; a < 16 / TPI; ++a) {
+      const int tt = a * TPI + lane / CH;
+      const uint64_t off = row_off(min(cs + tt, t_last)) + 16 * (c ^ swz(tt));
+      __builtin_amdgcn_global_load_lds(base + off, (__attribute__((address_space(3))) void*)(s + a * 1024), 16, 0,
+                                       nt ? 2 : 0);
+    }
+  }
+
+  // fetch_shared with the reads written as LDS instructions the compiler
+  // does not see, so that it adds no wait for loads still streaming into
+  // another slot (it cannot tell the slots apart); the reads are complete
+  // when this returns. The caller waits for the slot's own loads first.
+  __device__ void fetch_unseen(Tile& g, const unsigned char* sk, const unsigned char* sv) {
+    static_assert(kShared && NKR == VW && (NKR == 2 || NKR == 4), "rows of 128 or 256 bytes");
+    auto lds = [](const unsigned char* p) {
+      return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
+    };
+    // the lane's place passes through an empty asm statement so that its
+    // addressing is recomputed per tile instead of being hoisted out of the
+    // tile loops and held in registers across the math
+    int cl = col, gr = grp;
+    asm volatile("" : "+v"(cl), "+v"(gr));
+    uint32_t ka[NKR], va[4];
+#pragma unroll
+    for (int u = 0; u < NKR; ++u) ka[u] = lds(sk + cl * RB + 16 * ((4 * u + gr) ^ swz(cl)));
+    const int b = cl * VPL * E;  // the lane's V bytes within a row
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tt = 4 * gr + r;
+      va[r] = lds(sv + tt * RB + 16 * ((b / 16) ^ swz(tt)) + (b % 16));
+    }
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    if constexpr (NKR == 2) {
+      u32x4_t a0, a1;
+      u32x2_t w0, w1, w2, w3;
+      asm volatile(
+          "ds_read_b128 %0, %6\n\t"
+          "ds_read_b128 %1, %7\n\t"
+          "ds_read_b64 %2, %8\n\t"
+          "ds_read_b64 %3, %9\n\t"
+          "ds_read_b64 %4, %10\n\t"
+          "ds_read_b64 %5, %11\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(a0), "=&v"(a1), "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3)
+          : "v"(ka[0]), "v"(ka[1]), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3])
+          : "memory");
+      g.kr[0] = make_uint4(a0.x, a0.y, a0.z, a0.w);
+      g.kr[1] = make_uint4(a1.x, a1.y, a1.z, a1.w);
+      const u32x2_t w[4] = {w0, w1, w2, w3};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        g.vr[r][0] = w[r].x;
+        g.vr[r][1] = w[r].y;
+      }
+    } else {
+      // two blocks of four reads (K, then V): fewer registers tied up at once
+      u32x4_t a0, a1, a2, a3;
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %5\n\t"
+          "ds_read_b128 %2, %6\n\t"
+          "ds_read_b128 %3, %7\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
+          : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3])
+          : "memory");
+      g.kr[0] = make_uint4(a0.x, a0.y, a0.z, a0.w);
+      g.kr[1] = make_uint4(a1.x, a1.y, a1.z, a1.w);
+      g.kr[2] = make_uint4(a2.x, a2.y, a2.z, a2.w);
+      g.kr[3] = make_uint4(a3.x, a3.y, a3.z, a3.w);
+      u32x4_t w0, w1, w2, w3;
+      asm volatile(
+          "ds_read_b128 %0, %4\n\t"
+          "ds_read_b128 %1, %5\n\t"
+          "ds_read_b128 %2, %6\n\t"
+          "ds_read_b128 %3, %7\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3)
+          : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3])
+          : "memory");
+      const u32x4_t w[4] = {w0, w1, w2, w3};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        g.vr[r][0] = w[r].x;
+        g.vr[r][1] = w[r].y;
+        g.vr[r][2] = w[r].z;
+        g.vr[r][3] = w[r].w;
+      }
+    }
+  }
+
   // The operands of the tile in the slot pair (sk, sv), in the layout issue
   // leaves in registers: key chunk 4u + grp of row col (raw codes for e4m3),
   // and the V bytes [col VPL E, + VPL E) of rows 4 grp + r.
@@ -1223,26 +1323,57 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, unsigned char
   };
   using Yes = std::true_type;
   using No = std::false_type;
-  // several column groups: rounds of kWaves tiles, each loaded once into the
-  // tile slots in LDS (wave w loads tile w of the round) and read from there
-  // by one wave of every group; barriers bracket the loads of a round.
+  // several column groups: every key and value tile loaded once into the
+  // tile slots in LDS and read from there by one wave of every group.
+  //  * 16-bit pools with two groups: rounds of kWaves / 2 tiles (the K rows
+  //    of tile i of the round loaded by wave i, its V rows by wave
+  //    i + kWaves / 2); the slots hold two rounds, the next streaming into
+  //    one half while this one is worked on; one barrier per round.
+  //  * otherwise: rounds of kWaves tiles (wave w loads tile w of the round),
+  //    barriers around the loads of each round (measured faster there:
+  //    e4m3 tiles are half the bytes, and four or more groups do more math
+  //    per tile).
   auto shared_tiles = [&](auto nt, auto causal) {
     if constexpr (SH && Eng::kShared) {
+      constexpr bool NT = decltype(nt)::value;
+      constexpr bool CAUSAL = decltype(causal)::value;
+      constexpr int TS = 2 * Eng::SLOT_BYTES;  // one tile: K rows, then V rows
       unsigned char* slots = smem + bt_lds_bytes(p.partition < p.max_seq_len ? p.partition : p.max_seq_len, BS);
       const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
-      for (int r0 = 0; r0 < ntiles; r0 += kWaves) {
-        __syncthreads();  // every wave is done with the previous round's slots
-        if (r0 + wave < ntiles)
-          eng.template issue_shared<decltype(nt)::value>(slots + wave * 2 * Eng::SLOT_BYTES,
-                                                         slots + wave * 2 * Eng::SLOT_BYTES + Eng::SLOT_BYTES, kbase,
-                                                         vbase, t_begin + (r0 + wave) * kTile, t_end - 1, row_off);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        for (int k = wi; k < kWaves && r0 + k < ntiles; k += wpg) {
-          typename Eng::Tile g;
-          eng.fetch_shared(g, slots + k * 2 * Eng::SLOT_BYTES, slots + k * 2 * Eng::SLOT_BYTES + Eng::SLOT_BYTES);
-          eng.template consume<decltype(causal)::value, true>(g, t_begin + (r0 + k) * kTile, t_end - 1,
-                                                              scale_log2, nullptr);
+      if (!Eng::kF8 && nct == 2) {
+        constexpr int RT = kWaves / 2;  // tiles per round
+        const int half = wave / RT;     // 0: K rows, 1: V rows
+        const int mine = wave - half * RT;
+        auto issue = [&](int r0) {  // the round of tiles r0 .. r0 + RT - 1
+          if (r0 + mine < ntiles)
+            eng.template issue_half<NT>(slots + (((r0 / RT) & 1) * RT + mine) * TS + half * Eng::SLOT_BYTES,
+                                        half ? vbase : kbase, t_begin + (r0 + mine) * kTile, t_end - 1, row_off);
+        };
+        issue(0);
+        for (int r0 = 0; r0 < ntiles; r0 += RT) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of the round
+          __syncthreads();  // every wave's; and every wave is done with the other half
+          if (r0 + RT < ntiles) issue(r0 + RT);
+          const unsigned char* buf = slots + ((r0 / RT) & 1) * RT * TS;
+          for (int k = wi; k < RT && r0 + k < ntiles; k += wpg) {
+            typename Eng::Tile g;
+            eng.fetch_unseen(g, buf + k * TS, buf + k * TS + Eng::SLOT_BYTES);
+            eng.template consume<CAUSAL, true>(g, t_begin + (r0 + k) * kTile, t_end - 1, scale_log2, nullptr);
+          }
+        }
+      } else {
+        for (int r0 = 0; r0 < ntiles; r0 += kWaves) {
+          __syncthreads();  // every wave is done with the previous round's slots
+          if (r0 + wave < ntiles)
+            eng.template issue_shared<NT>(slots + wave * TS, slots + wave * TS + Eng::SLOT_BYTES, kbase, vbase,
+                                          t_begin + (r0 + wave) * kTile, t_end - 1, row_off);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          for (int k = wi; k < kWaves && r0 + k < ntiles; k += wpg) {
+            typename Eng::Tile g;
+            eng.fetch_shared(g, slots + k * TS, slots + k * TS + Eng::SLOT_BYTES);
+            eng.template consume<CAUSAL, true>(g, t_begin + (r0 + k) * kTile, t_end - 1, scale_log2, nullptr);
+          }
         }
       }
     }
@@ -1471,8 +1602,10 @@ __device__ __forceinline__ void run_items(const DecodeParams& p, const Plan& pl,
 // multiple of 8), each working through its items of the schedule above. A
 // workgroup whose next item is a counter one draws a ticket while it merges
 // its current item; every ticket advances the counter, so every workgroup
-// ends. The last workgroup to end sets the control word back to zero.
-template <class Tag, int D, int BS>
+// ends. The last workgroup to end sets the control word back to zero. WIDE:
+// compiled with the tiles shared by column groups (more than 16 query rows
+// per KV head); the other instance leaves that code out.
+template <class Tag, int D, int BS, bool WIDE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WavesPerEU<Tag, D>::value)))
 void decode_partition_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1499,13 +1632,13 @@ void decode_partition_kernel(DecodeParams p) {
     int ticket = 0;
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    decode_item<Tag, D, BS, true>(p, smem, lds_main, seq0, len0, kvh, part0, tid, wave, false, ticket);
+    decode_item<Tag, D, BS, WIDE>(p, smem, lds_main, seq0, len0, kvh, part0, tid, wave, false, ticket);
     __syncthreads();  // the list's scan reuses the item's LDS
   }
   Plan pl = plan_at(reinterpret_cast<unsigned char*>(s_next + kCtlInts), p.num_seqs);
   build_plan(p, pl, reinterpret_cast<uint64_t*>(smem));
   int parity = 0;
-  run_items<Tag, D, BS, true>(p, pl, smem, lds_main, s_next, wave, false, first, parity);
+  run_items<Tag, D, BS, WIDE>(p, pl, smem, lds_main, s_next, wave, false, first, parity);
   if (threadIdx.x == 0) finish_launch(p.work);  // after the workgroup's last ticket
 }
 
@@ -1579,11 +1712,11 @@ int resident_workgroups(const void* kernel, size_t lds) {
   return n;
 }
 
-template <class Tag, int D, int BS>
+template <class Tag, int D, int BS, bool WIDE>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   using Eng = TileEngine<Tag, D, BS>;
   const int span = p.partition < p.max_seq_len ? p.partition : p.max_seq_len;
-  const void* kfn = reinterpret_cast<const void*>(&decode_partition_kernel<Tag, D, BS>);
+  const void* kfn = reinterpret_cast<const void*>(&decode_partition_kernel<Tag, D, BS, WIDE>);
   const size_t q_row = (size_t)p.q_len * p.num_heads * D;  // elements per sequence
   const size_t q_elem = (size_t)KV<Tag>::kQBytes;  // the output, unless fp32, has the query's type
   const size_t out_elem = p.out_f32 ? 4 : q_elem;
@@ -1614,10 +1747,10 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream, hipEvent_t start,
     hipEvent_t ev0 = s0 == 0 ? start : nullptr;                 // the first launch's start
     hipEvent_t ev1 = s0 + c.num_seqs >= p.num_seqs ? stop : nullptr;  // the last one's end
     if (ev0 || ev1)
-      hipExtLaunchKernelGGL(decode_partition_kernel<Tag, D, BS>, dim3((unsigned)grid), dim3(kThreads),
+      hipExtLaunchKernelGGL(decode_partition_kernel<Tag, D, BS, WIDE>, dim3((unsigned)grid), dim3(kThreads),
                             (uint32_t)lds, stream, ev0, ev1, 0u, c);
     else
-      decode_partition_kernel<Tag, D, BS><<<dim3((unsigned)grid), dim3(kThreads), lds, stream>>>(c);
+      decode_partition_kernel<Tag, D, BS, WIDE><<<dim3((unsigned)grid), dim3(kThreads), lds, stream>>>(c);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1665,10 +1798,17 @@ hipError_t launch_pair_d(const DecodeParams& a, const DecodeParams& b, int d, in
 
 template <class Tag, int D>
 hipError_t launch_bs(const DecodeParams& p, int bs, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  // more than 16 query rows per KV head: the instance with the tiles shared
+  // by its column groups; decode and up to 16 rows run an instance without
+  // that code
+  const bool wide = col_tiles(p.q_len * p.group) > 1;
   switch (bs) {
-    case 8: return launch_t<Tag, D, 8>(p, stream, start, stop);
-    case 16: return launch_t<Tag, D, 16>(p, stream, start, stop);
-    case 32: return launch_t<Tag, D, 32>(p, stream, start, stop);
+    case 8: return wide ? launch_t<Tag, D, 8, true>(p, stream, start, stop)
+                        : launch_t<Tag, D, 8, false>(p, stream, start, stop);
+    case 16: return wide ? launch_t<Tag, D, 16, true>(p, stream, start, stop)
+                         : launch_t<Tag, D, 16, false>(p, stream, start, stop);
+    case 32: return wide ? launch_t<Tag, D, 32, true>(p, stream, start, stop)
+                         : launch_t<Tag, D, 32, false>(p, stream, start, stop);
     default: return hipErrorInvalidValue;
   }
 }
