@@ -129,10 +129,12 @@ def stream_read_peak(dev, gib=4, reps=8):
     return best
 
 
-def time_decode(pkv, wl, dev, layers=2, calls=20, P=0):
-    """Median decode-call time (us) of a workload: calls queued back to back
-    (as in the timed steps), rotating over layer copies of the pools. A
-    workload with several new tokens per sequence runs the multi-query pass."""
+def time_decode(pkv, wl, dev, layers=2, calls=100, P=0, warm=20):
+    """Median decode-call time (us) of a workload, the kernels' own start to
+    end (events the launch sets): calls queued back to back (as in the timed
+    steps) after `warm` untimed ones, rotating over layer copies of the
+    pools. A workload with several new tokens per sequence runs the
+    multi-query pass."""
     import torch
     attn = pkv.paged_attn_decode if wl.q_len == 1 else pkv.paged_attn_multi_query
     q = wl.query.to(dev)
@@ -145,17 +147,14 @@ def time_decode(pkv, wl, dev, layers=2, calls=20, P=0):
     pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(layers - 1)]
     out = torch.empty(wl.query.shape, dtype=wl.dtype, device=dev)
     ws = pkv.workspace_for(q, kc0, wl.max_seq_len, P)
-    for i in range(4):
+    for i in range(warm):
         kc, vc = pools[i % layers]
         attn(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(calls)]
+    ev = _events(calls)
     torch.cuda.synchronize()
     for i in range(calls):
         kc, vc = pools[i % layers]
-        ev[i][0].record()
-        attn(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws)
-        ev[i][1].record()
+        attn(out, q, kc, vc, bt, sl, wl.scale, wl.max_seq_len, P, ws, events=ev[i])
     torch.cuda.synchronize()
     del pools
     return statistics.median(a.elapsed_time(b) * 1e3 for a, b in ev)
@@ -211,13 +210,13 @@ def multi_query_rows(pkv, W, base, dev, q_lens=(2, 4, 8)):
     decode of the same batch; KV GB/s over the same pool bytes."""
     import torch
     G = base.num_heads // base.num_kv_heads
-    t_dec = time_decode(pkv, base, dev, calls=40)
+    t_dec = time_decode(pkv, base, dev)
     rows = {"decode_us": round(t_dec, 1)}
     for Q in q_lens:
         if Q * G > 128:
             continue
         wl = W.llama3_8b(q_len=Q)
-        t = time_decode(pkv, wl, dev, calls=40)
+        t = time_decode(pkv, wl, dev)
         rows[f"q_len={Q}"] = {"us": round(t, 1), "kv_GBps": round(wl.kv_bytes() / t / 1e3, 1),
                               "over_decode": round(t / t_dec, 3),
                               "tokens_per_s": round(Q * wl.num_seqs / (t * 1e-6), 1)}
