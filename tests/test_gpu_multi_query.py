@@ -80,6 +80,12 @@ MQ_SMALL = [
      [6, 63, 64, 65, 69, 70, 71, 1500], 64),  # R 24
     ("f16_d64_bs8_g8_q5_split16", torch.float16, 64, 8, 16, 2, 5, [5, 15, 16, 17, 20, 21, 333], 16),
     ("f32_d64_bs16_g1_q40_split32", torch.float32, 64, 16, 2, 2, 40, [40, 41, 63, 64, 65, 71, 250], 32),
+    # 17-32 rows over 16-bit pools: the double-buffered shared tiles, at both
+    # head dims (128-byte and 256-byte rows), several rounds and a ragged one
+    ("f16_d128_bs16_g4_q8", torch.float16, 128, 16, 32, 8, 8, [8, 9, 63, 64, 65, 129, 1400], 0),  # R 32
+    ("bf16_d64_bs16_g4_q6", torch.bfloat16, 64, 16, 16, 4, 6, [6, 7, 48, 64, 80, 900], 0),  # R 24
+    ("f16_d64_bs32_g2_q12_split64", torch.float16, 64, 32, 8, 4, 12,
+     [12, 13, 64, 65, 75, 76, 77, 600], 64),  # R 24
 ]
 
 
