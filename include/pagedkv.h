@@ -310,11 +310,11 @@ size_t paged_attn_shared_prefix_workspace_size(int num_groups, int group_size, i
  * split. The choice for 0 starts from a base B that depends on the query
  * rows per KV head, R = q_len * num_heads / num_kv_heads: for 16-bit and fp32
  * pools 1280 tokens (R <= 8) or 1024 (R <= 16); for PKV_E4M3 pools 2048
- * (R <= 16); above 16 rows 1280 for every pool. Then: no split when there are at least
- * 2048 (sequence, KV head) pairs and
- * max_seq_len <= 4096; else B while that makes at most 4096 (sequence, KV
- * head, partition) units; else 2 B. The workspace sizes are those of the
- * shortest choice (16-bit pools), which serve every dtype.
+ * (R <= 16); above 16 rows 1280 for every pool. Then: no split when there
+ * are at least 2048 (sequence, KV head) pairs and max_seq_len <= 4096; else
+ * B while that makes at most 4096 (sequence, KV head, partition) units; else
+ * 2 B. The workspace sizes are those of the shortest choice (16-bit pools),
+ * which serve every dtype.
  */
 int paged_attn_partition_tokens(int num_seqs, int q_len, int num_heads, int num_kv_heads,
                                 int block_size, int max_seq_len, int partition_size,
