@@ -202,6 +202,46 @@ def test_multi_query_workspace_garbage_and_reuse():
         assert_close(out, refs[k], wl.dtype, label=f"shared workspace {k} P={P}")
 
 
+def test_multi_query_graph_replays_match_the_oracle():
+    """The multi-query pass with 32 query rows per KV head (the instance
+    whose column groups share double-buffered tiles) captured into a HIP
+    graph and replayed with new queries: each replay matches the oracle and
+    leaves the control area zero."""
+    wl = _wl("graph_mq", torch.bfloat16, 128, 16, 32, 8, 8, [8, 9, 300, 1500, 2900, 64], 0,
+             new_token=False)
+    d = to_dev(wl)
+    for P in (256, 0):
+        ws, c = mq_ws(wl, P)
+        out = torch.empty(wl.query.shape, dtype=torch.float32, device=DEV)
+        q = d["q"].clone()
+
+        def call():
+            pkv.paged_attn_multi_query(out, q, d["kc"], d["vc"], d["bt"], d["sl"], wl.scale,
+                                       wl.max_seq_len, P, workspace=ws)
+
+        call()                          # eager first (occupancy figures cached)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call()
+        torch.cuda.synchronize()
+        gen = torch.Generator().manual_seed(40 + P)
+        for rep in range(3):
+            qh = torch.randn(wl.query.shape, generator=gen).to(wl.dtype)
+            q.copy_(qh.to(DEV))
+            out.fill_(float("nan"))
+            repoison(ws, c)
+            torch.cuda.synchronize()
+            say(f"multi-query graph replay {rep} P={P}")
+            graph.replay()
+            torch.cuda.synchronize()
+            assert control_is_zero(ws, c)
+            ref = oracle.multi_query(qh, wl.key_cache, wl.value_cache, wl.block_table,
+                                     wl.seq_lens, wl.scale)
+            assert_close(out, ref, wl.dtype, label=f"multi-query graph replay {rep} P={P}")
+        del graph
+
+
 @pytest.mark.parametrize("Q,P", [(4, 0), (4, 512), (8, 0)])
 def test_multi_query_llama3_8b_shaped_verification(Q, P):
     """Speculative verification at the Llama-3-8B shape: 64 sequences of
